@@ -1,0 +1,131 @@
+/*
+ * sdpa.h — C ABI of the MI355X (gfx950) scaled dot-product attention library.
+ *
+ * Operation (forward), per batch b, query head h, query row i:
+ *   S_ij = scale * q_i . k_j + M_bhij   for every key j the row may attend to,
+ *   P_i  = softmax over keys of S_i (row max subtracted),  O_i = sum_j P_ij v_j,
+ *   LSE_i = max_j S_ij + ln sum_j exp(S_ij - max_j S_ij)          (natural log, fp32).
+ * Sources: "Scaled dot-product attention (forward and backward)" (tinyllm L5.1),
+ * section 2 Principles and 2.2 Masking; cuDNN "Attention", SDPA FP16/BF16 Forward
+ * (Python API return values: stats = max + ln sum exp, shape (B, Hq, Sq, 1); Tensors
+ * table); torch "flex_attention" parameters (default scale 1/sqrt(E), lse (B, Hq, L)).
+ *
+ * Backward: dV = P^T dO, dP = dO V^T, dS = P o (dP - D) with D_i = rowsum(dO o O)_i,
+ *   dQ = scale dS K, dK = scale dS^T Q.  Source: tinyllm L5.1 section 2.3 The backward
+ *   pass; cuDNN "Attention", SDPA FP16/BF16 Backward (takes the forward's O and stats).
+ *
+ * Which keys a row may attend to (all conditions at once):
+ *  - additive mask: an entry of -inf blocks the pair, a finite entry is added as a bias
+ *    (Lucid ScaledDotProductAttentionBackward, Notes; cuDNN "Attention", Bias mask);
+ *  - is_causal: top-left aligned, key j is visible to query i iff j <= i
+ *    ("Understanding PyTorch Scaled Dot-Product Attention" section 3, tril);
+ *  - per-batch lengths: keys j >= seq_lens_kv[b] are blocked and query rows
+ *    i >= seq_lens_q[b] are empty (cuDNN "Attention", Support Matrix glossary note on
+ *    padded layouts; Configurable Options, Padding mask).  Rows and keys past a length
+ *    are never read.
+ * A row with no visible key (empty or fully masked) yields O = 0, LSE = -inf and zero
+ * gradients, never NaN (tinyllm L5.1 section 2.2).
+ *
+ * GQA: Hq must be a multiple of Hkv; query head h reads KV head h / (Hq / Hkv), the
+ * repeat_interleave order ("Understanding PyTorch Scaled Dot-Product Attention"
+ * section 4).  dK/dV of a shared head sum over the query heads it serves.
+ *
+ * Layout: every tensor is logically (B, H, L, D) with the element strides given below for
+ * (b, h, l); the innermost (d) stride is 1.  dO shares O's strides, dQ/dK/dV share
+ * Q/K/V's strides.  The mask is logically (B, Hq, Lq, Lk) with strides for (b, h, i) and a
+ * unit stride along keys; a stride of 0 broadcasts a dimension ((B|1, Hq|1, Lq, Lk)).
+ * LSE is contiguous (B, Hq, Lq) fp32.  One element type for q, k, v, o, dO, dq, dk, dv and
+ * the mask.
+ *
+ * Ownership and threading: every data pointer is a device pointer owned by the caller.
+ * The library allocates no device memory, keeps no handles, never synchronises the
+ * device, and launches only on the given stream (a hipStream_t; NULL = default stream).
+ * It is re-entrant; its only global state is a thread-local error message.
+ *
+ * Errors: every condition checkable on the host is validated before anything is
+ * launched; on failure the call returns a status, launches nothing and records a
+ * message readable with sdpa_last_error().  Device-resident preconditions are not
+ * checked: 0 <= seq_lens <= L, finite q/k/v/dO (rows past a length may hold anything),
+ * mask entries finite or -inf.
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID_ARGUMENT = 1,   /* malformed problem or pointer */
+  SDPA_ERR_UNSUPPORTED = 2,        /* well-formed but outside what the kernels cover */
+  SDPA_ERR_WORKSPACE_TOO_SMALL = 3,
+  SDPA_ERR_HIP = 4                 /* a launch failed; see sdpa_last_error() */
+} sdpa_status;
+
+typedef enum { SDPA_DTYPE_F32 = 0, SDPA_DTYPE_BF16 = 1 } sdpa_dtype;
+
+typedef struct {
+  int32_t dtype;                    /* sdpa_dtype */
+  int32_t B, Hq, Hkv, Lq, Lk, Dqk, Dv;
+  int64_t q_stride[3];              /* (b, h, l) element strides of q (and dq) */
+  int64_t k_stride[3];              /* of k (and dk) */
+  int64_t v_stride[3];              /* of v (and dv) */
+  int64_t o_stride[3];              /* of o (and dO) */
+  int64_t mask_stride[3];           /* (b, h, i) of the mask; keys have unit stride */
+  float scale;                      /* NaN selects 1/sqrt(Dqk); else finite and > 0 */
+  int32_t is_causal;                /* nonzero: top-left causal */
+} sdpa_problem;
+
+/*
+ * Supported by the kernels (SDPA_ERR_UNSUPPORTED otherwise):
+ *   bf16: Dqk == Dv in {64, 128};  fp32: Dqk == Dv in {32, 64, 128}.
+ *   Base pointers 16-byte aligned; (b, h, l) strides multiples of 8 elements (bf16) or
+ *   4 elements (fp32); mask (b, h, i) strides likewise.
+ */
+
+/* Device workspace (bytes) the forward needs: 0 for prefill; split-KV partial results
+ * when Lq == 1 (decode).  The caller allocates it; it may be reused after the call's
+ * work on the stream has finished. */
+size_t sdpa_forward_workspace_bytes(const sdpa_problem* p);
+
+/* Device workspace (bytes) the backward needs: D = rowsum(dO o O) in fp32. */
+size_t sdpa_backward_workspace_bytes(const sdpa_problem* p);
+
+/*
+ * Forward.  q (B,Hq,Lq,Dqk), k (B,Hkv,Lk,Dqk), v (B,Hkv,Lk,Dv), o (B,Hq,Lq,Dv) in the io
+ * dtype; lse (B,Hq,Lq) fp32 (may be NULL when not wanted); mask_or_null additive;
+ * seq_lens_q_or_null / seq_lens_kv_or_null (B) int32 device arrays.  O and LSE are fully
+ * written, including zeros / -inf for empty rows.  The result is bitwise repeatable.
+ */
+sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                         const int32_t* seq_lens_kv_or_null, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward.  Takes the forward's o and lse (same problem, mask, causal flag and lengths)
+ * and dO (B,Hq,Lq,Dv); writes dq, dk, dv (shapes and strides of q, k, v).  Every element
+ * of dq, dk, dv is written (zeros where no gradient flows).  Deterministic: no atomics.
+ */
+sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                          const void* o, const void* dO, const float* lse,
+                          const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                          const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+const char* sdpa_status_string(sdpa_status s);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* sdpa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDPA_H */

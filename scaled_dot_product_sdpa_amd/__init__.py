@@ -1,0 +1,17 @@
+"""Scaled dot-product attention for MI355X (gfx950): hand-written HIP kernels behind a
+small C ABI (include/sdpa.h), with this package as the thin Python binding.
+
+    o, lse = sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False,
+                          seq_lens_q=None, seq_lens_kv=None)
+    dq, dk, dv = sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
+                               seq_lens_q=None, seq_lens_kv=None)
+
+Importing the package does not load the library; the first call does, and fails if it
+has not been built (``python -m scaled_dot_product_sdpa_amd.build``).
+"""
+
+from .api import (EXPORTS, LIB_PATH, Problem, SdpaError, load_library, sdpa_backward,
+                  sdpa_forward)
+
+__all__ = ["sdpa_forward", "sdpa_backward", "load_library", "LIB_PATH", "EXPORTS", "Problem",
+           "SdpaError"]

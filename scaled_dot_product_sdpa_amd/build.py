@@ -1,0 +1,68 @@
+"""Build libsdpa.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
+
+Usage: ``python -m scaled_dot_product_sdpa_amd.build`` (or ``build()`` from Python).
+Each source is compiled to an object file in ``_build/`` in parallel, then linked.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+CSRC = PKG / "csrc"
+BUILD = PKG / "_build"
+LIB = PKG / "libsdpa.so"
+SOURCES = ["sdpa_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "attn_f32.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed-fp32 VALU forms are kept out of generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _compile(src: Path, obj: Path, extra=()) -> None:
+    lang = ["-x", "hip"] if src.suffix == ".cpp" else []
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", str(src), "-o", str(obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src.name}")
+    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if noise:
+        sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(verbose: bool = False, extra=()) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    objs = []
+    jobs = []
+    for name in SOURCES:
+        src = CSRC / name
+        obj = BUILD / (name.rsplit(".", 1)[0] + ".o")
+        objs.append(obj)
+        jobs.append((src, obj))
+    workers = min(len(jobs), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda j: _compile(j[0], j[1], extra), jobs))
+    tmp = LIB.with_name(LIB.name + f".tmp{os.getpid()}")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libsdpa.so failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,249 @@
+// attn_f32.hip — fp32 forward and backward (accuracy path for fp32 inputs), gfx950.
+//
+// Same operation as the bf16 kernels, computed entirely in fp32 on the vector ALUs with
+// one thread per query row (forward, dQ) or per key row (dK, dV).  Sources:
+// "Scaled dot-product attention (forward and backward)", section 2 Principles (S, P, O),
+// 2.2 Masking (-inf before the softmax, max subtracted, empty rows are zero) and 2.3 The
+// backward pass (dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = a dS K, dK = a dS^T Q,
+// D_i = dO_i . O_i).  The backward recomputes P_ij = exp(S_ij - LSE_i) from the forward's
+// LSE, as the FlashAttention-2 row of that page's "Going further" table describes.
+#include "kern_common.h"
+#include "launch.h"
+
+namespace sdpa {
+namespace {
+
+constexpr int kTpb = 64;
+
+struct RowCtx {
+  int b, h, g, i;
+  int q_end, kv_end, stop;  // stop: keys [0, stop) are candidates
+};
+
+__device__ __forceinline__ bool key_visible(const Problem& p, const RowCtx& r, int j) {
+  return j < r.kv_end && r.i < r.q_end && (!p.causal || j <= r.i);
+}
+
+__device__ __forceinline__ RowCtx row_ctx(const Problem& p, int64_t row) {
+  RowCtx r;
+  r.i = (int)(row % p.Lq);
+  r.h = (int)((row / p.Lq) % p.Hq);
+  r.b = (int)(row / ((int64_t)p.Lq * p.Hq));
+  r.g = r.h / p.G;
+  r.q_end = p.len_q ? min(p.len_q[r.b], p.Lq) : p.Lq;
+  r.kv_end = p.len_kv ? min(p.len_kv[r.b], p.Lk) : p.Lk;
+  r.stop = (r.i < r.q_end) ? (p.causal ? min(r.kv_end, r.i + 1) : r.kv_end) : 0;
+  return r;
+}
+
+// Score of (row, key j) in natural-log units, -inf if the pair is blocked.
+template <int D>
+__device__ __forceinline__ float score(const Problem& p, const RowCtx& r, const float* qv,
+                                       const float* kbase, int j) {
+  if (!key_visible(p, r, j)) return kNegInf;
+  const float* kj = kbase + (int64_t)j * p.k_sl;
+  float dot = 0.f;
+#pragma unroll
+  for (int t = 0; t < D; ++t) dot = fmaf(qv[t], kj[t], dot);
+  float s = dot * p.scale;
+  if (p.mask) {
+    const float* m = reinterpret_cast<const float*>(p.mask) + r.b * p.m_sb + r.h * p.m_sh +
+                     (int64_t)r.i * p.m_si;
+    s += m[j];
+  }
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a) {
+  const Problem& p = a.p;
+  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
+  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
+  const RowCtx r = row_ctx(p, row);
+  const float* qrow = reinterpret_cast<const float*>(a.q) + r.b * p.q_sb + r.h * p.q_sh +
+                      (int64_t)r.i * p.q_sl;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + r.b * p.k_sb + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + r.b * p.v_sb + r.g * p.v_sh;
+  float qv[D], acc[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) {
+    qv[t] = (r.i < r.q_end) ? qrow[t] : 0.f;
+    acc[t] = 0.f;
+  }
+  // pass 1: row max
+  float m = kNegInf;
+  for (int j = 0; j < r.stop; ++j) m = fmaxf(m, score<D>(p, r, qv, kbase, j));
+  // pass 2: weights and weighted sum of values
+  float l = 0.f;
+  if (m != kNegInf) {
+    for (int j = 0; j < r.stop; ++j) {
+      const float s = score<D>(p, r, qv, kbase, j);
+      if (s == kNegInf) continue;
+      const float e = expf(s - m);
+      l += e;
+      const float* vj = vbase + (int64_t)j * p.v_sl;
+#pragma unroll
+      for (int t = 0; t < D; ++t) acc[t] = fmaf(e, vj[t], acc[t]);
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* orow = reinterpret_cast<float*>(a.o) + r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+#pragma unroll
+  for (int t = 0; t < D; ++t) orow[t] = acc[t] * inv;
+  if (a.lse) a.lse[row] = l > 0.f ? m + logf(l) : kNegInf;
+}
+
+// dQ_i and D_i: one thread per query row.
+template <int D>
+__global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
+  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
+  const RowCtx r = row_ctx(p, row);
+  const int64_t qoff = r.b * p.q_sb + r.h * p.q_sh + (int64_t)r.i * p.q_sl;
+  const int64_t ooff = r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + r.b * p.k_sb + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + r.b * p.v_sb + r.g * p.v_sh;
+  float qv[D], dov[D], dq[D];
+  float Di = 0.f;
+#pragma unroll
+  for (int t = 0; t < D; ++t) {
+    const bool ok = r.i < r.q_end;
+    qv[t] = ok ? reinterpret_cast<const float*>(a.q)[qoff + t] : 0.f;
+    dov[t] = ok ? reinterpret_cast<const float*>(a.dO)[ooff + t] : 0.f;
+    const float ov = ok ? reinterpret_cast<const float*>(a.o)[ooff + t] : 0.f;
+    Di = fmaf(dov[t], ov, Di);
+    dq[t] = 0.f;
+  }
+  const float lse = a.lse[row];
+  if (lse != kNegInf) {
+    for (int j = 0; j < r.stop; ++j) {
+      const float s = score<D>(p, r, qv, kbase, j);
+      if (s == kNegInf) continue;
+      const float P = expf(s - lse);
+      const float* vj = vbase + (int64_t)j * p.v_sl;
+      float dP = 0.f;
+#pragma unroll
+      for (int t = 0; t < D; ++t) dP = fmaf(dov[t], vj[t], dP);
+      const float dS = P * (dP - Di);
+      const float* kj = kbase + (int64_t)j * p.k_sl;
+#pragma unroll
+      for (int t = 0; t < D; ++t) dq[t] = fmaf(dS, kj[t], dq[t]);
+    }
+  } else {
+    Di = 0.f;
+  }
+  float* dqrow = reinterpret_cast<float*>(a.dq) + qoff;
+#pragma unroll
+  for (int t = 0; t < D; ++t) dqrow[t] = dq[t] * p.scale;
+  a.dsum[row] = Di;
+}
+
+// dK_j and dV_j: one thread per key row of a KV head, summing over the query heads it
+// serves and over their rows.
+template <int D>
+__global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int64_t krow = (int64_t)blockIdx.x * kTpb + threadIdx.x;
+  if (krow >= (int64_t)p.B * p.Hkv * p.Lk) return;
+  const int j = (int)(krow % p.Lk);
+  const int g = (int)((krow / p.Lk) % p.Hkv);
+  const int b = (int)(krow / ((int64_t)p.Lk * p.Hkv));
+  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
+  const int64_t koff = b * p.k_sb + g * p.k_sh + (int64_t)j * p.k_sl;
+  const int64_t voff = b * p.v_sb + g * p.v_sh + (int64_t)j * p.v_sl;
+  float kv[D], vv[D], dk[D], dv[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) {
+    const bool ok = j < kv_end;
+    kv[t] = ok ? reinterpret_cast<const float*>(a.k)[koff + t] : 0.f;
+    vv[t] = ok ? reinterpret_cast<const float*>(a.v)[voff + t] : 0.f;
+    dk[t] = 0.f;
+    dv[t] = 0.f;
+  }
+  if (j < kv_end) {
+    const int i_begin = p.causal ? j : 0;
+    for (int hh = 0; hh < p.G; ++hh) {
+      const int h = g * p.G + hh;
+      for (int i = i_begin; i < q_end; ++i) {
+        const int64_t row = ((int64_t)b * p.Hq + h) * p.Lq + i;
+        const float lse = a.lse[row];
+        if (lse == kNegInf) continue;
+        const float* qi = reinterpret_cast<const float*>(a.q) + b * p.q_sb + h * p.q_sh + (int64_t)i * p.q_sl;
+        const float* doi = reinterpret_cast<const float*>(a.dO) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sl;
+        float dot = 0.f;
+#pragma unroll
+        for (int t = 0; t < D; ++t) dot = fmaf(qi[t], kv[t], dot);
+        float s = dot * p.scale;
+        if (p.mask) {
+          const float* m = reinterpret_cast<const float*>(p.mask) + b * p.m_sb + h * p.m_sh + (int64_t)i * p.m_si;
+          s += m[j];
+        }
+        if (s == kNegInf) continue;
+        const float P = expf(s - lse);
+        float dP = 0.f;
+#pragma unroll
+        for (int t = 0; t < D; ++t) dP = fmaf(doi[t], vv[t], dP);
+        const float dS = P * (dP - a.dsum[row]);
+#pragma unroll
+        for (int t = 0; t < D; ++t) {
+          dv[t] = fmaf(P, doi[t], dv[t]);
+          dk[t] = fmaf(dS, qi[t], dk[t]);
+        }
+      }
+    }
+  }
+  float* dkrow = reinterpret_cast<float*>(a.dk) + koff;
+  float* dvrow = reinterpret_cast<float*>(a.dv) + voff;
+#pragma unroll
+  for (int t = 0; t < D; ++t) {
+    dkrow[t] = dk[t] * p.scale;
+    dvrow[t] = dv[t];
+  }
+}
+
+template <int D>
+hipError_t fwd_d(const FwdArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)((rows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t qrows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
+  const int64_t krows = (int64_t)a.p.B * a.p.Hkv * a.p.Lk;
+  if (qrows > 0) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((unsigned)((qrows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (krows > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)((krows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
+  switch (a.p.D) {
+    case 32: return fwd_d<32>(a, s);
+    case 64: return fwd_d<64>(a, s);
+    case 128: return fwd_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s) {
+  switch (a.p.D) {
+    case 32: return bwd_d<32>(a, s);
+    case 64: return bwd_d<64>(a, s);
+    case 128: return bwd_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdpa

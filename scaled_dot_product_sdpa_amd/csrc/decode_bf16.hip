@@ -1,0 +1,233 @@
+// decode_bf16.hip — single-query (L_q = 1) forward with split-KV, bf16, gfx950.
+//
+// Same operation as the prefill forward for one query position per head.  The work is
+// bound by reading the KV cache from HBM ("Understanding PyTorch Scaled Dot-Product
+// Attention" section 5: the KV cache dominates decode), so:
+//  - the G = Hq/Hkv query heads that share a KV head are packed into the N columns of one
+//    MFMA tile (lane l%32 < G is query head g*G + l%32), so each K/V byte is read once for
+//    all of them ("Understanding PyTorch Scaled Dot-Product Attention" section 4 for the
+//    head map);
+//  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
+//    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> registers
+//    -> LDS (prefetched one tile ahead, 16-byte coalesced loads) and writes a partial
+//    (O_c normalised, lse_c); splits past the sequence length exit at once;
+//  - a combine kernel merges the partials exactly:  LSE = ln sum_c exp(lse_c),
+//    O = sum_c exp(lse_c - LSE) O_c  (the log-sum-exp merge of split-KV partial results
+//    that cuDNN "Attention", SDPA FP16/BF16 Forward, Python API describes for its stats).
+#include "kern_common.h"
+#include "launch.h"
+
+namespace sdpa {
+namespace {
+
+constexpr int kDT = 32;  // keys per tile
+
+template <int D>
+struct DecTile {
+  static constexpr int KP = D + 8;
+  static constexpr int VP = D + 8;
+  static constexpr int CPR = D / 8;
+  static constexpr int NCH = kDT * CPR / 64;  // 16-byte chunks per lane per tensor
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using T = DecTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kDT * T::KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kDT * T::VP];
+  const Problem& p = a.p;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int c = blockIdx.x % a.n_split;
+  const int bg = blockIdx.x / a.n_split;
+  const int b = bg / p.Hkv;
+  const int g = bg % p.Hkv;
+  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int k0 = c * a.split_keys;
+  if (k0 >= kv_end) return;  // the combine reads only splits that hold keys
+  const int k1 = min(k0 + a.split_keys, kv_end);
+  const int n_tiles = (k1 - k0 + kDT - 1) / kDT;
+
+  const bool qvalid = l32 < p.G;
+  const int h = g * p.G + (qvalid ? l32 : 0);
+  const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 16 + 8 * hi) : zero16());
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
+  float mrow = kNegInf, lrow = 0.f, frow = 0.f;  // max, rounded-weight sum, fp32-weight sum
+
+  u32x4 kst[T::NCH], vst[T::NCH];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < T::NCH; ++u) {
+      const int idx = lane + u * 64;
+      const int r = idx / T::CPR, cc = idx % T::CPR;
+      const int row = j0 + r;
+      const bool ok = row < k1;
+      kst[u] = ok ? ld16(kbase + (int64_t)row * p.k_sl + cc * 8) : zero16();
+      vst[u] = ok ? ld16(vbase + (int64_t)row * p.v_sl + cc * 8) : zero16();
+    }
+  };
+  load_tile(k0);
+  const int blk = lane >> 4;
+  const int arow = (lane & 15) >> 2;
+  const int acol = 4 * (lane & 3) + 16 * (blk & 1);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int j0 = k0 + t * kDT;
+#pragma unroll
+    for (int u = 0; u < T::NCH; ++u) {
+      const int idx = lane + u * 64;
+      const int r = idx / T::CPR, cc = idx % T::CPR;
+      *reinterpret_cast<u32x4*>(&Ks[r * T::KP + cc * 8]) = kst[u];
+      *reinterpret_cast<u32x4*>(&Vs[r * T::VP + cc * 8]) = vst[u];
+    }
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(j0 + kDT);
+
+    f32x16 sacc = f32x16{};
+    const bf16* krow = &Ks[perm_row(l32) * T::KP + 8 * hi];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qreg[kk], sacc);
+
+    const bool partial = j0 + kDT > k1;
+    float s[16];
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = sacc[v] * p.scale_log2;
+      if (partial) x = (j0 + 16 * hi + v < k1) ? x : kNegInf;
+      s[v] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(mrow, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float corr = fast_exp2(mrow - m_use);
+    mrow = m_new;
+    bf16x8 pop[2];
+    float psum = 0.f, fsum = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        const float pf = fast_exp2(s[half * 8 + t8] - m_use);
+        const bf16 e = (bf16)pf;
+        pop[half][t8] = e;
+        psum += bf2f(e);
+        fsum += pf;
+      }
+    }
+    lrow = lrow * corr + psum;
+    frow = frow * corr + fsum;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16* vrow = &Vs[(16 * hi + 8 * half + arow) * T::VP + acol];
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        bf16x8 vop = join_tr(lds_read_tr4(vrow + mb * 32), lds_read_tr4(vrow + 4 * T::VP + mb * 32));
+        oacc[mb] = mfma32(vop, pop[half], oacc[mb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  const float lt = xhalf_sum(lrow);
+  const float ft = xhalf_sum(frow);
+  if (qvalid) {
+    const int64_t prow = ((int64_t)b * p.Hq + h) * a.n_split + c;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[mb][v4 * 4 + e] * inv;
+        *reinterpret_cast<f32x4*>(po + mb * 32 + v4 * 8 + hi * 4) = w;
+      }
+    }
+    if (hi == 0) a.part_lse[prow] = lt > 0.f ? (mrow * kLn2 + logf(ft)) : kNegInf;
+  }
+}
+
+// One workgroup of D/4 threads per (batch, query head): merge the live splits.
+template <int D>
+__global__ __launch_bounds__(D / 4) void decode_combine_kernel(DecodeArgs a) {
+  const Problem& p = a.p;
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq;
+  const int h = bh % p.Hq;
+  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int n_live = (kv_end + a.split_keys - 1) / a.split_keys;
+  const float* pl = a.part_lse + (int64_t)bh * a.n_split;
+  const float* po = a.part_o + (int64_t)bh * a.n_split * D;
+  float M = kNegInf;
+  for (int c = 0; c < n_live; ++c) M = fmaxf(M, pl[c]);
+  float L = 0.f;
+  const int d0 = threadIdx.x * 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != kNegInf) {
+    for (int c = 0; c < n_live; ++c) {
+      const float w = expf(pl[c] - M);
+      L += w;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(po + (int64_t)c * D + d0);
+      acc += w * x;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  bf16x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[e] * inv);
+  bf16* orow = reinterpret_cast<bf16*>(a.o) + b * p.o_sb + h * p.o_sh;
+  *reinterpret_cast<bf16x4*>(orow + d0) = out;
+  if (a.lse && threadIdx.x == 0) a.lse[bh] = (L > 0.f) ? M + logf(L) : kNegInf;
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  const int grid = a.p.B * a.p.Hkv * a.n_split;
+  if (grid > 0) {
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(grid), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.p.B * a.p.Hq), dim3(D / 4), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void decode_split_plan(int B, int Hkv, int Lk, int* split_keys, int* n_split) {
+  // Enough splits that the (batch, KV head) pairs times splits fill the chip several
+  // times over, without partial-result traffic becoming noticeable.
+  int sk = 256;
+  const int64_t pairs = (int64_t)B * Hkv;
+  while (sk > kDT && pairs * ((Lk + sk - 1) / sk) < 2048) sk /= 2;
+  *split_keys = sk;
+  *n_split = Lk > 0 ? (Lk + sk - 1) / sk : 1;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  switch (a.p.D) {
+    case 64: return launch_d<64>(a, s);
+    case 128: return launch_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,87 @@
+// kern_common.h — device-side building blocks shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (wave64, measured on gfx950 with a lane-layout probe):
+//   v_mfma_f32_32x32x16_bf16  D(32x32) += A(32x16) * B(16x32)
+//     A: lane l holds A[l%32][8*(l/32) + t], t = 0..7      (one row, 8 consecutive k)
+//     B: lane l holds B[8*(l/32) + t][l%32], t = 0..7      (one column, 8 consecutive k)
+//     D: lane l holds D[(v/4)*8 + (l/32)*4 + v%4][l%32], v = 0..15
+//   ds_read_b64_tr_b16 within each 16-lane block: lane j supplies the address of a row of
+//   four 16-bit elements R_j[0..3]; lane i receives { R_{4s + i/4}[i%4] : s = 0..3 }.
+//
+// Row permutation used by every kernel: when the 32 M-rows of an MFMA are keys (or
+// queries) we place token  tok(r) = 16*((r>>2)&1) + 4*(r>>3) + (r&3)  at M-row r.  Then the
+// accumulator of lane l holds tokens 16*(l/32) + v for v = 0..15 — sixteen consecutive
+// tokens per lane, so a lane's half of the D tile feeds the next MFMA as a k-slice of 8
+// consecutive tokens without any data movement.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Token placed at M-row r of a 32-row MFMA block (see the header comment).
+__device__ __forceinline__ int perm_row(int r) {
+  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of a value over lanes l and l^32 (v_permlane32_swap returns both halves).
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// bf16 -> fp32 (exact).
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// Eight fp32 -> eight bf16, round to nearest even.
+__device__ __forceinline__ bf16x8 f32x8_to_bf16(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (bf16)x[t];
+  return r;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// LDS transposing read of four bf16 (see header comment for the lane mapping).
+__device__ __forceinline__ i16x4 lds_read_tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+}  // namespace sdpa

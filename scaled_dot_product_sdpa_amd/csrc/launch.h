@@ -1,0 +1,72 @@
+// launch.h — internal interface between the C-ABI host layer and the kernel sources.
+// Not installed; the public interface is include/sdpa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// Everything a kernel needs about one problem; strides are in elements.
+struct Problem {
+  int B, Hq, Hkv, G, Lq, Lk, D;  // G = Hq / Hkv; D = Dqk = Dv
+  int64_t q_sb, q_sh, q_sl;
+  int64_t k_sb, k_sh, k_sl;
+  int64_t v_sb, v_sh, v_sl;
+  int64_t o_sb, o_sh, o_sl;
+  int64_t m_sb, m_sh, m_si;
+  float scale;       // resolved scale
+  float scale_log2;  // scale * log2(e)
+  int causal;
+  const int32_t* len_q;   // may be null
+  const int32_t* len_kv;  // may be null
+  const void* mask;       // may be null (additive, io dtype)
+  int mask_vec;           // mask rows may be read with 16-byte vector loads
+};
+
+struct FwdArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+};
+
+struct BwdArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D = rowsum(dO o O), contiguous (B, Hq, Lq)
+};
+
+struct DecodeArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;       // may be null
+  float* part_o;    // workspace (B, Hq, n_split, D) fp32
+  float* part_lse;  // workspace (B, Hq, n_split) fp32
+  int split_keys;   // keys per split
+  int n_split;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+// Split-KV geometry used by the decode path (keys per split and number of splits).
+void decode_split_plan(int B, int Hkv, int Lk, int* split_keys, int* n_split);
+
+}  // namespace sdpa

@@ -1,0 +1,247 @@
+// sdpa_api.cpp — the C ABI declared in include/sdpa.h: argument validation, workspace
+// sizing and kernel selection.  Nothing here computes attention; every step of the
+// operation runs in the HIP kernels behind launch.h.
+//
+// Validation follows the contracts the pages state: q and k share the key width and k and
+// v share the key length (Lucid ScaledDotProductAttentionBackward, forward); Hq is a
+// multiple of Hkv (the GQA head map of "Understanding PyTorch Scaled Dot-Product
+// Attention", section 4); a bad scale or mismatched shape fails loudly ("Scaled
+// dot-product attention (forward and backward)", section 4, test_rejects_bad_arguments);
+// one element type for all io tensors and rejection instead of silent resolution (cuDNN
+// "Attention", SDPA PyTorch Custom Ops, Contracts and limits).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/sdpa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sdpa_status fail(sdpa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool aligned_to(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == SDPA_DTYPE_BF16 ? 2 : 4; }
+
+// Shape / dtype / scale checks that do not involve pointers.
+sdpa_status check_problem(const sdpa_problem* p) {
+  if (!p) return fail(SDPA_ERR_INVALID_ARGUMENT, "problem pointer is null");
+  if (p->dtype != SDPA_DTYPE_F32 && p->dtype != SDPA_DTYPE_BF16)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Lq < 0 || p->Lk < 0 || p->Dqk < 1 || p->Dv < 1)
+    return fail(SDPA_ERR_INVALID_ARGUMENT,
+                "sizes must satisfy B, Hq, Hkv, Dqk, Dv >= 1 and Lq, Lk >= 0 (got B=%d Hq=%d "
+                "Hkv=%d Lq=%d Lk=%d Dqk=%d Dv=%d)",
+                p->B, p->Hq, p->Hkv, p->Lq, p->Lk, p->Dqk, p->Dv);
+  if (p->Hq % p->Hkv != 0)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!std::isnan(p->scale) && !(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be NaN (default) or finite and > 0");
+  if (p->Dqk != p->Dv)
+    return fail(SDPA_ERR_UNSUPPORTED, "Dqk (%d) != Dv (%d) is not supported", p->Dqk, p->Dv);
+  if (p->dtype == SDPA_DTYPE_BF16 && p->Dqk != 64 && p->Dqk != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "bf16 head dim %d not supported (64, 128)", p->Dqk);
+  if (p->dtype == SDPA_DTYPE_F32 && p->Dqk != 32 && p->Dqk != 64 && p->Dqk != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "fp32 head dim %d not supported (32, 64, 128)", p->Dqk);
+  // bf16 kernels move q/k/v/o rows in 16-byte vectors; the fp32 kernels use scalar loads.
+  // Mask rows of any stride are accepted (vector loads are used only when aligned).
+  const int64_t vec = p->dtype == SDPA_DTYPE_BF16 ? 8 : 1;
+  const int64_t* strides[5] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride, p->mask_stride};
+  const char* names[5] = {"q", "k", "v", "o", "mask"};
+  // A stride only matters along a dimension of size > 1 (the mask may broadcast b and h).
+  const int32_t dims[5][3] = {{p->B, p->Hq, p->Lq}, {p->B, p->Hkv, p->Lk}, {p->B, p->Hkv, p->Lk},
+                              {p->B, p->Hq, p->Lq}, {p->B, p->Hq, p->Lq}};
+  for (int t = 0; t < 5; ++t)
+    for (int a = 0; a < 3; ++a) {
+      if (strides[t][a] < 0)
+        return fail(SDPA_ERR_INVALID_ARGUMENT, "%s stride %d is negative", names[t], a);
+      if (t < 4 && dims[t][a] > 1 && strides[t][a] % vec != 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "%s stride %d (%lld) is not a multiple of %lld elements",
+                    names[t], a, (long long)strides[t][a], (long long)vec);
+    }
+  // Rows of one (b, h) must not overlap: the row stride covers the row.
+  if (p->Lq > 1 && p->q_stride[2] < p->Dqk) return fail(SDPA_ERR_INVALID_ARGUMENT, "q rows overlap");
+  if (p->Lk > 1 && p->k_stride[2] < p->Dqk) return fail(SDPA_ERR_INVALID_ARGUMENT, "k rows overlap");
+  if (p->Lk > 1 && p->v_stride[2] < p->Dv) return fail(SDPA_ERR_INVALID_ARGUMENT, "v rows overlap");
+  if (p->Lq > 1 && p->o_stride[2] < p->Dv) return fail(SDPA_ERR_INVALID_ARGUMENT, "o rows overlap");
+  return SDPA_OK;
+}
+
+bool use_decode(const sdpa_problem* p, bool has_mask) {
+  return p->dtype == SDPA_DTYPE_BF16 && p->Lq == 1 && !p->is_causal && !has_mask &&
+         p->Hq / p->Hkv <= 32;
+}
+
+sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_t* lq,
+                           const int32_t* lk) {
+  sdpa::Problem k{};
+  k.B = p->B; k.Hq = p->Hq; k.Hkv = p->Hkv; k.G = p->Hq / p->Hkv;
+  k.Lq = p->Lq; k.Lk = p->Lk; k.D = p->Dqk;
+  k.q_sb = p->q_stride[0]; k.q_sh = p->q_stride[1]; k.q_sl = p->q_stride[2];
+  k.k_sb = p->k_stride[0]; k.k_sh = p->k_stride[1]; k.k_sl = p->k_stride[2];
+  k.v_sb = p->v_stride[0]; k.v_sh = p->v_stride[1]; k.v_sl = p->v_stride[2];
+  k.o_sb = p->o_stride[0]; k.o_sh = p->o_stride[1]; k.o_sl = p->o_stride[2];
+  k.m_sb = p->mask_stride[0]; k.m_sh = p->mask_stride[1]; k.m_si = p->mask_stride[2];
+  k.scale = std::isnan(p->scale) ? 1.0f / std::sqrt((float)p->Dqk) : p->scale;
+  k.scale_log2 = k.scale * 1.4426950408889634f;
+  k.causal = p->is_causal ? 1 : 0;
+  k.len_q = lq;
+  k.len_kv = lk;
+  k.mask = mask;
+  // 16-byte mask vectors need every (b, h, i) row start 16-byte aligned
+  k.mask_vec = mask != nullptr && p->dtype == SDPA_DTYPE_BF16 && aligned16(mask) &&
+               (p->B == 1 || k.m_sb % 8 == 0) && (p->Hq == 1 || k.m_sh % 8 == 0) &&
+               (p->Lq == 1 || k.m_si % 8 == 0);
+  return k;
+}
+
+sdpa_status check_ptr(const void* ptr, const char* name, bool required, uintptr_t align) {
+  if (!ptr) {
+    if (required) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s is null", name);
+    return SDPA_OK;
+  }
+  if (!aligned_to(ptr, align))
+    return fail(SDPA_ERR_UNSUPPORTED, "%s is not %d-byte aligned", name, (int)align);
+  return SDPA_OK;
+}
+
+// io tensors: 16-byte alignment for bf16 (vector loads), 4 for fp32; the mask needs only
+// its element alignment, the length arrays 4 bytes.
+sdpa_status check_ptrs(int dtype, std::initializer_list<std::pair<const void*, const char*>> req,
+                       const void* mask, const void* lq, const void* lk, const void* lse,
+                       bool lse_required) {
+  const uintptr_t io = dtype == SDPA_DTYPE_BF16 ? 16 : 4;
+  for (auto& x : req) {
+    sdpa_status s = check_ptr(x.first, x.second, true, io);
+    if (s != SDPA_OK) return s;
+  }
+  sdpa_status s = check_ptr(mask, "mask", false, dtype == SDPA_DTYPE_BF16 ? 2 : 4);
+  if (s == SDPA_OK) s = check_ptr(lq, "seq_lens_q", false, 4);
+  if (s == SDPA_OK) s = check_ptr(lk, "seq_lens_kv", false, 4);
+  if (s == SDPA_OK) s = check_ptr(lse, "lse", lse_required, 4);
+  return s;
+}
+
+sdpa_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_last_error.clear();
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdpa_forward_workspace_bytes(const sdpa_problem* p) {
+  if (check_problem(p) != SDPA_OK) return 0;
+  if (!use_decode(p, false)) return 0;
+  int sk = 0, ns = 0;
+  sdpa::decode_split_plan(p->B, p->Hkv, p->Lk, &sk, &ns);
+  const size_t rows = (size_t)p->B * p->Hq * ns;
+  return round_up(rows * p->Dv * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+size_t sdpa_backward_workspace_bytes(const sdpa_problem* p) {
+  if (check_problem(p) != SDPA_OK) return 0;
+  return round_up((size_t)p->B * p->Hq * p->Lq * sizeof(float));
+}
+
+sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* mask, const int32_t* lq, const int32_t* lk, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa_status st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  st = check_ptrs(p->dtype, {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}}, mask, lq, lk, lse, false);
+  if (st != SDPA_OK) return st;
+  (void)elem_bytes;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  sdpa::Problem kp = make_problem(p, mask, lq, lk);
+  if (p->Lq == 0) {
+    g_last_error.clear();
+    return SDPA_OK;
+  }
+  if (p->dtype == SDPA_DTYPE_F32) {
+    sdpa::FwdArgs a{kp, q, k, v, o, lse};
+    return hip_result(sdpa::launch_fwd_f32(a, s), "fp32 forward launch");
+  }
+  if (use_decode(p, mask != nullptr)) {
+    const size_t need = sdpa_forward_workspace_bytes(p);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "forward (decode) needs %zu workspace bytes, got %zu",
+                  need, workspace_bytes);
+    if (need > 0 && !aligned16(workspace))
+      return fail(SDPA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+    sdpa::DecodeArgs a{};
+    a.p = kp; a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    sdpa::decode_split_plan(p->B, p->Hkv, p->Lk, &a.split_keys, &a.n_split);
+    const size_t rows = (size_t)p->B * p->Hq * a.n_split;
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                          round_up(rows * p->Dv * sizeof(float)));
+    return hip_result(sdpa::launch_decode_bf16(a, s), "decode launch");
+  }
+  sdpa::FwdArgs a{kp, q, k, v, o, lse};
+  return hip_result(sdpa::launch_fwd_bf16(a, s), "bf16 forward launch");
+}
+
+sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                          const void* o, const void* dO, const float* lse, const void* mask,
+                          const int32_t* lq, const int32_t* lk, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa_status st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  st = check_ptrs(p->dtype, {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dO, "dO"}, {dq, "dq"},
+                             {dk, "dk"}, {dv, "dv"}},
+                  mask, lq, lk, lse, true);
+  if (st != SDPA_OK) return st;
+  const size_t need = sdpa_backward_workspace_bytes(p);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  if (need > 0 && !aligned16(workspace))
+    return fail(SDPA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  sdpa::BwdArgs a{};
+  a.p = make_problem(p, mask, lq, lk);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsum = reinterpret_cast<float*>(workspace);
+  if (p->dtype == SDPA_DTYPE_F32) return hip_result(sdpa::launch_bwd_f32(a, s), "fp32 backward launch");
+  return hip_result(sdpa::launch_bwd_bf16(a, s), "bf16 backward launch");
+}
+
+const char* sdpa_status_string(sdpa_status s) {
+  switch (s) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SDPA_ERR_UNSUPPORTED: return "unsupported";
+    case SDPA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SDPA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* sdpa_last_error(void) { return g_last_error.c_str(); }
+
+int sdpa_version(void) { return 100; }
+
+}  // extern "C"
