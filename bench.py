@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the scaled dot-product attention hot path on one MI355X.
+
+One step = the whole hot path over one batch of the headline workload (causal MHA
+prefill, B=4, H=16, L=1024, d=64, bf16): forward (O, LSE) then backward (D prep, dK/dV,
+dQ).  The step is captured once into a HIP graph and replayed; inputs are resident in HBM
+before the timed region starts.  Prints ONE JSON line.
+
+Also reported (same line, "workloads"): the other workloads' forward / backward TFLOP/s
+and the GQA decode's HBM GB/s, the per-kernel durations (HIP events around graph
+replays of that kernel alone), the roofline of the dominant kernel, and the fp64 CPU
+oracle timed on the host cores as a baseline.
+
+FLOP convention: pairs (i, j) a query may attend to (causal and lengths applied, the
+random mask entries not subtracted); forward 2 (Dqk + Dv) flops per pair, backward
+2 (3 Dqk + 2 Dv).  Decode GB/s counts the K/V rows read (valid lengths), q, o and lse.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "SDPA fwd / fwd+bwd TFLOP/s (+% bf16 MFMA peak); decode GB/s (+% HBM)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+HEADLINE = "mha_causal_1k"
+
+# kernel-name fragments (as rocprofv3 reports them) of each launch stage
+KERNEL_NAMES = {
+    "fwd": "fwd_bf16_kernel", "prep": "bwd_prep_kernel", "dkdv": "bwd_dkdv_kernel",
+    "dq": "bwd_dq_kernel", "decode_split": "decode_split_kernel",
+    "decode_combine": "decode_combine_kernel",
+}
+# source file of each kernel (traffic counters are dropped once the source changes)
+KERNEL_SOURCES = {
+    "fwd": "fwd_bf16.hip", "prep": "bwd_bf16.hip", "dkdv": "bwd_bf16.hip", "dq": "bwd_bf16.hip",
+    "decode_split": "decode_bf16.hip", "decode_combine": "decode_bf16.hip",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(stage: str) -> str:
+    src = ROOT / "scaled_dot_product_sdpa_amd" / "csrc" / KERNEL_SOURCES[stage]
+    h = hashlib.sha256(src.read_bytes())
+    h.update((ROOT / "scaled_dot_product_sdpa_amd" / "csrc" / "kern_common.h").read_bytes())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(w, len_q=None, len_kv=None) -> int:
+    """Number of (b, h, i, j) a query may attend to under causality and lengths."""
+    import numpy as np
+    lq = np.full(w.B, w.Lq) if len_q is None else np.asarray(len_q.cpu()).astype(np.int64)
+    lk = np.full(w.B, w.Lk) if len_kv is None else np.asarray(len_kv.cpu()).astype(np.int64)
+    total = 0
+    for b in range(w.B):
+        i = np.arange(int(lq[b]))
+        n = np.minimum(i + 1, lk[b]) if w.causal else np.full(i.shape, lk[b])
+        total += int(n.sum())
+    return total * w.Hq
+
+
+def flops(w, pairs):
+    fwd = 2 * (w.D + w.D) * pairs
+    bwd = 2 * (3 * w.D + 2 * w.D) * pairs
+    # per-kernel algorithmic shares of the backward: dK/dV does S, dP, dV, dK; dQ adds dQ
+    return {"fwd": fwd, "bwd": bwd, "dkdv": 2 * (2 * w.D + 2 * w.D) * pairs, "dq": 2 * w.D * pairs}
+
+
+class Timer:
+    """Graph-replay timing on the current stream with HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def capture(self, fn, reps=1):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()  # warm the launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g, iters, warmup=2):
+        torch = self.torch
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters  # ms per replay
+
+
+def kernel_ms(timer, fn, reps=20, iters=5):
+    """Average duration of one launch of fn: a graph of `reps` back-to-back launches."""
+    g = timer.capture(fn, reps=reps)
+    return timer.time_graph(g, iters) / reps
+
+
+def run_workload(torch, timer, name, w, iters, want_bwd=True):
+    """Per-stage kernel times and throughput of one workload."""
+    from scaled_dot_product_sdpa_amd import BackwardCall, ForwardCall
+    from scaled_dot_product_sdpa_amd.workloads import make_inputs
+    inp = make_inputs(w, device="cuda")
+    fc = ForwardCall(inp["q"], inp["k"], inp["v"], inp["mask"], inp["scale"], inp["is_causal"],
+                     inp["len_q"], inp["len_kv"])
+    fc.launch()
+    torch.cuda.synchronize()
+    res = {"config": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lk": w.Lk, "D": w.D,
+                      "causal": w.causal, "mask": inp["mask"] is not None,
+                      "lens": inp["len_kv"] is not None, "dtype": w.dtype}}
+    t = {"fwd": kernel_ms(timer, fc.launch, reps=10, iters=iters)}
+    if w.Lq == 1:
+        # decode: algorithmic bytes = K/V rows within the lengths + q + o + lse
+        lk = inp["len_kv"].to(torch.int64).sum().item() if inp["len_kv"] is not None else w.B * w.Lk
+        nbytes = lk * w.Hkv * 2 * w.D * 2 + w.B * w.Hq * (2 * w.D * 2 + 4)
+        gbs = nbytes / (t["fwd"] * 1e-3) / 1e9
+        res.update(ms={"fwd": t["fwd"]}, bytes=nbytes, GBps=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
+        return res, inp, fc, None
+    pairs = visible_pairs(w, inp["len_q"], inp["len_kv"])
+    fl = flops(w, pairs)
+    bc = None
+    if want_bwd and w.backward:
+        o, lse = fc.result()
+        bc = BackwardCall(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, inp["mask"],
+                          inp["scale"], inp["is_causal"], inp["len_q"], inp["len_kv"])
+        bc.launch()
+        torch.cuda.synchronize()
+        for st in ("prep", "dkdv", "dq"):
+            t[st] = kernel_ms(timer, lambda st=st: bc.launch(st), reps=10, iters=iters)
+        t["bwd"] = t["prep"] + t["dkdv"] + t["dq"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    tf = {"fwd": fl["fwd"] / (t["fwd"] * 1e-3) / 1e12}
+    if "bwd" in t:
+        tf["bwd"] = fl["bwd"] / (t["bwd"] * 1e-3) / 1e12
+        tf["fwd+bwd"] = (fl["fwd"] + fl["bwd"]) / ((t["fwd"] + t["bwd"]) * 1e-3) / 1e12
+    res.update(pairs=pairs, gflop={k: v / 1e9 for k, v in fl.items()}, ms=t, TFLOPs=tf,
+               peak_frac={k: v / peak for k, v in tf.items()})
+    return res, inp, fc, bc
+
+
+def cpu_baseline(w, inp):
+    """The fp64 oracle (as it stands) on the host cores, on the headline workload's step."""
+    from oracle import load_oracle
+    orc = load_oracle()
+    f = lambda t: None if t is None else t.detach().double().cpu().numpy()
+    q, k, v, dO = f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["dO"])
+    t0 = time.perf_counter()
+    orc.forward(q, k, v, scale=w.scale, is_causal=w.causal)
+    t1 = time.perf_counter()
+    orc.backward(q, k, v, dO, scale=w.scale, is_causal=w.causal)
+    t2 = time.perf_counter()
+    fl = flops(w, visible_pairs(w))
+    return {"value": (fl["fwd"] + fl["bwd"]) / (t2 - t0) / 1e12, "unit": "TFLOP/s",
+            "cores": orc.num_threads, "kind": "oracle",
+            "sample": f"the full {HEADLINE} step (fwd + bwd over all {w.B}x{w.Hq} heads), fp64",
+            "seconds": {"fwd": t1 - t0, "bwd": t2 - t1}}
+
+
+def traffic_for(stage, launches_per_step=1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current source of that kernel (else None)."""
+    path = ROOT / "profiles" / "traffic.json"
+    if not path.exists():
+        return None
+    try:
+        data = json.loads(path.read_text())
+    except ValueError:
+        return None
+    ent = data.get(stage)
+    if not ent or ent.get("source_hash") != source_hash(stage):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads to run")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(sharding across GPUs is not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from scaled_dot_product_sdpa_amd import load_library
+    from scaled_dot_product_sdpa_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    load_library()
+    timer = Timer(torch)
+    w = WORKLOADS[HEADLINE]
+
+    # ---- headline: the whole step, graph-replayed
+    log(f"headline {HEADLINE}: building inputs")
+    head, inp, fc, bc = run_workload(torch, timer, HEADLINE, w, iters=5)
+
+    def step():
+        fc.launch()
+        bc.launch("prep")
+        bc.launch("dkdv")
+        bc.launch("dq")
+
+    g = timer.capture(step)
+    # the replayed graph must reproduce the eager step bit for bit
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)]
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)):
+        if not torch.equal(a, b):
+            raise SystemExit("bench.py: graph replay differs from the eager step")
+
+    log(f"headline: {args.warmup} warmup + {args.steps} timed steps")
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    gfl = head["gflop"]
+    value = (gfl["fwd"] + gfl["bwd"]) * 1e9 / (ms_per_step * 1e-3) / 1e12
+
+    # ---- dominant kernel of the step and its roofline
+    kt = {k: head["ms"][k] for k in ("fwd", "prep", "dkdv", "dq")}
+    dom = max(kt, key=kt.get)
+    if dom == "prep":
+        nbytes = w.B * w.Hq * w.Lq * (2 * w.D * 2 + 4)
+        roof = {"bound": "hbm", "achieved": nbytes / (kt[dom] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        fl_dom = gfl[dom] * 1e9
+        roof = {"bound": "mfma", "achieved": fl_dom / (kt[dom] * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(dom)
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel_ms"] = kt[dom]
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": HEADLINE, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.Lq, "D": w.D,
+                   "causal": True, "step": "fwd + bwd (prep, dkdv, dq)"},
+        "peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "kernels_ms": kt,
+    }
+
+    # ---- other workloads
+    if not args.no_extra:
+        names = ["gqa_causal_4k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32"]
+        if args.only:
+            names = [n for n in names if n in args.only.split(",")]
+        extra = {}
+        for name in names:
+            log(f"workload {name}")
+            res, _, fc2, bc2 = run_workload(torch, timer, name, WORKLOADS[name], iters=3)
+            extra[name] = res
+            del fc2, bc2
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
+
+    # ---- CPU baseline (rank 0, N = 1 only)
+    if not args.no_cpu:
+        log("cpu baseline: fp64 oracle on the headline step")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,6 +117,32 @@ sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, c
                           const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three stages sdpa_backward runs, in this order, for callers that schedule them
+ * themselves.  Same arguments, validation and workspace as sdpa_backward.
+ *   prep: D_i = rowsum(dO o O)_i (fp32, into the workspace; 0 for empty rows);
+ *   dkdv: dK and dV (reads D from the workspace);
+ *   dq:   dQ       (reads D from the workspace).
+ * Once prep has finished, dkdv and dq are independent of each other and may run
+ * concurrently on two streams.  Source: the backward of tinyllm L5.1 section 2.3, with D
+ * computed from the output as that section's identity D_i = dO_i . o_i allows.
+ */
+sdpa_status sdpa_backward_prep(const sdpa_problem* p, const void* q, const void* k,
+                               const void* v, const void* o, const void* dO, const float* lse,
+                               const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                               const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+sdpa_status sdpa_backward_dkdv(const sdpa_problem* p, const void* q, const void* k,
+                               const void* v, const void* o, const void* dO, const float* lse,
+                               const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                               const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+sdpa_status sdpa_backward_dq(const sdpa_problem* p, const void* q, const void* k,
+                             const void* v, const void* o, const void* dO, const float* lse,
+                             const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                             const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 const char* sdpa_status_string(sdpa_status s);
 
 /* Text of the last failure on the calling thread ("" if none). */

@@ -10,8 +10,8 @@ Importing the package does not load the library; the first call does, and fails 
 has not been built (``python -m scaled_dot_product_sdpa_amd.build``).
 """
 
-from .api import (EXPORTS, LIB_PATH, Problem, SdpaError, load_library, sdpa_backward,
-                  sdpa_forward)
+from .api import (BACKWARD_STAGES, EXPORTS, LIB_PATH, BackwardCall, ForwardCall, Problem,
+                  SdpaError, load_library, sdpa_backward, sdpa_forward)
 
-__all__ = ["sdpa_forward", "sdpa_backward", "load_library", "LIB_PATH", "EXPORTS", "Problem",
-           "SdpaError"]
+__all__ = ["sdpa_forward", "sdpa_backward", "ForwardCall", "BackwardCall", "BACKWARD_STAGES",
+           "load_library", "LIB_PATH", "EXPORTS", "Problem", "SdpaError"]

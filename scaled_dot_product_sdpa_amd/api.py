@@ -4,6 +4,10 @@ Argument marshalling only: shapes and strides are read off torch tensors, output
 workspace are allocated with torch on the inputs' device, and the call is forwarded to the
 C ABI on torch's current stream.  Every step of the attention itself runs in the HIP
 kernels; there is no fallback path.  If the library is missing the call fails.
+
+``ForwardCall`` / ``BackwardCall`` marshal once and then launch with the cached
+arguments (used for timing and for capture into HIP graphs); ``sdpa_forward`` /
+``sdpa_backward`` are the one-shot forms.
 """
 
 from __future__ import annotations
@@ -27,8 +31,10 @@ SDPA_DTYPE_BF16 = 1
 
 EXPORTS = (
     "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes", "sdpa_forward",
-    "sdpa_backward", "sdpa_status_string", "sdpa_last_error", "sdpa_version",
+    "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
+    "sdpa_status_string", "sdpa_last_error", "sdpa_version",
 )
+BACKWARD_STAGES = ("prep", "dkdv", "dq")
 
 
 class Problem(ctypes.Structure):
@@ -71,8 +77,10 @@ def load_library(path: Path | str | None = None):
     lib.sdpa_backward_workspace_bytes.restype = sz
     lib.sdpa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_forward.restype = ctypes.c_int
-    lib.sdpa_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.sdpa_backward.restype = ctypes.c_int
+    for name in ("sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq"):
+        f = getattr(lib, name)
+        f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []
@@ -83,7 +91,7 @@ def load_library(path: Path | str | None = None):
     return lib
 
 
-def _raise(lib, status: int):
+def raise_status(lib, status: int):
     msg = lib.sdpa_last_error().decode()
     name = lib.sdpa_status_string(status).decode()
     text = f"sdpa: {name}: {msg}"
@@ -150,7 +158,7 @@ def _lens(x, B, device, name):
     return x.to(device=device, dtype=torch.int32).contiguous()
 
 
-def _ptr(t):
+def _vp(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
@@ -187,68 +195,110 @@ def _check_io(*ts):
             raise ValueError("sdpa: q, k, v (and o, dO, mask) must share one dtype")
 
 
+class ForwardCall:
+    """Marshalled forward: outputs ``o``, ``lse`` and the workspace are allocated once;
+    ``launch()`` enqueues the kernels on the current stream with the cached arguments."""
+
+    def __init__(self, q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
+                 seq_lens_kv=None, return_lse=True):
+        self.lib = load_library()
+        self.squeeze = q.dim() == 3
+        q, k, v = _as4d(q, "q"), _as4d(k, "k"), _as4d(v, "v")
+        _check_io(q, k, v, *([mask] if mask is not None else []))
+        B, Hq, Lq, _ = q.shape
+        Lk, Dv = k.shape[2], v.shape[3]
+        self.o = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+        self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+        m, mst = _mask4d(mask, B, Hq, Lq, Lk)
+        self.p = make_problem(q, k, v, _strides3(self.o, "o"), mst, scale, is_causal)
+        lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
+        lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
+        nws = self.lib.sdpa_forward_workspace_bytes(ctypes.byref(self.p))
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k, v, m, lq, lk)
+        self.device = q.device
+        self.args = [ctypes.byref(self.p), _vp(q), _vp(k), _vp(v), _vp(m), _vp(lq), _vp(lk),
+                     _vp(self.o), _vp(self.lse), _vp(self.ws), nws]
+
+    def launch(self):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        st = self.lib.sdpa_forward(*self.args, stream)
+        if st != SDPA_OK:
+            raise_status(self.lib, st)
+
+    def result(self):
+        o, lse = self.o, self.lse
+        if self.squeeze:
+            o = o.squeeze(0)
+            lse = lse.squeeze(0) if lse is not None else None
+        return o, lse
+
+
+class BackwardCall:
+    """Marshalled backward: dq, dk, dv and the workspace are allocated once; ``launch()``
+    runs all stages, ``launch(stage)`` one of "prep", "dkdv", "dq" (prep must precede the
+    other two)."""
+
+    def __init__(self, q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
+                 seq_lens_q=None, seq_lens_kv=None):
+        self.lib = load_library()
+        self.squeeze = q.dim() == 3
+        q, k, v, o, dO = (_as4d(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")))
+        if lse.dim() == 2:
+            lse = lse.unsqueeze(0)
+        _check_io(q, k, v, o, dO, *([mask] if mask is not None else []))
+        B, Hq, Lq, _ = q.shape
+        Lk = k.shape[2]
+        if tuple(o.shape) != (B, Hq, Lq, v.shape[3]) or dO.shape != o.shape:
+            raise ValueError("sdpa: o and dO must be (B, Hq, Lq, Dv)")
+        if o.stride() != dO.stride():
+            dO = dO.contiguous()
+            o = o.contiguous()
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
+            raise ValueError("sdpa: lse must be float32 (B, Hq, Lq)")
+        lse = lse.contiguous()
+        m, mst = _mask4d(mask, B, Hq, Lq, Lk)
+        self.p = make_problem(q, k, v, _strides3(o, "o"), mst, scale, is_causal)
+        lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
+        lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
+        self.dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        self.dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+        self.dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+        nws = self.lib.sdpa_backward_workspace_bytes(ctypes.byref(self.p))
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k, v, o, dO, lse, m, lq, lk)
+        self.device = q.device
+        self.args = [ctypes.byref(self.p), _vp(q), _vp(k), _vp(v), _vp(o), _vp(dO), _vp(lse),
+                     _vp(m), _vp(lq), _vp(lk), _vp(self.dq), _vp(self.dk), _vp(self.dv),
+                     _vp(self.ws), nws]
+        self.fns = {"all": self.lib.sdpa_backward, "prep": self.lib.sdpa_backward_prep,
+                    "dkdv": self.lib.sdpa_backward_dkdv, "dq": self.lib.sdpa_backward_dq}
+
+    def launch(self, stage: str = "all"):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        st = self.fns[stage](*self.args, stream)
+        if st != SDPA_OK:
+            raise_status(self.lib, st)
+
+    def result(self):
+        g = (self.dq, self.dk, self.dv)
+        if self.squeeze:
+            g = tuple(t.squeeze(0) for t in g)
+        return g
+
+
 def sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                  seq_lens_kv=None, return_lse=True):
     """O (and LSE) of scaled dot-product attention.  q (B,Hq,Lq,D), k/v (B,Hkv,Lk,D)."""
-    lib = load_library()
-    squeeze = q.dim() == 3
-    q, k, v = _as4d(q, "q"), _as4d(k, "k"), _as4d(v, "v")
-    _check_io(q, k, v, *([mask] if mask is not None else []))
-    B, Hq, Lq, _ = q.shape
-    Lk, Dv = k.shape[2], v.shape[3]
-    o = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-    p = make_problem(q, k, v, _strides3(o, "o"), mst, scale, is_causal)
-    lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
-    lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
-    nws = lib.sdpa_forward_workspace_bytes(ctypes.byref(p))
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.sdpa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(lq), _ptr(lk),
-                          _ptr(o), _ptr(lse), _ptr(ws), nws, ctypes.c_void_p(stream))
-    if st != SDPA_OK:
-        _raise(lib, st)
-    if squeeze:
-        o = o.squeeze(0)
-        lse = lse.squeeze(0) if lse is not None else None
+    call = ForwardCall(q, k, v, mask, scale, is_causal, seq_lens_q, seq_lens_kv, return_lse)
+    call.launch()
+    o, lse = call.result()
     return (o, lse) if return_lse else o
 
 
 def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                   seq_lens_kv=None):
     """(dQ, dK, dV) from the forward's o and lse and the output gradient dO."""
-    lib = load_library()
-    squeeze = q.dim() == 3
-    q, k, v, o, dO = (_as4d(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")))
-    if lse.dim() == 2:
-        lse = lse.unsqueeze(0)
-    _check_io(q, k, v, o, dO, *([mask] if mask is not None else []))
-    B, Hq, Lq, _ = q.shape
-    Lk = k.shape[2]
-    if tuple(o.shape) != (B, Hq, Lq, v.shape[3]) or dO.shape != o.shape:
-        raise ValueError("sdpa: o and dO must be (B, Hq, Lq, Dv)")
-    if o.stride() != dO.stride():
-        dO = dO.contiguous()
-        o = o.contiguous()
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
-        raise ValueError("sdpa: lse must be float32 (B, Hq, Lq)")
-    lse = lse.contiguous()
-    m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-    p = make_problem(q, k, v, _strides3(o, "o"), mst, scale, is_causal)
-    lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
-    lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
-    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
-    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
-    nws = lib.sdpa_backward_workspace_bytes(ctypes.byref(p))
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.sdpa_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
-                           _ptr(m), _ptr(lq), _ptr(lk), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nws,
-                           ctypes.c_void_p(stream))
-    if st != SDPA_OK:
-        _raise(lib, st)
-    if squeeze:
-        dq, dk, dv = dq.squeeze(0), dk.squeeze(0), dv.squeeze(0)
-    return dq, dk, dv
+    call = BackwardCall(q, k, v, o, dO, lse, mask, scale, is_causal, seq_lens_q, seq_lens_kv)
+    call.launch()
+    return call.result()

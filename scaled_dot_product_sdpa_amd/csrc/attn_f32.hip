@@ -93,7 +93,25 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a) {
   if (a.lse) a.lse[row] = l > 0.f ? m + logf(l) : kNegInf;
 }
 
-// dQ_i and D_i: one thread per query row.
+// D_i = dO_i . O_i: one thread per query row (0 for empty rows).
+template <int D>
+__global__ __launch_bounds__(kTpb) void bwd_prep_f32_kernel(BwdArgs a) {
+  const Problem& p = a.p;
+  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
+  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
+  const RowCtx r = row_ctx(p, row);
+  float Di = 0.f;
+  if (r.i < r.q_end) {
+    const int64_t ooff = r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+    const float* orow = reinterpret_cast<const float*>(a.o) + ooff;
+    const float* drow = reinterpret_cast<const float*>(a.dO) + ooff;
+#pragma unroll
+    for (int t = 0; t < D; ++t) Di = fmaf(drow[t], orow[t], Di);
+  }
+  a.dsum[row] = Di;
+}
+
+// dQ_i: one thread per query row.
 template <int D>
 __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
   const Problem& p = a.p;
@@ -105,18 +123,16 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
   const float* kbase = reinterpret_cast<const float*>(a.k) + r.b * p.k_sb + r.g * p.k_sh;
   const float* vbase = reinterpret_cast<const float*>(a.v) + r.b * p.v_sb + r.g * p.v_sh;
   float qv[D], dov[D], dq[D];
-  float Di = 0.f;
+  const bool ok = r.i < r.q_end;
 #pragma unroll
   for (int t = 0; t < D; ++t) {
-    const bool ok = r.i < r.q_end;
     qv[t] = ok ? reinterpret_cast<const float*>(a.q)[qoff + t] : 0.f;
     dov[t] = ok ? reinterpret_cast<const float*>(a.dO)[ooff + t] : 0.f;
-    const float ov = ok ? reinterpret_cast<const float*>(a.o)[ooff + t] : 0.f;
-    Di = fmaf(dov[t], ov, Di);
     dq[t] = 0.f;
   }
+  const float Di = a.dsum[row];
   const float lse = a.lse[row];
-  if (lse != kNegInf) {
+  if (ok && lse != kNegInf) {
     for (int j = 0; j < r.stop; ++j) {
       const float s = score<D>(p, r, qv, kbase, j);
       if (s == kNegInf) continue;
@@ -130,13 +146,10 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < D; ++t) dq[t] = fmaf(dS, kj[t], dq[t]);
     }
-  } else {
-    Di = 0.f;
   }
   float* dqrow = reinterpret_cast<float*>(a.dq) + qoff;
 #pragma unroll
   for (int t = 0; t < D; ++t) dqrow[t] = dq[t] * p.scale;
-  a.dsum[row] = Di;
 }
 
 // dK_j and dV_j: one thread per key row of a KV head, summing over the query heads it
@@ -212,16 +225,22 @@ hipError_t fwd_d(const FwdArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
+hipError_t bwd_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int64_t qrows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
   const int64_t krows = (int64_t)a.p.B * a.p.Hkv * a.p.Lk;
-  if (qrows > 0) {
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((unsigned)((qrows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+  const dim3 qgrid((unsigned)((qrows + kTpb - 1) / kTpb)), kgrid((unsigned)((krows + kTpb - 1) / kTpb));
+  if ((stages & kBwdPrep) && qrows > 0) {
+    hipLaunchKernelGGL((bwd_prep_f32_kernel<D>), qgrid, dim3(kTpb), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (krows > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)((krows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+  if ((stages & kBwdDkdv) && krows > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), kgrid, dim3(kTpb), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((stages & kBwdDq) && qrows > 0) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), qgrid, dim3(kTpb), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -237,11 +256,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   }
 }
 
-hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   switch (a.p.D) {
-    case 32: return bwd_d<32>(a, s);
-    case 64: return bwd_d<64>(a, s);
-    case 128: return bwd_d<128>(a, s);
+    case 32: return bwd_d<32>(a, stages, s);
+    case 64: return bwd_d<64>(a, stages, s);
+    case 128: return bwd_d<128>(a, stages, s);
     default: return hipErrorInvalidValue;
   }
 }

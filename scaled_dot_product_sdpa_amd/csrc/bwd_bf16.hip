@@ -459,40 +459,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL, bool MASK>
-hipError_t launch_main(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   const int n_kt = (a.p.Lk + kKT - 1) / kKT;
-  if (n_kt > 0) {
+  if ((stages & kBwdDkdv) && n_kt > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, MASK>), dim3(n_kt * a.p.B * a.p.Hkv), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_qt = (a.p.Lq + 127) / 128;
-  if (n_qt > 0) {
+  if ((stages & kBwdDq) && n_qt > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int64_t rows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
-  if (rows > 0) {
+  if ((stages & kBwdPrep) && rows > 0) {
     constexpr int RPB = kThreads / (D / 8);
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(stages & (kBwdDkdv | kBwdDq))) return hipSuccess;
   const bool causal = a.p.causal != 0, mask = a.p.mask != nullptr;
-  if (causal) return mask ? launch_main<D, true, true>(a, s) : launch_main<D, true, false>(a, s);
-  return mask ? launch_main<D, false, true>(a, s) : launch_main<D, false, false>(a, s);
+  if (causal) return mask ? launch_main<D, true, true>(a, stages, s) : launch_main<D, true, false>(a, stages, s);
+  return mask ? launch_main<D, false, true>(a, stages, s) : launch_main<D, false, false>(a, stages, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   switch (a.p.D) {
-    case 64: return launch_d<64>(a, s);
-    case 128: return launch_d<128>(a, s);
+    case 64: return launch_d<64>(a, stages, s);
+    case 128: return launch_d<128>(a, stages, s);
     default: return hipErrorInvalidValue;
   }
 }

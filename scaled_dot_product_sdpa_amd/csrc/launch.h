@@ -62,8 +62,10 @@ struct DecodeArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
+// Backward stages (see sdpa_backward_prep / _dkdv / _dq in include/sdpa.h).
+enum BwdStage { kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7 };
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 // Split-KV geometry used by the decode path (keys per split and number of splits).

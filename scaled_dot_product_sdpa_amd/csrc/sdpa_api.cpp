@@ -203,10 +203,12 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
   return hip_result(sdpa::launch_fwd_bf16(a, s), "bf16 forward launch");
 }
 
-sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, const void* v,
-                          const void* o, const void* dO, const float* lse, const void* mask,
-                          const int32_t* lq, const int32_t* lk, void* dq, void* dk, void* dv,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, const void* k,
+                            const void* v, const void* o, const void* dO, const float* lse,
+                            const void* mask, const int32_t* lq, const int32_t* lk, void* dq,
+                            void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   sdpa_status st = check_problem(p);
   if (st != SDPA_OK) return st;
   st = check_ptrs(p->dtype, {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dO, "dO"}, {dq, "dq"},
@@ -225,9 +227,23 @@ sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, c
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = reinterpret_cast<float*>(workspace);
-  if (p->dtype == SDPA_DTYPE_F32) return hip_result(sdpa::launch_bwd_f32(a, s), "fp32 backward launch");
-  return hip_result(sdpa::launch_bwd_bf16(a, s), "bf16 backward launch");
+  if (p->dtype == SDPA_DTYPE_F32)
+    return hip_result(sdpa::launch_bwd_f32(a, stages, s), "fp32 backward launch");
+  return hip_result(sdpa::launch_bwd_bf16(a, stages, s), "bf16 backward launch");
 }
+}  // namespace
+
+#define SDPA_BWD_ARGS                                                                      \
+  const sdpa_problem *p, const void *q, const void *k, const void *v, const void *o,       \
+      const void *dO, const float *lse, const void *mask, const int32_t *lq,               \
+      const int32_t *lk, void *dq, void *dk, void *dv, void *workspace,                    \
+      size_t workspace_bytes, void *stream
+#define SDPA_BWD_PASS p, q, k, v, o, dO, lse, mask, lq, lk, dq, dk, dv, workspace, workspace_bytes, stream
+
+sdpa_status sdpa_backward(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdAll, SDPA_BWD_PASS); }
+sdpa_status sdpa_backward_prep(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdPrep, SDPA_BWD_PASS); }
+sdpa_status sdpa_backward_dkdv(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDkdv, SDPA_BWD_PASS); }
+sdpa_status sdpa_backward_dq(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDq, SDPA_BWD_PASS); }
 
 const char* sdpa_status_string(sdpa_status s) {
   switch (s) {

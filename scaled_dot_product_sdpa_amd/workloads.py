@@ -64,19 +64,25 @@ WORKLOADS = {
 }
 
 
-def make_inputs(w: Workload) -> dict:
-    """Draw the workload's inputs (CPU tensors in the workload's dtype)."""
-    g = torch.Generator().manual_seed(w.seed)
+def make_inputs(w: Workload, device="cpu") -> dict:
+    """Draw the workload's inputs in the workload's dtype.
+
+    ``device="cpu"`` uses torch's CPU generator; another device draws with that device's
+    generator (same seed and draw order, different stream of numbers), which is how the
+    full-size workloads are made without a host round trip.  Either way every consumer,
+    the oracle included, reads the very tensors drawn here."""
+    g = torch.Generator(device=device).manual_seed(w.seed)
     dt = w.torch_dtype
-    q = torch.randn(w.B, w.Hq, w.Lq, w.D, generator=g).to(dt)
-    k = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g).to(dt)
-    v = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g).to(dt)
-    dO = torch.randn(w.B, w.Hq, w.Lq, w.D, generator=g).to(dt) if w.backward else None
+    kw = dict(generator=g, device=device)
+    q = torch.randn(w.B, w.Hq, w.Lq, w.D, **kw).to(dt)
+    k = torch.randn(w.B, w.Hkv, w.Lk, w.D, **kw).to(dt)
+    v = torch.randn(w.B, w.Hkv, w.Lk, w.D, **kw).to(dt)
+    dO = torch.randn(w.B, w.Hq, w.Lq, w.D, **kw).to(dt) if w.backward else None
 
     len_q = len_kv = None
     if w.lens != "none":
         lo, hi = w.len_range
-        lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int32)
+        lens = torch.randint(lo, hi + 1, (w.B,), dtype=torch.int32, **kw)
         len_kv = lens.clone()
         if w.lens == "qkv":
             len_q = lens.clone()
@@ -86,22 +92,21 @@ def make_inputs(w: Workload) -> dict:
         # -inf outside each batch's length (rows and columns), plus independent
         # Bernoulli(mask_drop) -inf entries inside it, plus one fully masked in-length row.
         L, S = w.Lq, w.Lk
-        lens_b = len_kv if len_kv is not None else torch.full((w.B,), S, dtype=torch.int32)
-        ii = torch.arange(L).view(1, L, 1)
-        jj = torch.arange(S).view(1, 1, S)
+        lens_b = len_kv if len_kv is not None else torch.full((w.B,), S, dtype=torch.int32, device=device)
+        ii = torch.arange(L, device=device).view(1, L, 1)
+        jj = torch.arange(S, device=device).view(1, 1, S)
         lb = lens_b.view(-1, 1, 1).long()
         blocked = (ii >= lb) | (jj >= lb)
-        drop = torch.rand(w.B, L, S, generator=g) < w.mask_drop
+        drop = torch.rand(w.B, L, S, **kw) < w.mask_drop
         blocked = blocked | drop
         row = int(lens_b[0]) // 2
         blocked[0, row, :] = True
-        mask = torch.zeros(w.B, 1, L, S, dtype=torch.float32)
+        mask = torch.zeros(w.B, 1, L, S, dtype=torch.float32, device=device)
         mask.masked_fill_(blocked.view(w.B, 1, L, S), float("-inf"))
         mask = mask.to(dt)
 
     if w.poison and len_kv is not None:
-        for b in range(w.B):
-            n = int(len_kv[b])
+        for b, n in enumerate(len_kv.tolist()):
             k[b, :, n:, :] = float("nan")
             v[b, :, n:, :] = float("nan")
 
