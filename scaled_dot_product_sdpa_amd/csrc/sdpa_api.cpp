@@ -124,14 +124,20 @@ sdpa_status check_ptr(const void* ptr, const char* name, bool required, uintptr_
   return SDPA_OK;
 }
 
-// io tensors: 16-byte alignment for bf16 (vector loads), 4 for fp32; the mask needs only
-// its element alignment, the length arrays 4 bytes.
-sdpa_status check_ptrs(int dtype, std::initializer_list<std::pair<const void*, const char*>> req,
-                       const void* mask, const void* lq, const void* lk, const void* lse,
-                       bool lse_required) {
+struct IoPtr {
+  const void* ptr;
+  const char* name;
+  bool nonempty;  // the tensor has elements, so the pointer is required
+};
+
+// io tensors: 16-byte alignment for bf16 (vector loads), 4 for fp32; an empty tensor (a
+// zero length) may be null.  The mask needs only its element alignment, the length arrays
+// and lse 4 bytes.
+sdpa_status check_ptrs(int dtype, std::initializer_list<IoPtr> req, const void* mask,
+                       const void* lq, const void* lk, const void* lse, bool lse_required) {
   const uintptr_t io = dtype == SDPA_DTYPE_BF16 ? 16 : 4;
   for (auto& x : req) {
-    sdpa_status s = check_ptr(x.first, x.second, true, io);
+    sdpa_status s = check_ptr(x.ptr, x.name, x.nonempty, io);
     if (s != SDPA_OK) return s;
   }
   sdpa_status s = check_ptr(mask, "mask", false, dtype == SDPA_DTYPE_BF16 ? 2 : 4);
@@ -170,7 +176,9 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   sdpa_status st = check_problem(p);
   if (st != SDPA_OK) return st;
-  st = check_ptrs(p->dtype, {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}}, mask, lq, lk, lse, false);
+  const bool hq = p->Lq > 0, hk = p->Lk > 0;
+  st = check_ptrs(p->dtype, {{q, "q", hq}, {k, "k", hk}, {v, "v", hk}, {o, "o", hq}}, mask, lq,
+                  lk, lse, false);
   if (st != SDPA_OK) return st;
   (void)elem_bytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -211,9 +219,10 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
                             void* stream) {
   sdpa_status st = check_problem(p);
   if (st != SDPA_OK) return st;
-  st = check_ptrs(p->dtype, {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dO, "dO"}, {dq, "dq"},
-                             {dk, "dk"}, {dv, "dv"}},
-                  mask, lq, lk, lse, true);
+  const bool hq = p->Lq > 0, hk = p->Lk > 0;
+  st = check_ptrs(p->dtype, {{q, "q", hq}, {k, "k", hk}, {v, "v", hk}, {o, "o", hq},
+                             {dO, "dO", hq}, {dq, "dq", hq}, {dk, "dk", hk}, {dv, "dv", hk}},
+                  mask, lq, lk, lse, hq);
   if (st != SDPA_OK) return st;
   const size_t need = sdpa_backward_workspace_bytes(p);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))

@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: the library loads and exports every function that
+include/sdpa.h declares, workspace sizes follow their documented formulas, and every
+host-checkable bad argument returns its status code before anything is launched."""
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import pytest
+
+import scaled_dot_product_sdpa_amd as sd
+from scaled_dot_product_sdpa_amd.api import (SDPA_DTYPE_BF16, SDPA_DTYPE_F32,
+                                             SDPA_ERR_INVALID_ARGUMENT, SDPA_ERR_UNSUPPORTED,
+                                             SDPA_ERR_WORKSPACE_TOO_SMALL, Problem)
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "sdpa.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not sd.LIB_PATH.exists():
+        from scaled_dot_product_sdpa_amd.build import build
+        build()
+    return sd.load_library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "sdpa_forward" in names and "sdpa_backward" in names
+    for n in names:
+        assert hasattr(lib, n), f"libsdpa.so does not export {n}"
+    assert set(names) == set(sd.EXPORTS)
+
+
+def _problem(dtype=SDPA_DTYPE_BF16, B=2, Hq=4, Hkv=2, Lq=16, Lk=16, D=64, scale=math.nan, causal=0):
+    p = Problem()
+    p.dtype = dtype
+    p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.Dqk, p.Dv = B, Hq, Hkv, Lq, Lk, D, D
+    p.q_stride[:] = (Hq * Lq * D, Lq * D, D)
+    p.k_stride[:] = (Hkv * Lk * D, Lk * D, D)
+    p.v_stride[:] = (Hkv * Lk * D, Lk * D, D)
+    p.o_stride[:] = (Hq * Lq * D, Lq * D, D)
+    p.mask_stride[:] = (0, 0, Lk)
+    p.scale = scale
+    p.is_causal = causal
+    return p
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation first
+
+
+def _fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, mask=None, o=FAKE, lse=FAKE, ws=None, nws=0):
+    return lib.sdpa_forward(ctypes.byref(p), q, k, v, mask, None, None, o, lse, ws, nws, None)
+
+
+def _bwd(lib, p, lse=FAKE, dq=FAKE, ws=FAKE, nws=1 << 20, stage="sdpa_backward"):
+    f = getattr(lib, stage)
+    return f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, lse, None, None, None, dq, FAKE, FAKE,
+             ws, nws, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "dtype", 7), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "B", 0), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "Hq", 3), SDPA_ERR_INVALID_ARGUMENT),          # Hq % Hkv != 0
+    (lambda p: setattr(p, "Lk", -1), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "scale", -0.5), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "scale", 0.0), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "scale", math.inf), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "Dv", 32), SDPA_ERR_UNSUPPORTED),              # Dqk != Dv
+    (lambda p: (setattr(p, "Dqk", 96), setattr(p, "Dv", 96)), SDPA_ERR_UNSUPPORTED),
+    (lambda p: p.k_stride.__setitem__(2, 60), SDPA_ERR_UNSUPPORTED),     # not a multiple of 8
+    (lambda p: p.q_stride.__setitem__(1, -64), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: p.o_stride.__setitem__(2, 32), SDPA_ERR_INVALID_ARGUMENT),  # rows overlap
+])
+def test_forward_rejects(lib, mutate, status):
+    p = _problem()
+    mutate(p)
+    assert _fwd(lib, p) == status, lib.sdpa_last_error()
+    assert lib.sdpa_last_error().decode() != ""
+
+
+def test_forward_rejects_pointers(lib):
+    p = _problem()
+    assert _fwd(lib, p, q=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _fwd(lib, p, k=FAKE + 8) == SDPA_ERR_UNSUPPORTED       # bf16 io needs 16-byte alignment
+    assert _fwd(lib, p, lse=FAKE + 2) == SDPA_ERR_UNSUPPORTED     # fp32 lse needs 4-byte alignment
+    pf = _problem(dtype=SDPA_DTYPE_F32, D=32)
+    assert _fwd(lib, pf, o=None) == SDPA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_workspace(lib):
+    p = _problem(B=64, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128)
+    need = lib.sdpa_forward_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert _fwd(lib, p, ws=FAKE, nws=need - 1) == SDPA_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(lib, p, ws=None, nws=need) == SDPA_ERR_WORKSPACE_TOO_SMALL
+    # a causal single-query problem runs on the prefill kernel and needs none
+    pc = _problem(B=64, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128, causal=1)
+    assert lib.sdpa_forward_workspace_bytes(ctypes.byref(pc)) == 0
+
+
+def test_prefill_and_backward_workspace(lib):
+    p = _problem(B=4, Hq=16, Hkv=16, Lq=1024, Lk=1024, D=64)
+    assert lib.sdpa_forward_workspace_bytes(ctypes.byref(p)) == 0
+    nb = lib.sdpa_backward_workspace_bytes(ctypes.byref(p))
+    assert nb >= 4 * 16 * 1024 * 4 and nb % 256 == 0
+    bad = _problem(Hq=3)
+    assert lib.sdpa_backward_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("stage", ["sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv",
+                                   "sdpa_backward_dq"])
+def test_backward_rejects(lib, stage):
+    p = _problem()
+    assert _bwd(lib, p, lse=None, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+    assert _bwd(lib, p, dq=None, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+    assert _bwd(lib, p, nws=16, stage=stage) == SDPA_ERR_WORKSPACE_TOO_SMALL
+    bad = _problem(Hq=3)
+    assert _bwd(lib, bad, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+
+
+def test_status_strings_and_version(lib):
+    assert lib.sdpa_status_string(0) == b"ok"
+    assert lib.sdpa_status_string(SDPA_ERR_WORKSPACE_TOO_SMALL) == b"workspace too small"
+    assert lib.sdpa_version() >= 100
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sd.sdpa_forward(q, q, q)

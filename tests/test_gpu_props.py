@@ -1,0 +1,167 @@
+"""GPU properties and edge cases of the HIP path (through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (banner, check_grad, compare_forward, f64, gpu_backward, gpu_forward,
+                        oracle_backward, oracle_forward, rel_fro, to_dev)
+from scaled_dot_product_sdpa_amd import BackwardCall, ForwardCall, sdpa_backward, sdpa_forward
+from scaled_dot_product_sdpa_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MID = WORKLOADS["gqa_causal_4k"].scaled(B=2, Hq=8, Hkv=2, Lq=700, Lk=700, seed=31)
+
+
+def test_forward_and_backward_are_bitwise_repeatable():
+    banner("repeatability")
+    d = to_dev(make_inputs(MID))
+    o1, l1 = gpu_forward(d)
+    o2, l2 = gpu_forward(d)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = gpu_backward(d, o1, l1)
+    g2 = gpu_backward(d, o1, l1)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_causal_equals_tril_mask():
+    """is_causal and an explicit additive mask built from tril give the same result."""
+    banner("causal == tril mask")
+    w = MID.scaled(Hq=4, Hkv=4, D=64, Lq=300, Lk=300)
+    d = to_dev(make_inputs(w))
+    o1, l1 = gpu_forward(d)
+    tril = torch.ones(w.Lq, w.Lk, dtype=torch.bool, device="cuda").tril()
+    m = torch.zeros(w.Lq, w.Lk, device="cuda").masked_fill(~tril, float("-inf")).to(torch.bfloat16)
+    d2 = dict(d, is_causal=False, mask=m.view(1, 1, w.Lq, w.Lk))
+    o2, l2 = gpu_forward(d2)
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-4
+    g1 = gpu_backward(d, o1, l1)
+    g2 = gpu_backward(d2, o2, l2)
+    for a, b in zip(g1, g2):
+        assert rel_fro(f64(a), f64(b)) <= 1e-2
+
+
+def test_gqa_equals_repeat_interleave():
+    """GQA equals MHA on K/V expanded in repeat_interleave order; a shared head's dK/dV is
+    the sum of the expanded heads' gradients."""
+    banner("GQA == repeat_interleave")
+    d = to_dev(make_inputs(MID))
+    G = MID.Hq // MID.Hkv
+    de = dict(d, k=d["k"].repeat_interleave(G, dim=1).contiguous(),
+              v=d["v"].repeat_interleave(G, dim=1).contiguous())
+    o1, l1 = gpu_forward(d)
+    o2, l2 = gpu_forward(de)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    dq1, dk1, dv1 = gpu_backward(d, o1, l1)
+    dq2, dk2, dv2 = gpu_backward(de, o2, l2)
+    assert torch.equal(dq1, dq2)
+    sk = dk2.float().view(MID.B, MID.Hkv, G, MID.Lk, MID.D).sum(2)
+    sv = dv2.float().view(MID.B, MID.Hkv, G, MID.Lk, MID.D).sum(2)
+    assert rel_fro(f64(dk1), f64(sk)) <= 1e-2 and rel_fro(f64(dv1), f64(sv)) <= 1e-2
+
+
+def test_padding_is_never_read(orc):
+    """With length arrays, NaN in q/k/v/dO rows past the lengths changes nothing."""
+    banner("NaN-poisoned padding (prefill, fwd + bwd)")
+    w = MID.scaled(lens="qkv", len_range=(50, 700), causal=False, seed=33)
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    o1, l1 = gpu_forward(d)
+    g1 = gpu_backward(d, o1, l1)
+    pois = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in d.items()}
+    for b, n in enumerate(inp["len_kv"].tolist()):
+        for name in ("q", "k", "v", "dO"):
+            pois[name][b, :, n:] = float("nan")
+    o2, l2 = gpu_forward(pois)
+    g2 = gpu_backward(pois, o2, l2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    o_ref, lse_ref = oracle_forward(orc, inp)
+    compare_forward(inp, o1, l1, o_ref, lse_ref)
+
+
+def test_zero_lengths_and_empty_batches(orc):
+    """A batch with length 0 gives O = 0, LSE = -inf and zero gradients."""
+    banner("zero lengths")
+    w = MID.scaled(B=3, lens="qkv", len_range=(0, 0), seed=34, causal=True)
+    inp = make_inputs(w)
+    inp["len_q"] = torch.tensor([0, 300, 700], dtype=torch.int32)
+    inp["len_kv"] = torch.tensor([0, 123, 700], dtype=torch.int32)
+    d = to_dev(inp)
+    o, lse = gpu_forward(d)
+    dq, dk, dv = gpu_backward(d, o, lse)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(dq[0] == 0) and torch.all(dk[0] == 0) and torch.all(dv[0] == 0)
+    assert torch.all(dk[1, :, 123:] == 0) and torch.all(dq[1, :, 300:] == 0)
+    o_ref, lse_ref = oracle_forward(orc, inp)
+    compare_forward(inp, o, lse, o_ref, lse_ref)
+    rq, rk, rv, _ = oracle_backward(orc, inp)
+    for g, r, n in zip((dq, dk, dv), (rq, rk, rv), ("dQ", "dK", "dV")):
+        check_grad(f64(g), r, torch.bfloat16, n)
+
+
+def test_empty_key_sequence():
+    """Lk = 0: every row is empty (O = 0, LSE = -inf); Lq = 0 is a no-op."""
+    banner("Lk = 0 / Lq = 0")
+    q = torch.randn(1, 2, 5, 64, device="cuda").to(torch.bfloat16)
+    k = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = sdpa_forward(q, k, k)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    q0 = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    kk = torch.randn(1, 2, 7, 64, device="cuda").to(torch.bfloat16)
+    o0, l0 = sdpa_forward(q0, kk, kk)
+    dq, dk, dv = sdpa_backward(q0, kk, kk, o0, o0, l0)
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_strided_bshd_layout(orc):
+    """Inputs in (B, S, H, D) memory order (strided views) give the same result."""
+    banner("BSHD strided layout")
+    w = MID.scaled(Hq=4, Hkv=2, Lq=200, Lk=200, seed=35)
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    o1, l1 = gpu_forward(d)
+    ds = dict(d)
+    for n in ("q", "k", "v"):
+        ds[n] = d[n].transpose(1, 2).contiguous().transpose(1, 2)  # BSHD storage, BHSD view
+    o2, l2 = gpu_forward(ds)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_graph_replay_matches_eager():
+    """A HIP graph of the forward and backward replays to the eager result every time,
+    with eager work and synchronisations between replays."""
+    banner("graph replay")
+    d = to_dev(make_inputs(MID))
+    fc = ForwardCall(d["q"], d["k"], d["v"], None, d["scale"], True)
+    fc.launch()
+    torch.cuda.synchronize()
+    bc = BackwardCall(d["q"], d["k"], d["v"], fc.o, d["dO"], fc.lse, None, d["scale"], True)
+
+    def step():
+        fc.launch()
+        bc.launch()
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (fc.o, fc.lse, bc.dq, bc.dk, bc.dv):
+            t.fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)):
+            assert torch.equal(a, b), f"replay {rep} differs"
