@@ -92,7 +92,8 @@ typedef struct {
  * work on the stream has finished. */
 size_t sdpa_forward_workspace_bytes(const sdpa_problem* p);
 
-/* Device workspace (bytes) the backward needs: D = rowsum(dO o O) in fp32. */
+/* Device workspace (bytes) the backward needs: per query row, D = rowsum(dO o O) and
+ * LSE * log2(e), both fp32. */
 size_t sdpa_backward_workspace_bytes(const sdpa_problem* p);
 
 /*

@@ -8,9 +8,10 @@
 //    all of them ("Understanding PyTorch Scaled Dot-Product Attention" section 4 for the
 //    head map);
 //  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
-//    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> registers
-//    -> LDS (prefetched one tile ahead, 16-byte coalesced loads) and writes a partial
-//    (O_c normalised, lse_c); splits past the sequence length exit at once;
+//    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> LDS with
+//    global_load_lds (no staging registers, so several such workgroups share a CU and
+//    many bytes are in flight), double-buffered; splits past the sequence length exit at
+//    once; each split writes a partial (O_c normalised, lse_c);
 //  - a combine kernel merges the partials exactly:  LSE = ln sum_c exp(lse_c),
 //    O = sum_c exp(lse_c - LSE) O_c  (the log-sum-exp merge of split-KV partial results
 //    that cuDNN "Attention", SDPA FP16/BF16 Forward, Python API describes for its stats).
@@ -23,18 +24,14 @@ namespace {
 constexpr int kDT = 32;  // keys per tile
 
 template <int D>
-struct DecTile {
-  static constexpr int KP = D + 8;
-  static constexpr int VP = D + 8;
-  static constexpr int CPR = D / 8;
-  static constexpr int NCH = kDT * CPR / 64;  // 16-byte chunks per lane per tensor
-};
-
-template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  using T = DecTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kDT * T::KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kDT * T::VP];
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_split_kernel(DecodeArgs a) {
+  constexpr int CPR = D / 8;
+  constexpr int TILE = kDT * D;
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
   const Problem& p = a.p;
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -56,6 +53,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
   const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
 
+  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
+    tile_to_lds_swz<kDT, D, 1>(kbase, p.k_sl, j0, k1, Kd, 0, lane);
+    tile_to_lds_swz<kDT, D, 1>(vbase, p.v_sl, j0, k1, Vd, 0, lane);
+  };
+  load_tile(k0, K0, V0);
+
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
@@ -66,52 +69,42 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
   float mrow = kNegInf, lrow = 0.f, frow = 0.f;  // max, rounded-weight sum, fp32-weight sum
 
-  u32x4 kst[T::NCH], vst[T::NCH];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int u = 0; u < T::NCH; ++u) {
-      const int idx = lane + u * 64;
-      const int r = idx / T::CPR, cc = idx % T::CPR;
-      const int row = j0 + r;
-      const bool ok = row < k1;
-      kst[u] = ok ? ld16(kbase + (int64_t)row * p.k_sl + cc * 8) : zero16();
-      vst[u] = ok ? ld16(vbase + (int64_t)row * p.v_sl + cc * 8) : zero16();
-    }
-  };
-  load_tile(k0);
+  const float c2 = p.scale_log2;
+  const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+  const int kr = perm_row(l32);
+  const int ksw = swz(kr) & (CPR - 1);
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
-  const int acol = 4 * (lane & 3) + 16 * (blk & 1);
+  const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
+  const int thalf = 4 * (lane & 1);
 
-  for (int t = 0; t < n_tiles; ++t) {
+  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
+                  __attribute__((always_inline)) {
     const int j0 = k0 + t * kDT;
-#pragma unroll
-    for (int u = 0; u < T::NCH; ++u) {
-      const int idx = lane + u * 64;
-      const int r = idx / T::CPR, cc = idx % T::CPR;
-      *reinterpret_cast<u32x4*>(&Ks[r * T::KP + cc * 8]) = kst[u];
-      *reinterpret_cast<u32x4*>(&Vs[r * T::VP + cc * 8]) = vst[u];
-    }
+    wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(j0 + kDT);
+    if (t + 1 < n_tiles) load_tile(j0 + kDT, Kn, Vn);
 
     f32x16 sacc = f32x16{};
-    const bf16* krow = &Ks[perm_row(l32) * T::KP + 8 * hi];
+    {
+      bf16x8 kop[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qreg[kk], sacc);
-
+      for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = *reinterpret_cast<const bf16x8*>(Kt + kr * D + (((2 * kk + hi) ^ ksw) * 8));
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(kop[kk], qreg[kk], sacc);
+    }
     const bool partial = j0 + kDT > k1;
     float s[16];
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      float x = sacc[v] * p.scale_log2;
+      float x = sacc[v];
       if (partial) x = (j0 + 16 * hi + v < k1) ? x : kNegInf;
       s[v] = x;
       mx = fmaxf(mx, x);
     }
-    mx = xhalf_max(mx);
+    mx = xhalf_max(mx) * c2;
     const float m_new = fmaxf(mrow, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float corr = fast_exp2(mrow - m_use);
@@ -121,28 +114,45 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        const float pf = fast_exp2(s[half * 8 + t8] - m_use);
-        const bf16 e = (bf16)pf;
-        pop[half][t8] = e;
-        psum += bf2f(e);
-        fsum += pf;
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const int v = half * 8 + 2 * t2;
+        f32x2 e;
+        e[0] = fast_exp2(fmaf(s[v], c2, -m_use));
+        e[1] = fast_exp2(fmaf(s[v + 1], c2, -m_use));
+        const bf16x2 e2 = __builtin_convertvector(e, bf16x2);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, psum, false);
+        fsum += e[0];
+        fsum += e[1];
+        pop[half][2 * t2] = e2[0];
+        pop[half][2 * t2 + 1] = e2[1];
       }
     }
     lrow = lrow * corr + psum;
     frow = frow * corr + fsum;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+    // V^T operands (transposing reads)
+    bf16x8 vop[2][D / 32];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const bf16* vrow = &Vs[(16 * hi + 8 * half + arow) * T::VP + acol];
+      const int tr = 16 * hi + 8 * half + arow;  // rows tr and tr + 4
+      const int tsw = swz(tr) & (CPR - 1);
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        bf16x8 vop = join_tr(lds_read_tr4(vrow + mb * 32), lds_read_tr4(vrow + 4 * T::VP + mb * 32));
-        oacc[mb] = mfma32(vop, pop[half], oacc[mb]);
+        const int off = tr * D + ((tchunk + 4 * mb) ^ tsw) * 8 + thalf;
+        vop[half][mb] = join_tr(lds_read_tr4(Vt + off), lds_read_tr4(Vt + off + 4 * D));
       }
     }
-    __syncthreads();
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(vop[half][mb], pop[half], oacc[mb]);
+  };
+
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, K0, V0, K1, V1);
+    if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
   }
 
   const float lt = xhalf_sum(lrow);

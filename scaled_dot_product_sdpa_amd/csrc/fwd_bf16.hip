@@ -6,49 +6,77 @@
 // one-pass online softmax (running max and sum; the page's "Going further" table names
 // Milakov and Gimelshein's online normaliser).
 //
-// Work decomposition: one workgroup = 4 waves = BM query rows of one (batch, head); each
-// wave owns NQB blocks of 32 query rows and keeps their Q operand, O accumulator and
-// running max / sum in registers.  K/V tiles of BN = 64 keys stream through LDS
-// (coalesced 16-byte loads, prefetched into registers one tile ahead).
+// Work decomposition: a workgroup of NW waves owns BM = NW * 32 * NQB query rows of one
+// (batch, head); each wave owns NQB blocks of 32 query rows and keeps their Q operand, O
+// accumulator and running statistics in registers.  K/V tiles of 64 keys stream
+// HBM -> LDS with global_load_lds (16 bytes per lane, no staging registers) into two
+// LDS buffers: tile t+1 is in flight while tile t is computed, one barrier per tile.
+// Tiles are stored unpadded with XOR-swizzled 16-byte chunks (kern_common.h) so the MFMA
+// operand reads are free of bank conflicts.  With NQB = 2 every K/V operand read from
+// LDS feeds two MFMAs, which halves LDS traffic per flop.
 //
 //   S^T = K Q^T   (keys x queries): A = K rows from LDS (row-permuted, see kern_common.h),
 //                 B = Q held in registers; lane l ends up with 16 consecutive keys of
-//                 query l%32, so the row max needs one in-register reduction plus one
-//                 permlane32 swap, and the row sum is kept per half-wave until the end.
+//                 query l%32, so the row max needs v_max3 reductions in registers plus one
+//                 permlane32 swap, and the row sums stay per half-wave until the end.
 //   O^T += V^T P^T (d x queries): A = V^T read with ds_read_b64_tr_b16, B = bf16(P) taken
 //                 straight from the S accumulator registers.  O^T keeps one query per
-//                 lane, so the rescale by exp(m_old - m_new) is a per-lane multiply.
+//                 lane, so a rescale is a per-lane multiply.
 //
-// Scores are kept in log2 units (scale * log2 e folded into one multiply) and
-// exponentiated with v_exp_f32.  Tiles entirely above the causal diagonal or past the
-// key length are never visited; only tiles touching the diagonal or a length boundary
-// evaluate per-element predicates.  Rows with no visible key produce O = 0, LSE = -inf.
-// The output is normalised by the sum of the bf16-rounded weights actually fed to the
-// PV product, so each output row is an exact convex combination of value rows.
+// Softmax arithmetic per score: one FMA folds scale * log2(e) and the reference max into
+// the exp2 argument; v_exp_f32; v_cvt_pk_bf16_f32; the bf16 weights are summed with
+// v_dot2 (this sum normalises O, so each output row is an exact convex combination of
+// value rows) and the fp32 weights with one add (this sum gives LSE).  The reference max
+// is only moved when a row's max grows by more than 2^8 (weights stay <= 256, exact in
+// fp32 sums and in bf16 range), so the O rescale runs on a few tiles only.
+//
+// Tiles entirely above the causal diagonal or past the key length are never visited, and
+// a wave skips the 32-key blocks that none of its rows can see.  Only tiles touching the
+// diagonal or a length boundary evaluate per-element predicates.  Rows with no visible
+// key produce O = 0, LSE = -inf.
 #include "kern_common.h"
 #include "launch.h"
 
 namespace sdpa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;  // keys per K/V tile (two 32-key MFMA blocks)
+constexpr int kBN = 64;             // keys per K/V tile (two 32-key MFMA blocks)
+constexpr float kRescaleLog2 = 8.f; // move the reference max only past this growth
 
-template <int D>
+template <int D, int NW>
 struct FwdTile {
-  static constexpr int KP = D + 8;  // LDS row pitch of the K tile (elements)
-  static constexpr int VP = D + 8;  // LDS row pitch of the V tile (elements)
-  static constexpr int CPR = D / 8; // 16-byte chunks per row
-  static constexpr int NCH = kBN * CPR / kThreads;  // chunks per thread per tensor
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int TILE = kBN * D;       // elements per K (or V) tile
+  static constexpr int LPW = CPR / NW;       // global_load_lds per wave per tensor per tile
 };
 
-template <int D, int NQB, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
-  using T = FwdTile<D>;
-  constexpr int BM = kWaves * 32 * NQB;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * T::KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kBN * T::VP];
+// Issue the HBM -> LDS copies of one 64-row tile (rows j0.. of `g`, clamped to the last
+// row below `stop`: a clamped row is finite and every key it stands for is masked).
+// Wave w copies the LDS chunks [w * LPW * 64, (w + 1) * LPW * 64); LDS chunk ci holds
+// logical chunk (ci % CPR) ^ swz(row) of row ci / CPR.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void tile_to_lds(const bf16* g, int64_t row_stride, int j0, int stop,
+                                            bf16* lds_tile, int wave, int lane) {
+  using T = FwdTile<D, NW>;
+#pragma unroll
+  for (int i = 0; i < T::LPW; ++i) {
+    const int blk = wave * T::LPW + i;
+    const int ci = blk * 64 + lane;
+    const int r = ci / T::CPR;
+    const int c = (ci % T::CPR) ^ ((IS_V ? swz_v(r) : swz_k(r)) & (T::CPR - 1));
+    const int row = min(j0 + r, stop - 1);
+    global_to_lds16(g + (int64_t)row * row_stride + c * 8, lds_tile + blk * 512);
+  }
+}
+
+template <int D, int NW, int NQB, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
+  using T = FwdTile<D, NW>;
+  constexpr int BM = NW * 32 * NQB;
+  __shared__ __attribute__((aligned(16))) bf16 K0[T::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K1[T::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V0[T::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V1[T::TILE];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -57,19 +85,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
 
-  // ---- work item: heavy causal tiles first; the heads of one KV group are adjacent.
-  const int n_qt = (p.Lq + BM - 1) / BM;
+  // ---- work item; the heads of one KV group are adjacent in launch order.
   const int bh_count = p.B * p.Hq;
   const int rank = blockIdx.x / bh_count;
   const int bh = blockIdx.x % bh_count;
-  const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
   const int g = h / p.G;
 
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  const int i0 = qt * BM;
+  // Rows of this workgroup.  Non-causal: query tile `rank` of BM rows.  Causal, large
+  // grids: tile n_qt - 1 - rank (heavy tiles launch first and the scheduler evens the
+  // load).  Causal, grids of about one round (pair_rows): the half-tiles (BM/2 rows)
+  // `rank` and `n_half - 1 - rank`, one per half of the waves, so every workgroup carries
+  // the same causal work (a middle half-tile pairs with nothing).
+  int wq_lo, row_lo, row_hi;  // this wave's first row; the workgroup's row span
+  if (CAUSAL && !p.pair_rows) {
+    const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
+    wq_lo = qt * BM + wave * 32 * NQB;
+    row_lo = qt * BM;
+    row_hi = row_lo + BM;
+  } else if (CAUSAL) {
+    constexpr int HB = BM / 2;
+    const int n_half = (p.Lq + HB - 1) / HB;
+    const int heavy = n_half - 1 - rank;
+    const int mine = wave < NW / 2 ? rank : heavy;
+    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32 * NQB;
+    row_lo = rank * HB;
+    row_hi = (heavy + 1) * HB;
+  } else {
+    wq_lo = rank * BM + wave * 32 * NQB;
+    row_lo = rank * BM;
+    row_hi = row_lo + BM;
+  }
+  const int wq_hi = min(wq_lo + 32 * NQB, q_end) - 1;     // this wave's last live row
 
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
   const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
@@ -80,8 +130,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   // Keys this tile of queries can see.
   int kv_stop = kv_end;
-  if (CAUSAL) kv_stop = min(kv_stop, min(i0 + BM, q_end));
-  if (i0 >= q_end) kv_stop = 0;
+  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
+  if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
 
   // ---- Q operand (B of S^T = K Q^T): lane holds query row, 8 consecutive d per k-step.
@@ -89,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   int qrow[NQB];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
-    qrow[nb] = i0 + wave * 32 * NQB + nb * 32 + l32;
+    qrow[nb] = wq_lo + nb * 32 + l32;
     const bool ok = qrow[nb] < q_end;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -98,82 +148,86 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
+  // reference max (log2 units), sum of bf16 weights (normalises O), sum of fp32 weights
+  // (gives LSE); both sums are relative to the reference max.
   f32x16 oacc[NQB][D / 32];
-  // running max (log2 units), sum of the bf16-rounded weights (normalises O) and sum of
-  // the fp32 weights (gives LSE)
-  float mrow[NQB], lrow[NQB], frow[NQB];
+  float mref[NQB], lrow[NQB], frow[NQB];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
-    mrow[nb] = kNegInf;
+    mref[nb] = kNegInf;
     lrow[nb] = 0.f;
     frow[nb] = 0.f;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[nb][mb] = f32x16{};
   }
 
-  // ---- K/V tile staging: thread handles NCH 16-byte chunks of each tensor.
-  u32x4 kst[T::NCH], vst[T::NCH];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int u = 0; u < T::NCH; ++u) {
-      const int idx = tid + u * kThreads;
-      const int r = idx / T::CPR, c = idx % T::CPR;
-      const int row = j0 + r;
-      const bool ok = row < kv_stop;
-      kst[u] = ok ? ld16(kb_ + (int64_t)row * p.k_sl + c * 8) : zero16();
-      vst[u] = ok ? ld16(vb_ + (int64_t)row * p.v_sl + c * 8) : zero16();
-    }
+  // ---- K/V tiles: HBM -> LDS, double-buffered.
+  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
+    tile_to_lds<D, NW, false>(kb_, p.k_sl, j0, kv_stop, Kd, wave, lane);
+    tile_to_lds<D, NW, true>(vb_, p.v_sl, j0, kv_stop, Vd, wave, lane);
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < T::NCH; ++u) {
-      const int idx = tid + u * kThreads;
-      const int r = idx / T::CPR, c = idx % T::CPR;
-      *reinterpret_cast<u32x4*>(&Ks[r * T::KP + c * 8]) = kst[u];
-      *reinterpret_cast<u32x4*>(&Vs[r * T::VP + c * 8]) = vst[u];
-    }
-  };
+  if (n_tiles > 0) load_tile(0, K0, V0);
+  const float c2 = p.scale_log2;
+  const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
+  // K operand read: row kb*32 + perm_row(l32), logical chunk 2*kk + hi
+  const int krow_l = perm_row(l32);
+  // V^T operand (transposing read): row key_base + arow, logical chunk vchunk, half vhalf
+  const int blk = lane >> 4;
+  const int arow = (lane & 15) >> 2;
+  const int vchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
+  const int vhalf = 4 * (lane & 1);
 
-  if (n_tiles > 0) load_tile(0);
-
-  for (int t = 0; t < n_tiles; ++t) {
+  // One tile step; the loop below is unrolled by two so that the buffer being read and
+  // the one being filled are distinct LDS objects at compile time (the compiler then
+  // does not make the reads of tile t wait for the copies of tile t+1).
+  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
+                  __attribute__((always_inline)) {
     const int j0 = t * kBN;
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(j0 + kBN);
+    wait_vmem();       // this wave's copies of tile t have landed
+    __syncthreads();   // ... and everyone's; the other buffer is no longer being read
+    if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
 
-    // ---- S^T = K Q^T for the two 32-key blocks of the tile.
-    f32x16 sacc[NQB][2];
+    // The tile's two 32-key blocks one after the other: S^T, softmax, then PV.
+    const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo) ||
+                           (wq_lo + 32 * NQB > q_end);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) sacc[nb][kb] = f32x16{};
-      const bf16* krow = &Ks[(kb * 32 + perm_row(l32)) * T::KP + 8 * hi];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
-#pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) sacc[nb][kb] = mfma32(kop, qreg[nb][kk], sacc[nb][kb]);
-      }
-    }
+      const int key_lo = j0 + kb * 32;
+      // a block none of this wave's rows can see is skipped (wave-uniform)
+      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi))) continue;
 
-    // ---- online softmax; lane holds keys j0 + kb*32 + 16*hi + v of query qrow[nb].
-    const bool partial = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > i0) ||
-                         (i0 + BM > q_end);
-    bf16x8 pop[NQB][2][2];
+      // ---- S^T = K Q^T for keys key_lo .. key_lo + 31
+      f32x16 sacc[NQB];
 #pragma unroll
-    for (int nb = 0; nb < NQB; ++nb) {
-      const int qi = qrow[nb];
-      float s[2][16];
+      for (int nb = 0; nb < NQB; ++nb) sacc[nb] = f32x16{};
+      {
+        // all K operands of the block first, so the LDS reads are in flight together
+        const int kr = kb * 32 + krow_l;
+        const bf16* krow = Kt + kr * D;
+        const int ksw = swz_k(kr) & (T::CPR - 1);
+        bf16x8 kop[D / 16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key0 = j0 + kb * 32 + 16 * hi;
-        float mv[16];
+        for (int kk = 0; kk < D / 16; ++kk)
+          kop[kk] = *reinterpret_cast<const bf16x8*>(krow + (((2 * kk + hi) ^ ksw) * 8));
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < NQB; ++nb) sacc[nb] = mfma32(kop[kk], qreg[nb][kk], sacc[nb]);
+      }
+
+      // ---- online softmax; lane holds keys key0 + v (v < 16) of query qrow[nb].
+      const int key0 = key_lo + 16 * hi;
+      bf16x8 pop[NQB][2];
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        const int qi = qrow[nb];
+        // x: raw dot products (no mask) or log2-unit scores (mask)
+        float x[16];
         if (MASK) {
+          float mv[16];
           if (p.mask_vec && qi < q_end && key0 + 16 <= p.Lk) {
             const bf16* mp = mb_ + (int64_t)qi * p.m_si + key0;
-            u32x4 m0 = ld16(mp), m1 = ld16(mp + 8);
-            bf16x8 b0 = __builtin_bit_cast(bf16x8, m0), b1 = __builtin_bit_cast(bf16x8, m1);
+            bf16x8 b0 = __builtin_bit_cast(bf16x8, ld16(mp)), b1 = __builtin_bit_cast(bf16x8, ld16(mp + 8));
 #pragma unroll
             for (int v = 0; v < 8; ++v) { mv[v] = bf2f(b0[v]); mv[v + 8] = bf2f(b1[v]); }
           } else {
@@ -181,85 +235,100 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
             for (int v = 0; v < 16; ++v)
               mv[v] = (qi < q_end && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) : 0.f;
           }
-        }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[nb][kb][v] * p.scale_log2;
-          if (MASK) x += mv[v] * kLog2e;
-          if (partial) {
+          for (int v = 0; v < 16; ++v) x[v] = fmaf(sacc[nb][v], c2, mv[v] * kLog2e);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x[v] = sacc[nb][v];
+        }
+        if (partial_t) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
             const int key = key0 + v;
             const bool ok = key < kv_end && qi < q_end && (!CAUSAL || key <= qi);
-            x = ok ? x : kNegInf;
+            x[v] = ok ? x[v] : kNegInf;
           }
-          s[kb][v] = x;
         }
-      }
-      float mx = kNegInf;
+        float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
+        mx = xhalf_max(mx);
+        const float mt = MASK ? mx : mx * c2;  // block max in log2 units (c2 > 0)
+        // lazy rescale: move the reference only when some row grew past the threshold
+        const bool need = mt > mref[nb] + kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float mnew = need ? mt : mref[nb];
+          const float corr = need ? fast_exp2(mref[nb] - mnew) : 1.f;
+          mref[nb] = mnew;
+          lrow[nb] *= corr;
+          frow[nb] *= corr;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(mrow[nb], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float corr = fast_exp2(mrow[nb] - m_use);
-      mrow[nb] = m_new;
-      float psum = 0.f, fsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+          for (int mb = 0; mb < D / 32; ++mb) oacc[nb][mb] *= corr;
+        }
+        const float m_use = (mref[nb] == kNegInf) ? 0.f : mref[nb];
+        float psum = lrow[nb], fsum = frow[nb];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           bf16x8 pb;
 #pragma unroll
-          for (int t8 = 0; t8 < 8; ++t8) {
-            const float pf = fast_exp2(s[kb][half * 8 + t8] - m_use);
-            const bf16 e = (bf16)pf;
-            pb[t8] = e;
-            psum += bf2f(e);
-            fsum += pf;
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const int v = half * 8 + 2 * t2;
+            f32x2 e;
+            if (MASK) {
+              e[0] = fast_exp2(x[v] - m_use);
+              e[1] = fast_exp2(x[v + 1] - m_use);
+            } else {
+              e[0] = fast_exp2(fmaf(x[v], c2, -m_use));
+              e[1] = fast_exp2(fmaf(x[v + 1], c2, -m_use));
+            }
+            const bf16x2 e2 = __builtin_convertvector(e, bf16x2);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, psum, false);
+            fsum += e[0];
+            fsum += e[1];
+            pb[2 * t2] = e2[0];
+            pb[2 * t2 + 1] = e2[1];
           }
-          pop[nb][kb][half] = pb;
+          pop[nb][half] = pb;
         }
+        lrow[nb] = psum;
+        frow[nb] = fsum;
       }
-      lrow[nb] = lrow[nb] * corr + psum;
-      frow[nb] = frow[nb] * corr + fsum;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[nb][mb] *= corr;
-    }
 
-    // ---- O^T += V^T P^T.  V^T operand via transposing LDS reads: lane (within its
-    // 16-lane block) supplies row  key_base + (lane%16)/4, columns d_base + 4*(lane%4).
-    {
-      const int blk = lane >> 4;
-      const int arow = (lane & 15) >> 2;
-      const int acol = 4 * (lane & 3) + 16 * (blk & 1);
+      // ---- O^T += V^T P^T.  V^T operand via transposing LDS reads: lane (within its
+      // 16-lane block) supplies row  key_base + (lane%16)/4, columns d_base + 4*(lane%4).
+      bf16x8 vop[2][D / 32];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int half = 0; half < 2; ++half) {
+        const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr and vr + 4
+        const bf16* vrow = Vt + vr * D + vhalf;
+        const int vsw = swz_v(vr) & (T::CPR - 1);               // same for vr + 4
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16* vrow = &Vs[(kb * 32 + 16 * hi + 8 * half + arow) * T::VP + acol];
-#pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) {
-            i16x4 lo = lds_read_tr4(vrow + mb * 32);
-            i16x4 hi4 = lds_read_tr4(vrow + 4 * T::VP + mb * 32);
-            bf16x8 vop = join_tr(lo, hi4);
-#pragma unroll
-            for (int nb = 0; nb < NQB; ++nb) oacc[nb][mb] = mfma32(vop, pop[nb][kb][half], oacc[nb][mb]);
-          }
+        for (int mb = 0; mb < D / 32; ++mb) {
+          const int off = ((vchunk + 4 * mb) ^ vsw) * 8;
+          vop[half][mb] = join_tr(lds_read_tr4(vrow + off), lds_read_tr4(vrow + 4 * D + off));
         }
       }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NQB; ++nb) oacc[nb][mb] = mfma32(vop[half][mb], pop[nb][half], oacc[nb][mb]);
     }
-    __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, K0, V0, K1, V1);
+    if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
   }
 
-  // ---- epilogue: O = O^T / l (0 for empty rows), LSE = ln2 * (m + log2 l).
+  // ---- epilogue: O = O^T / l (0 for empty rows), LSE = ln2 * (mref + log2 f).
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     const int qi = qrow[nb];
     const float lt = xhalf_sum(lrow[nb]);
     const float ft = xhalf_sum(frow[nb]);
-    const bool live = qi < q_end && lt > 0.f;
-    const float inv = live ? 1.f / lt : 0.f;
+    const bool rowlive = qi < q_end && lt > 0.f;
+    const float inv = rowlive ? 1.f / lt : 0.f;
     if (qi < p.Lq) {
       bf16* orow = ob + (int64_t)qi * p.o_sl;
 #pragma unroll
@@ -272,26 +341,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
           *reinterpret_cast<bf16x4*>(orow + mb * 32 + v4 * 8 + hi * 4) = w;
         }
       }
-      if (lseb && hi == 0) lseb[qi] = live ? (mrow[nb] * kLn2 + logf(ft)) : kNegInf;
+      if (lseb && hi == 0) lseb[qi] = rowlive ? (mref[nb] * kLn2 + logf(ft)) : kNegInf;
     }
   }
 }
 
-template <int D, int NQB, bool CAUSAL, bool MASK>
+template <int D, int NW, int NQB, bool CAUSAL, bool MASK>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = kWaves * 32 * NQB;
+  constexpr int BM = NW * 32 * NQB;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
-  const int grid = n_qt * a.p.B * a.p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NQB, CAUSAL, MASK>), dim3(grid), dim3(kThreads), 0, s, a);
+  FwdArgs args = a;
+  // pair half-tiles when whole tiles would give about one round of workgroups
+  args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
+  const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
+  const int grid = n_wg * a.p.B * a.p.Hq;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NQB, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_shape(const FwdArgs& a, hipStream_t s) {
+  // 8 waves of 32 query rows per workgroup: two waves per SIMD hide each other's LDS and
+  // MFMA latencies, which measured faster than 64 rows per wave at one wave per SIMD.
+  return launch_t<D, 8, 1, CAUSAL, MASK>(a, s);
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const bool causal = a.p.causal != 0;
   const bool mask = a.p.mask != nullptr;
-  if (causal) return mask ? launch_t<D, 1, true, true>(a, s) : launch_t<D, 1, true, false>(a, s);
-  return mask ? launch_t<D, 1, false, true>(a, s) : launch_t<D, 1, false, false>(a, s);
+  if (causal) return mask ? launch_shape<D, true, true>(a, s) : launch_shape<D, true, false>(a, s);
+  return mask ? launch_shape<D, false, true>(a, s) : launch_shape<D, false, false>(a, s);
 }
 
 }  // namespace

@@ -22,6 +22,7 @@ struct Problem {
   const int32_t* len_kv;  // may be null
   const void* mask;       // may be null (additive, io dtype)
   int mask_vec;           // mask rows may be read with 16-byte vector loads
+  int pair_rows;          // causal query-stationary kernels: pair light and heavy half-tiles
 };
 
 struct FwdArgs {
@@ -45,6 +46,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;  // workspace: D = rowsum(dO o O), contiguous (B, Hq, Lq)
+  float* lse2;  // workspace: LSE * log2(e), +inf for empty rows, contiguous (B, Hq, Lq)
 };
 
 struct DecodeArgs {

@@ -107,8 +107,10 @@ sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_
   k.len_q = lq;
   k.len_kv = lk;
   k.mask = mask;
-  // 16-byte mask vectors need every (b, h, i) row start 16-byte aligned
+  // 16-byte mask vectors need every (b, h, i) row start 16-byte aligned and whole 8-key
+  // chunks per row
   k.mask_vec = mask != nullptr && p->dtype == SDPA_DTYPE_BF16 && aligned16(mask) &&
+               p->Lk % 8 == 0 &&
                (p->B == 1 || k.m_sb % 8 == 0) && (p->Hq == 1 || k.m_sh % 8 == 0) &&
                (p->Lq == 1 || k.m_si % 8 == 0);
   return k;
@@ -168,7 +170,8 @@ size_t sdpa_forward_workspace_bytes(const sdpa_problem* p) {
 
 size_t sdpa_backward_workspace_bytes(const sdpa_problem* p) {
   if (check_problem(p) != SDPA_OK) return 0;
-  return round_up((size_t)p->B * p->Hq * p->Lq * sizeof(float));
+  // D = rowsum(dO o O) and LSE * log2(e), one fp32 each per query row
+  return 2 * round_up((size_t)p->B * p->Hq * p->Lq * sizeof(float));
 }
 
 sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, const void* v,
@@ -236,6 +239,7 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = reinterpret_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + need / 2);
   if (p->dtype == SDPA_DTYPE_F32)
     return hip_result(sdpa::launch_bwd_f32(a, stages, s), "fp32 backward launch");
   return hip_result(sdpa::launch_bwd_bf16(a, stages, s), "bf16 backward launch");
