@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
 
   const float c2 = p.scale_log2;
   const int qr = perm_row(l32);              // Q / dO row read by this lane (S, dP)
-  const int qsw = swz(qr) & (CPR - 1);
+
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
@@ -190,12 +190,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 op[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        op[kk] = *reinterpret_cast<const bf16x8*>(Qt + qr * D + (((2 * kk + hi) ^ qsw) * 8));
+        op[kk] = tile_row8<D>(Qt, qr, 2 * kk + hi);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) s_acc = mfma32(op[kk], kreg[kk], s_acc);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        op[kk] = *reinterpret_cast<const bf16x8*>(Gt + qr * D + (((2 * kk + hi) ^ qsw) * 8));
+        op[kk] = tile_row8<D>(Gt, qr, 2 * kk + hi);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) dp_acc = mfma32(op[kk], vreg[kk], dp_acc);
     }
@@ -237,14 +237,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
     // dV^T += dO^T P,  dK^T += Q^T dS   (A operands: transposing LDS reads)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr and tr + 4
-      const int tsw = swz(tr) & (CPR - 1);
+      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7 (two quads)
       bf16x8 gT[D / 32], qT[D / 32];
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        const int off = tr * D + ((tchunk + 4 * mb) ^ tsw) * 8 + thalf;
-        gT[mb] = join_tr(lds_read_tr4(Gt + off), lds_read_tr4(Gt + off + 4 * D));
-        qT[mb] = join_tr(lds_read_tr4(Qt + off), lds_read_tr4(Qt + off + 4 * D));
+        gT[mb] = tile_tr8<D>(Gt, tr, tchunk + 4 * mb, thalf);
+        qT[mb] = tile_tr8<D>(Qt, tr, tchunk + 4 * mb, thalf);
       }
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
@@ -387,16 +385,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
         const int kr = kb * 32 + krow_l;
-        const int ksw = swz(kr) & (CPR - 1);
+
         bf16x8 op[D / 16];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-          op[kk] = *reinterpret_cast<const bf16x8*>(Kt + kr * D + (((2 * kk + hi) ^ ksw) * 8));
+          op[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) s_acc = mfma32(op[kk], qreg[kk], s_acc);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-          op[kk] = *reinterpret_cast<const bf16x8*>(Vt + kr * D + (((2 * kk + hi) ^ ksw) * 8));
+          op[kk] = tile_row8<D>(Vt, kr, 2 * kk + hi);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) dp_acc = mfma32(op[kk], doreg[kk], dp_acc);
       }
@@ -434,14 +432,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
       // dQ^T += K^T dS^T  (K^T via transposing LDS reads)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr and tr + 4
-        const int tsw = swz(tr) & (CPR - 1);
+        const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
         bf16x8 kT[D / 32];
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const int off = tr * D + ((tchunk + 4 * mb) ^ tsw) * 8 + thalf;
-          kT[mb] = join_tr(lds_read_tr4(Kt + off), lds_read_tr4(Kt + off + 4 * D));
-        }
+        for (int mb = 0; mb < D / 32; ++mb) kT[mb] = tile_tr8<D>(Kt, tr, tchunk + 4 * mb, thalf);
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) dq_acc[mb] = mfma32(kT[mb], dsb[half], dq_acc[mb]);
       }

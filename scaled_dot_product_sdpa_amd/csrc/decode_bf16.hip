@@ -72,7 +72,6 @@ void decode_split_kernel(DecodeArgs a) {
   const float c2 = p.scale_log2;
   const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
   const int kr = perm_row(l32);
-  const int ksw = swz(kr) & (CPR - 1);
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
@@ -90,7 +89,7 @@ void decode_split_kernel(DecodeArgs a) {
       bf16x8 kop[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(Kt + kr * D + (((2 * kk + hi) ^ ksw) * 8));
+        kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(kop[kk], qreg[kk], sacc);
     }
@@ -135,13 +134,9 @@ void decode_split_kernel(DecodeArgs a) {
     bf16x8 vop[2][D / 32];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr and tr + 4
-      const int tsw = swz(tr) & (CPR - 1);
+      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        const int off = tr * D + ((tchunk + 4 * mb) ^ tsw) * 8 + thalf;
-        vop[half][mb] = join_tr(lds_read_tr4(Vt + off), lds_read_tr4(Vt + off + 4 * D));
-      }
+      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
     }
 
 #pragma unroll

@@ -47,27 +47,7 @@ template <int D, int NW>
 struct FwdTile {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int TILE = kBN * D;       // elements per K (or V) tile
-  static constexpr int LPW = CPR / NW;       // global_load_lds per wave per tensor per tile
 };
-
-// Issue the HBM -> LDS copies of one 64-row tile (rows j0.. of `g`, clamped to the last
-// row below `stop`: a clamped row is finite and every key it stands for is masked).
-// Wave w copies the LDS chunks [w * LPW * 64, (w + 1) * LPW * 64); LDS chunk ci holds
-// logical chunk (ci % CPR) ^ swz(row) of row ci / CPR.
-template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void tile_to_lds(const bf16* g, int64_t row_stride, int j0, int stop,
-                                            bf16* lds_tile, int wave, int lane) {
-  using T = FwdTile<D, NW>;
-#pragma unroll
-  for (int i = 0; i < T::LPW; ++i) {
-    const int blk = wave * T::LPW + i;
-    const int ci = blk * 64 + lane;
-    const int r = ci / T::CPR;
-    const int c = (ci % T::CPR) ^ ((IS_V ? swz_v(r) : swz_k(r)) & (T::CPR - 1));
-    const int row = min(j0 + r, stop - 1);
-    global_to_lds16(g + (int64_t)row * row_stride + c * 8, lds_tile + blk * 512);
-  }
-}
 
 template <int D, int NW, int NQB, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
@@ -163,8 +143,8 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   // ---- K/V tiles: HBM -> LDS, double-buffered.
   auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    tile_to_lds<D, NW, false>(kb_, p.k_sl, j0, kv_stop, Kd, wave, lane);
-    tile_to_lds<D, NW, true>(vb_, p.v_sl, j0, kv_stop, Vd, wave, lane);
+    tile_to_lds_swz<kBN, D, NW>(kb_, p.k_sl, j0, kv_stop, Kd, wave, lane);
+    tile_to_lds_swz<kBN, D, NW>(vb_, p.v_sl, j0, kv_stop, Vd, wave, lane);
   };
   if (n_tiles > 0) load_tile(0, K0, V0);
   const float c2 = p.scale_log2;
@@ -203,12 +183,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
       {
         // all K operands of the block first, so the LDS reads are in flight together
         const int kr = kb * 32 + krow_l;
-        const bf16* krow = Kt + kr * D;
-        const int ksw = swz_k(kr) & (T::CPR - 1);
         bf16x8 kop[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          kop[kk] = *reinterpret_cast<const bf16x8*>(krow + (((2 * kk + hi) ^ ksw) * 8));
+        for (int kk = 0; kk < D / 16; ++kk) kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
@@ -299,14 +276,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
       bf16x8 vop[2][D / 32];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr and vr + 4
-        const bf16* vrow = Vt + vr * D + vhalf;
-        const int vsw = swz_v(vr) & (T::CPR - 1);               // same for vr + 4
+        const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr .. vr + 7
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const int off = ((vchunk + 4 * mb) ^ vsw) * 8;
-          vop[half][mb] = join_tr(lds_read_tr4(vrow + off), lds_read_tr4(vrow + 4 * D + off));
-        }
+        for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, vr, vchunk + 4 * mb, vhalf);
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half)

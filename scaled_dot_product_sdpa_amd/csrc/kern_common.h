@@ -78,6 +78,12 @@ __device__ __forceinline__ i16x4 lds_read_tr4(const bf16* p) {
       (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
 }
 
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Global -> LDS without registers: lane L's 16 bytes from `src` land at lds_base + 16 * L
 // (measured on gfx950).  lds_base must be the same for every lane of the wave.
 __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
@@ -87,23 +93,42 @@ __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base)
 // Wait until this wave's global loads (including global -> LDS copies) have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded; the
-// result is masked to the row's chunk count).  Tiles are read two ways:
-//  - 16 bytes per lane, lanes 0..7 on rows {r..r+3, r+16..r+19} (the MFMA row permutation)
-//    at one logical chunk: the map is distinct on those rows (mod 8);
-//  - ds_read_b64_tr_b16, four consecutive rows r..r+3 (r % 4 == 0) at chunks {c, c+1}
-//    (c even): the map sends the four rows' pairs to disjoint chunks (mod 8).
-// So both kinds of read touch each bank group once per eight 16-byte accesses.  The map
-// does not depend on row bit 2, so rows r and r + 4 (r % 8 < 4) share it: one transposing
-// read pair uses one swizzle.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 4) & 1); }
-__device__ __forceinline__ int swz_k(int r) { return swz(r); }
-__device__ __forceinline__ int swz_v(int r) { return swz(r); }
+// XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded).
+// gfx950 LDS has 64 four-byte banks (measured: a conflict-free pattern reads ~245 B/clk per
+// CU), i.e. sixteen 16-byte bank groups per 256 bytes.  Tiles are read two ways:
+//  - 16 bytes per lane, in 16-lane phases on rows {r..r+3, r+16..r+19, r+4..r+7,
+//    r+20..r+23} (the MFMA row permutation) at one logical chunk;
+//  - ds_read_b64_tr_b16, in 32-lane phases on four consecutive rows r..r+3 (r % 4 == 0) at
+//    four consecutive chunks {c..c+3} (c % 4 == 0).
+// For both head dims the map below sends every phase's sixteen 16-byte accesses to
+// sixteen distinct bank groups.  It depends on row bit 2, so the two row quads of one
+// transposing read pair (r and r + 4) each need their own swizzle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+  else return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+}
+
+// MFMA operand from a swizzled tile: 16 bytes (8 elements) of row r at logical chunk c.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row8(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ swz<D>(r)) * 8));
+}
+
+// Transposed MFMA operand from a swizzled tile: this lane's element column of rows
+// tr..tr+7 (two ds_read_b64_tr_b16 on the quads tr..tr+3 and tr+4..tr+7).  `c` and `h`
+// are the lane's logical chunk and 4-element half within it (see the lane map above).
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr8(const bf16* tile, int tr, int c, int h) {
+  const int o0 = tr * D + ((c ^ swz<D>(tr)) * 8) + h;
+  const int o1 = (tr + 4) * D + ((c ^ swz<D>(tr + 4)) * 8) + h;
+  return join_tr(lds_read_tr4(tile + o0), lds_read_tr4(tile + o1));
+}
 
 // HBM -> LDS copy of one tile of ROWS rows x D bf16 (rows r0.. of `g`, clamped to the row
 // below `stop`, so a clamped row repeats finite data whose pairs the caller masks) by the
 // NW waves of the workgroup.  LDS chunk ci of the tile holds logical chunk
-// (ci % CPR) ^ swz(row) of row ci / CPR.
+// (ci % CPR) ^ swz<D>(row) of row ci / CPR.
 template <int ROWS, int D, int NW>
 __device__ __forceinline__ void tile_to_lds_swz(const bf16* g, int64_t row_stride, int r0,
                                                 int stop, bf16* lds_tile, int wave, int lane) {
@@ -115,16 +140,10 @@ __device__ __forceinline__ void tile_to_lds_swz(const bf16* g, int64_t row_strid
     const int blk = wave * (NBLK / NW) + i;
     const int ci = blk * 64 + lane;
     const int r = ci / CPR;
-    const int c = (ci % CPR) ^ (swz(r) & (CPR - 1));
+    const int c = (ci % CPR) ^ swz<D>(r);
     const int row = min(r0 + r, stop - 1);
     global_to_lds16(g + (int64_t)row * row_stride + c * 8, lds_tile + blk * 512);
   }
-}
-
-__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, r);
 }
 
 }  // namespace sdpa
