@@ -6,14 +6,13 @@
 // one-pass online softmax (running max and sum; the page's "Going further" table names
 // Milakov and Gimelshein's online normaliser).
 //
-// Work decomposition: a workgroup of NW waves owns BM = NW * 32 * NQB query rows of one
-// (batch, head); each wave owns NQB blocks of 32 query rows and keeps their Q operand, O
-// accumulator and running statistics in registers.  K/V tiles of 64 keys stream
-// HBM -> LDS with global_load_lds (16 bytes per lane, no staging registers) into two
-// LDS buffers: tile t+1 is in flight while tile t is computed, one barrier per tile.
-// Tiles are stored unpadded with XOR-swizzled 16-byte chunks (kern_common.h) so the MFMA
-// operand reads are free of bank conflicts.  With NQB = 2 every K/V operand read from
-// LDS feeds two MFMAs, which halves LDS traffic per flop.
+// Work decomposition: a workgroup of NW waves owns BM = NW * 32 query rows of one
+// (batch, head); each wave owns 32 query rows and keeps their Q operand, O accumulator
+// and running statistics in registers.  K/V tiles of 64 keys stream HBM -> LDS with
+// global_load_lds (16 bytes per lane, no staging registers) through three LDS buffers:
+// while tile t is computed, tile t+1 is resident or landing and tile t+2 is requested,
+// one barrier per tile.  Tiles are stored unpadded with XOR-swizzled 16-byte chunks
+// (kern_common.h) so the MFMA operand reads are free of bank conflicts.
 //
 //   S^T = K Q^T   (keys x queries): A = K rows from LDS (row-permuted, see kern_common.h),
 //                 B = Q held in registers; lane l ends up with 16 consecutive keys of
@@ -23,17 +22,23 @@
 //                 straight from the S accumulator registers.  O^T keeps one query per
 //                 lane, so a rescale is a per-lane multiply.
 //
+// Software pipeline inside each wave: the softmax of a 32-key block costs about as many
+// SIMD cycles (16 exponentials and ~70 other vector ops per lane) as its 16 MFMAs, so
+// the S MFMAs of block b+1 are issued interleaved with the softmax arithmetic of block b
+// and the matrix and vector units of the SIMD work at the same time; the PV MFMAs of
+// block b follow.
+//
 // Softmax arithmetic per score: one FMA folds scale * log2(e) and the reference max into
 // the exp2 argument; v_exp_f32; v_cvt_pk_bf16_f32; the bf16 weights are summed with
 // v_dot2 (this sum normalises O, so each output row is an exact convex combination of
 // value rows) and the fp32 weights with one add (this sum gives LSE).  The reference max
 // is only moved when a row's max grows by more than 2^8 (weights stay <= 256, exact in
-// fp32 sums and in bf16 range), so the O rescale runs on a few tiles only.
+// fp32 sums and in bf16 range), so the O rescale runs on a few blocks only.
 //
 // Tiles entirely above the causal diagonal or past the key length are never visited, and
-// a wave skips the 32-key blocks that none of its rows can see.  Only tiles touching the
-// diagonal or a length boundary evaluate per-element predicates.  Rows with no visible
-// key produce O = 0, LSE = -inf.
+// a wave works only on the 32-key blocks that some of its rows can see (a prefix of the
+// key range).  Only blocks touching the diagonal or a length boundary evaluate
+// per-element predicates.  Rows with no visible key produce O = 0, LSE = -inf.
 #include "kern_common.h"
 #include "launch.h"
 
@@ -43,20 +48,18 @@ namespace {
 constexpr int kBN = 64;             // keys per K/V tile (two 32-key MFMA blocks)
 constexpr float kRescaleLog2 = 8.f; // move the reference max only past this growth
 
-template <int D, int NW>
-struct FwdTile {
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int TILE = kBN * D;       // elements per K (or V) tile
-};
-
-template <int D, int NW, int NQB, bool CAUSAL, bool MASK>
+template <int D, int NW, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
-  using T = FwdTile<D, NW>;
-  constexpr int BM = NW * 32 * NQB;
-  __shared__ __attribute__((aligned(16))) bf16 K0[T::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K1[T::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V0[T::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V1[T::TILE];
+  constexpr int BM = NW * 32;
+  constexpr int TILE = kBN * D;
+  // global_load_lds instructions per wave for one K+V tile
+  constexpr int LOADS_PER_TILE = 2 * (kBN * D / 8 / 64) / NW;
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   int wq_lo, row_lo, row_hi;  // this wave's first row; the workgroup's row span
   if (CAUSAL && !p.pair_rows) {
     const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
-    wq_lo = qt * BM + wave * 32 * NQB;
+    wq_lo = qt * BM + wave * 32;
     row_lo = qt * BM;
     row_hi = row_lo + BM;
   } else if (CAUSAL) {
@@ -91,15 +94,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     const int n_half = (p.Lq + HB - 1) / HB;
     const int heavy = n_half - 1 - rank;
     const int mine = wave < NW / 2 ? rank : heavy;
-    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32 * NQB;
+    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32;
     row_lo = rank * HB;
     row_hi = (heavy + 1) * HB;
   } else {
-    wq_lo = rank * BM + wave * 32 * NQB;
+    wq_lo = rank * BM + wave * 32;
     row_lo = rank * BM;
     row_hi = row_lo + BM;
   }
-  const int wq_hi = min(wq_lo + 32 * NQB, q_end) - 1;     // this wave's last live row
+  const int wq_hi = min(wq_lo + 32, q_end) - 1;  // this wave's last live row
 
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
   const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
@@ -113,40 +116,39 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
+  // 32-key blocks this wave works on: a prefix of the keys.
+  int vis_stop = wq_lo < q_end ? kv_stop : 0;
+  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1);
+  const int nvis = (vis_stop + 31) / 32;
 
+  // ---- K/V tiles: HBM -> LDS (rows past kv_stop arrive as zeros).
+  TileCopy<kBN, D, NW> kcopy, vcopy;
+  kcopy.init(p.k_sl, wave, lane);
+  vcopy.init(p.v_sl, wave, lane);
+  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
+    kcopy.copy(rows_rsrc<D>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
+    vcopy.copy(rows_rsrc<D>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
+  };
   // ---- Q operand (B of S^T = K Q^T): lane holds query row, 8 consecutive d per k-step.
-  bf16x8 qreg[NQB][D / 16];
-  int qrow[NQB];
+  const int qrow = wq_lo + l32;
+  bf16x8 qreg[D / 16];
 #pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    qrow[nb] = wq_lo + nb * 32 + l32;
-    const bool ok = qrow[nb] < q_end;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = ok ? ld16(qb + (int64_t)qrow[nb] * p.q_sl + kk * 16 + 8 * hi) : zero16();
-      qreg[nb][kk] = __builtin_bit_cast(bf16x8, x);
-    }
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 x = qrow < q_end ? ld16(qb + (int64_t)qrow * p.q_sl + kk * 16 + 8 * hi) : zero16();
+    qreg[kk] = __builtin_bit_cast(bf16x8, x);
   }
+  // first two tiles in flight behind Q
+  if (n_tiles > 0) load_tile(0, K0, V0);
+  if (n_tiles > 1) load_tile(kBN, K1, V1);
 
   // reference max (log2 units), sum of bf16 weights (normalises O), sum of fp32 weights
   // (gives LSE); both sums are relative to the reference max.
-  f32x16 oacc[NQB][D / 32];
-  float mref[NQB], lrow[NQB], frow[NQB];
+  f32x16 oacc[D / 32];
+  // frow is kept as two partial sums (even / odd scores) so the adds form two chains
+  float mref = kNegInf, lrow = 0.f, frow = 0.f, frow2 = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    mref[nb] = kNegInf;
-    lrow[nb] = 0.f;
-    frow[nb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[nb][mb] = f32x16{};
-  }
+  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
 
-  // ---- K/V tiles: HBM -> LDS, double-buffered.
-  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    tile_to_lds_swz<kBN, D, NW>(kb_, p.k_sl, j0, kv_stop, Kd, wave, lane);
-    tile_to_lds_swz<kBN, D, NW>(vb_, p.v_sl, j0, kv_stop, Vd, wave, lane);
-  };
-  if (n_tiles > 0) load_tile(0, K0, V0);
   const float c2 = p.scale_log2;
   const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
   // K operand read: row kb*32 + perm_row(l32), logical chunk 2*kk + hi
@@ -157,185 +159,254 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int vchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int vhalf = 4 * (lane & 1);
 
-  // One tile step; the loop below is unrolled by two so that the buffer being read and
-  // the one being filled are distinct LDS objects at compile time (the compiler then
-  // does not make the reads of tile t wait for the copies of tile t+1).
-  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
-                  __attribute__((always_inline)) {
-    const int j0 = t * kBN;
-    wait_vmem();       // this wave's copies of tile t have landed
-    __syncthreads();   // ... and everyone's; the other buffer is no longer being read
-    if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
-
-    // The tile's two 32-key blocks one after the other: S^T, softmax, then PV.
-    const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo) ||
-                           (wq_lo + 32 * NQB > q_end);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key_lo = j0 + kb * 32;
-      // a block none of this wave's rows can see is skipped (wave-uniform)
-      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi))) continue;
-
-      // ---- S^T = K Q^T for keys key_lo .. key_lo + 31
-      f32x16 sacc[NQB];
-#pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) sacc[nb] = f32x16{};
-      {
-        // all K operands of the block first, so the LDS reads are in flight together
-        const int kr = kb * 32 + krow_l;
-        bf16x8 kop[D / 16];
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-          for (int nb = 0; nb < NQB; ++nb) sacc[nb] = mfma32(kop[kk], qreg[nb][kk], sacc[nb]);
-      }
-
-      // ---- online softmax; lane holds keys key0 + v (v < 16) of query qrow[nb].
-      const int key0 = key_lo + 16 * hi;
-      bf16x8 pop[NQB][2];
-#pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) {
-        const int qi = qrow[nb];
-        // x: raw dot products (no mask) or log2-unit scores (mask)
-        float x[16];
-        if (MASK) {
-          float mv[16];
-          if (p.mask_vec && qi < q_end && key0 + 16 <= p.Lk) {
-            const bf16* mp = mb_ + (int64_t)qi * p.m_si + key0;
-            bf16x8 b0 = __builtin_bit_cast(bf16x8, ld16(mp)), b1 = __builtin_bit_cast(bf16x8, ld16(mp + 8));
-#pragma unroll
-            for (int v = 0; v < 8; ++v) { mv[v] = bf2f(b0[v]); mv[v + 8] = bf2f(b1[v]); }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              mv[v] = (qi < q_end && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) : 0.f;
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) x[v] = fmaf(sacc[nb][v], c2, mv[v] * kLog2e);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) x[v] = sacc[nb][v];
-        }
-        if (partial_t) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + v;
-            const bool ok = key < kv_end && qi < q_end && (!CAUSAL || key <= qi);
-            x[v] = ok ? x[v] : kNegInf;
-          }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        mx = xhalf_max(mx);
-        const float mt = MASK ? mx : mx * c2;  // block max in log2 units (c2 > 0)
-        // lazy rescale: move the reference only when some row grew past the threshold
-        const bool need = mt > mref[nb] + kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float mnew = need ? mt : mref[nb];
-          const float corr = need ? fast_exp2(mref[nb] - mnew) : 1.f;
-          mref[nb] = mnew;
-          lrow[nb] *= corr;
-          frow[nb] *= corr;
-#pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) oacc[nb][mb] *= corr;
-        }
-        const float m_use = (mref[nb] == kNegInf) ? 0.f : mref[nb];
-        float psum = lrow[nb], fsum = frow[nb];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 pb;
-#pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            const int v = half * 8 + 2 * t2;
-            f32x2 e;
-            if (MASK) {
-              e[0] = fast_exp2(x[v] - m_use);
-              e[1] = fast_exp2(x[v + 1] - m_use);
-            } else {
-              e[0] = fast_exp2(fmaf(x[v], c2, -m_use));
-              e[1] = fast_exp2(fmaf(x[v + 1], c2, -m_use));
-            }
-            const bf16x2 e2 = __builtin_convertvector(e, bf16x2);
-            psum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, psum, false);
-            fsum += e[0];
-            fsum += e[1];
-            pb[2 * t2] = e2[0];
-            pb[2 * t2 + 1] = e2[1];
-          }
-          pop[nb][half] = pb;
-        }
-        lrow[nb] = psum;
-        frow[nb] = fsum;
-      }
-
-      // ---- O^T += V^T P^T.  V^T operand via transposing LDS reads: lane (within its
-      // 16-lane block) supplies row  key_base + (lane%16)/4, columns d_base + 4*(lane%4).
-      bf16x8 vop[2][D / 32];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr .. vr + 7
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, vr, vchunk + 4 * mb, vhalf);
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NQB; ++nb) oacc[nb][mb] = mfma32(vop[half][mb], pop[nb][half], oacc[nb][mb]);
+  // Mask values of block `bi` for this lane (keys 32*bi + 16*hi + 0..15 of row qrow),
+  // read one block ahead.  Rows whose mask cannot be read with 16-byte loads take the
+  // element path in `scores`.
+  auto mask_vec_ok = [&](int bi) {
+    return p.mask_vec && qrow < q_end && 32 * bi + 16 * hi + 16 <= p.Lk;
+  };
+  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
+    if (MASK && bi < nvis && mask_vec_ok(bi)) {
+      const bf16* mp = mb_ + (int64_t)qrow * p.m_si + 32 * bi + 16 * hi;
+      m[0] = ld16(mp);
+      m[1] = ld16(mp + 8);
+    } else {
+      m[0] = zero16();
+      m[1] = zero16();
     }
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, K0, V0, K1, V1);
-    if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
+
+  constexpr int NS = D / 16;  // S MFMAs per block = K operand reads = PV MFMAs = V reads
+  constexpr int E = 16 / NS;  // scores per lane handled in one pipeline slot
+  constexpr int KPRE = 2;     // K operand reads issued ahead of their MFMA
+
+  auto read_k1 = [&](const bf16* Kt, int kb, int kk) {
+    return tile_row8<D>(Kt, kb * 32 + krow_l, 2 * kk + hi);
+  };
+  // V^T operand i (half i / (D/32), d-block i % (D/32)) of the block at rows kb*32..
+  auto read_v1 = [&](const bf16* Vt, int kb, int i) {
+    const int half = i / (D / 32), mb = i % (D / 32);
+    const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr .. vr + 7
+    return tile_tr8<D>(Vt, vr, vchunk + 4 * mb, vhalf);
+  };
+
+  // Scores of block bi before the max, in place in its S accumulator: raw dot products,
+  // or log2-unit scores with a mask; -inf where a block touching a boundary hides a key.
+  auto pre_scores = [&](int bi, f32x16& x, const u32x4 (&mk)[2]) {
+    const int key_lo = 32 * bi;
+    const int key0 = key_lo + 16 * hi;
+    if (MASK) {
+      float mv[16];
+      if (mask_vec_ok(bi)) {
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, mk[0]), b1 = __builtin_bit_cast(bf16x8, mk[1]);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) { mv[v] = bf2f(b0[v]); mv[v + 8] = bf2f(b1[v]); }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          mv[v] = (qrow < q_end && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qrow * p.m_si + key0 + v]) : 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], c2, mv[v] * kLog2e);
+    }
+    const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo) ||
+                         (wq_lo + 32 > q_end);
+    if (partial) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + v;
+        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow);
+        x[v] = ok ? x[v] : kNegInf;
+      }
+    }
+  };
+
+  // Row max of the block (partial maxima `mx` over the lane's scores) -> moves the
+  // reference max if some row grew past the threshold; returns the exp2 offset.
+  auto post_max = [&](float mx) {
+    mx = xhalf_max(mx);
+    const float mt = MASK ? mx : mx * c2;  // block max in log2 units (c2 > 0)
+    const bool need = mt > mref + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? mt : mref;
+      const float corr = need ? fast_exp2(mref - mnew) : 1.f;
+      mref = mnew;
+      lrow *= corr;
+      frow *= corr;
+      frow2 *= corr;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+    }
+    return (mref == kNegInf) ? 0.f : mref;
+  };
+
+  // Weights of score pair pr (scores 2pr, 2pr+1) in three stages one pipeline slot apart,
+  // so that no stage waits on the result of the one before it:
+  //   A: exp2 argument;  B: exp2;  C: bf16 B operand of O^T += V^T P^T, both sums.
+  auto stage_a = [&](const f32x16& x, float m_use, int pr, f32x2 (&t)[8]) {
+    if (MASK) {
+      t[pr][0] = x[2 * pr] - m_use;
+      t[pr][1] = x[2 * pr + 1] - m_use;
+    } else {
+      t[pr][0] = fmaf(x[2 * pr], c2, -m_use);
+      t[pr][1] = fmaf(x[2 * pr + 1], c2, -m_use);
+    }
+  };
+  auto stage_b = [&](int pr, f32x2 (&t)[8]) {
+    t[pr][0] = fast_exp2(t[pr][0]);
+    t[pr][1] = fast_exp2(t[pr][1]);
+  };
+  auto stage_c = [&](int pr, const f32x2 (&t)[8], bf16x8 (&pop)[2]) {
+    const bf16x2 e2 = __builtin_convertvector(t[pr], bf16x2);
+    lrow = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, lrow, false);
+    frow += t[pr][0];
+    frow2 += t[pr][1];
+    pop[pr / 4][2 * (pr % 4)] = e2[0];
+    pop[pr / 4][2 * (pr % 4) + 1] = e2[1];
+  };
+
+  // PV operands of the previous block, consumed one block late (zero before the first).
+  bf16x8 pv_v[NS];
+  bf16x8 pv_p[2];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) pv_v[i] = bf16x8{};
+  pv_p[0] = bf16x8{};
+  pv_p[1] = bf16x8{};
+  auto pv_mfma1 = [&](int i) {
+    const int half = i / (D / 32), mb = i % (D / 32);
+    oacc[mb] = mfma32(pv_v[i], pv_p[half], oacc[mb]);
+  };
+
+  // S of the current block and of the next one; the two phases of a tile step swap them.
+  f32x16 sacc_a = f32x16{}, sacc_b = f32x16{};
+  u32x4 mk[2];
+  load_mask(0, mk);
+
+  // ---- one pipeline phase for block bi (V rows kb*32.. of Vt; the next block's K rows
+  // kbn*32.. of Kn).  Region 1: PV MFMAs of block bi-1 with the row max of block bi.
+  // Region 2: S MFMAs of block bi+1 with the exponentials and sums of block bi, the K
+  // operand reads of block bi+1 and the V operand reads of block bi.  Slots are fenced
+  // with sched_barrier so each MFMA issues next to its share of vector work.
+  // The S of block bi+1 is computed even past the wave's last block (from whatever the
+  // buffer holds; never used), which keeps one code path.
+  auto body = [&](int bi, const bf16* Vt, int kb, const bf16* Kn, int kbn, f32x16& x,
+                  f32x16& snext) __attribute__((always_inline)) {
+    u32x4 mk_next[2];
+    bf16x8 kop[NS];
+    pre_scores(bi, x, mk);
+    // region 1
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j < KPRE) kop[j] = read_k1(Kn, kbn, j);
+      if (MASK && j == 0) load_mask(bi + 1, mk_next);
+      pv_mfma1(j);
+#pragma unroll
+      for (int v = j * E; v < (j + 1) * E; ++v) mx = fmaxf(mx, x[v]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float m_use = post_max(mx);
+    // region 2
+    snext = f32x16{};
+    constexpr int P = 8 / NS;  // score pairs per slot
+    f32x2 t[8];
+#pragma unroll
+    for (int pr = 0; pr < 2 * P; ++pr) stage_a(x, m_use, pr, t);
+#pragma unroll
+    for (int pr = 0; pr < P; ++pr) stage_b(pr, t);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + KPRE < NS) kop[i + KPRE] = read_k1(Kn, kbn, i + KPRE);
+      pv_v[i] = read_v1(Vt, kb, i);
+      snext = mfma32(kop[i], qreg[i], snext);
+#pragma unroll
+      for (int pr = (i + 2) * P; pr < (i + 3) * P && pr < 8; ++pr) stage_a(x, m_use, pr, t);
+#pragma unroll
+      for (int pr = (i + 1) * P; pr < (i + 2) * P && pr < 8; ++pr) stage_b(pr, t);
+#pragma unroll
+      for (int pr = i * P; pr < (i + 1) * P; ++pr) stage_c(pr, t, pv_p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MASK) { mk[0] = mk_next[0]; mk[1] = mk_next[1]; }
+  };
+  auto phase = [&](int bi, const bf16* Vt, int kb, const bf16* Kn, int kbn, f32x16& sacc,
+                   f32x16& snext) __attribute__((always_inline)) {
+    if (bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext);
+  };
+
+  // One tile step; the loop below is unrolled by three so that the buffers being read,
+  // the next tile's and the one being filled are distinct LDS objects at compile time
+  // (the compiler then does not make the reads wait for the copies in flight).
+  auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl)
+                  __attribute__((always_inline)) {
+    // block 2t: V from this tile, K of block 2t+1 from this tile
+    phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b);
+    // tile t+1 has landed for every wave, and no wave still reads tile t-1
+    if (t + 1 < n_tiles) wait_vmem();
+    __syncthreads();
+    if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
+    // block 2t+1: V from this tile, K of block 2t+2 from the next tile
+    phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a);
+  };
+
+  if (n_tiles > 0) {
+    // tile 0 (and Q) landed; tile 1 may still be in flight
+    if (n_tiles > 1) wait_vmem_le<LOADS_PER_TILE>();
+    else wait_vmem();
+    __syncthreads();
+    if (nvis > 0) {
+#pragma unroll
+      for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(K0, 0, kk), qreg[kk], sacc_a);
+    }
   }
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, K0, V0, K1, K2, V2);
+    if (t + 1 < n_tiles) step(t + 1, K1, V1, K2, K0, V0);
+    if (t + 2 < n_tiles) step(t + 2, K2, V2, K0, K1, V1);
+  }
+  // the last block's PV
+#pragma unroll
+  for (int j = 0; j < NS; ++j) pv_mfma1(j);
 
   // ---- epilogue: O = O^T / l (0 for empty rows), LSE = ln2 * (mref + log2 f).
+  const float lt = xhalf_sum(lrow);
+  const float ft = xhalf_sum(frow + frow2);
+  const bool rowlive = qrow < q_end && lt > 0.f;
+  const float inv = rowlive ? 1.f / lt : 0.f;
+  if (qrow < p.Lq) {
+    bf16* orow = ob + (int64_t)qrow * p.o_sl;
 #pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) {
-    const int qi = qrow[nb];
-    const float lt = xhalf_sum(lrow[nb]);
-    const float ft = xhalf_sum(frow[nb]);
-    const bool rowlive = qi < q_end && lt > 0.f;
-    const float inv = rowlive ? 1.f / lt : 0.f;
-    if (qi < p.Lq) {
-      bf16* orow = ob + (int64_t)qi * p.o_sl;
+    for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 w;
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[nb][mb][v4 * 4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + mb * 32 + v4 * 8 + hi * 4) = w;
-        }
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(oacc[mb][v4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + mb * 32 + v4 * 8 + hi * 4) = w;
       }
-      if (lseb && hi == 0) lseb[qi] = rowlive ? (mref[nb] * kLn2 + logf(ft)) : kNegInf;
     }
+    if (lseb && hi == 0) lseb[qrow] = rowlive ? (mref * kLn2 + logf(ft)) : kNegInf;
   }
 }
 
-template <int D, int NW, int NQB, bool CAUSAL, bool MASK>
+template <int D, int NW, bool CAUSAL, bool MASK>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = NW * 32 * NQB;
+  constexpr int BM = NW * 32;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
   FwdArgs args = a;
   // pair half-tiles when whole tiles would give about one round of workgroups
   args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
   const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
   const int grid = n_wg * a.p.B * a.p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NQB, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_shape(const FwdArgs& a, hipStream_t s) {
   // 8 waves of 32 query rows per workgroup: two waves per SIMD hide each other's LDS and
-  // MFMA latencies, which measured faster than 64 rows per wave at one wave per SIMD.
-  return launch_t<D, 8, 1, CAUSAL, MASK>(a, s);
+  // MFMA latencies.
+  return launch_t<D, 8, CAUSAL, MASK>(a, s);
 }
 
 template <int D>

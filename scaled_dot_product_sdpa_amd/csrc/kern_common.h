@@ -92,6 +92,9 @@ __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base)
 
 // Wait until this wave's global loads (including global -> LDS copies) have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// ... until at most N of them are outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded).
 // gfx950 LDS has 64 four-byte banks (measured: a conflict-free pattern reads ~245 B/clk per
@@ -145,5 +148,61 @@ __device__ __forceinline__ void tile_to_lds_swz(const bf16* g, int64_t row_strid
     global_to_lds16(g + (int64_t)row * row_stride + c * 8, lds_tile + blk * 512);
   }
 }
+
+// ---- HBM -> LDS through a buffer resource (buffer_load ... lds): the per-lane byte offset
+// inside a tile is fixed, so after set-up a tile copy costs no vector instructions; the
+// tile's first row moves with the (scalar) resource base.
+
+// The resource type exists only for the GPU target; the host pass of this single-source
+// file parses the device functions with a placeholder.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+#else
+struct buf_rsrc_t { uint32_t w[4]; };
+#endif
+
+// Raw buffer over rows r0 .. stop-1 of a row-major bf16 matrix (row_stride elements, rows
+// of D elements); reads at or past row `stop` return zeros.
+template <int D>
+__device__ __forceinline__ buf_rsrc_t rows_rsrc(const bf16* base, int64_t row_stride, int r0, int stop) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int64_t bytes = stop > r0 ? (int64_t)(stop - 1 - r0) * row_stride * 2 + D * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)r0 * row_stride),
+                                           (short)0, (int)bytes, 0x00020000);
+#else
+  return buf_rsrc_t{};
+#endif
+}
+
+// Per-lane byte offsets of a ROWS x D tile copy by NW waves: instruction i of wave w moves
+// LDS chunks (w * NBLK/NW + i) * 64 + lane, chunk ci holding logical chunk
+// (ci % CPR) ^ swz<D>(row) of row ci / CPR (the layout tile_to_lds_swz writes).
+template <int ROWS, int D, int NW>
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int NBLK = ROWS * CPR / 64;  // 1 KB wave-instructions per tile
+  static constexpr int PER_WAVE = NBLK / NW;
+  static_assert(NBLK % NW == 0, "tile must split evenly over the waves");
+  uint32_t voff[PER_WAVE];
+  __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int ci = (wave * PER_WAVE + i) * 64 + lane;
+      const int r = ci / CPR;
+      const int c = (ci % CPR) ^ swz<D>(r);
+      voff[i] = (uint32_t)(r * row_stride * 2 + c * 16);
+    }
+  }
+  __device__ __forceinline__ void copy(buf_rsrc_t src, bf16* lds_tile, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    wave = __builtin_amdgcn_readfirstlane(wave);  // the LDS destination is wave-uniform
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src, (__attribute__((address_space(3))) void*)(lds_tile + (wave * PER_WAVE + i) * 512), 16,
+          voff[i], 0, 0, 0);
+#endif
+  }
+};
 
 }  // namespace sdpa
