@@ -14,12 +14,14 @@
 //            both fp32 into the workspace.
 //  2. dkdv:  key-stationary.  A workgroup owns 32 * NW keys of one (batch, KV head); each
 //            wave keeps its 32 keys' K and V operands and their dK^T, dV^T accumulators in
-//            registers, and walks the query heads of the group and their 32-row query
-//            tiles.  Q, dO (and lse2, D) tiles stream HBM -> LDS with global_load_lds into
-//            two buffers (tile t+1 in flight while tile t is computed).  Per 32x32 block:
+//            registers, and walks the query heads of the group and their 64-row query
+//            tiles.  Q, dO (and lse2, D) tiles stream HBM -> LDS with buffer loads through
+//            three buffers (one barrier per tile).  Per 32x32 block:
 //              S = Q K^T,  P = exp2(S * scale * log2e - lse2),  dP = dO V^T,
 //              dS = P o (dP - D),  dV^T += dO^T P,  dK^T += Q^T dS
-//            with dO^T and Q^T read from LDS by ds_read_b64_tr_b16.
+//            with dO^T and Q^T read from LDS by ds_read_b64_tr_b16.  Inside a wave the
+//            blocks are software-pipelined: the dV, dK MFMAs of block b-1 run with the P, dS
+//            arithmetic of block b, and the S, dP MFMAs of block b+1 with the rest of it.
 //  3. dq:    query-stationary (the forward's decomposition, 8 waves of 32 rows).  Per
 //            32-key block of a double-buffered 64-key K/V tile:
 //              S^T = K Q^T,  P^T,  dP^T = V dO^T,  dS^T = P^T o (dP^T - D),
@@ -72,22 +74,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------------------
-constexpr int kQT = 32;  // query rows per inner tile
+constexpr int kQT = 64;  // query rows per LDS tile (two 32-row blocks)
 
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int KT = 32 * NW;   // keys per workgroup
-  constexpr int CPR = D / 8;
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int KT = 32 * NW;    // keys per workgroup
   constexpr int TILE = kQT * D;
+  constexpr int NS = D / 16;     // MFMAs of one S (or dP) block
+  constexpr int NT = D / 32;     // MFMAs of one half of a dV (or dK) block
+  constexpr int R1 = 4 * NT;     // slots of region 1 (dV, dK MFMAs)
+  constexpr int R2 = 2 * NS;     // slots of region 2 (S, dP MFMAs)
+  constexpr int E1 = 16 / R1;    // scores per lane per region-1 slot
+  constexpr int MT = MASK ? kQT * KT : 8;
   __shared__ __attribute__((aligned(16))) bf16 Q0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 Q1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Q2[TILE];
   __shared__ __attribute__((aligned(16))) bf16 G0[TILE];  // dO
   __shared__ __attribute__((aligned(16))) bf16 G1[TILE];
-  __shared__ __attribute__((aligned(16))) float S0[2 * kQT];  // lse2 rows, then D rows
-  __shared__ __attribute__((aligned(16))) float S1[2 * kQT];
+  __shared__ __attribute__((aligned(16))) bf16 G2[TILE];
+  __shared__ __attribute__((aligned(16))) float R0[2 * kQT];  // lse2 rows, then D rows
+  __shared__ __attribute__((aligned(16))) float R1s[2 * kQT];
+  __shared__ __attribute__((aligned(16))) float R2s[2 * kQT];
   // mask tiles (kQT rows x KT keys, unswizzled), used when mask rows allow 16-byte copies
-  __shared__ __attribute__((aligned(16))) bf16 M0[MASK ? kQT * KT : 8];
-  __shared__ __attribute__((aligned(16))) bf16 M1[MASK ? kQT * KT : 8];
+  __shared__ __attribute__((aligned(16))) bf16 M0[MT];
+  __shared__ __attribute__((aligned(16))) bf16 M1[MT];
+  __shared__ __attribute__((aligned(16))) bf16 M2[MT];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -111,151 +122,250 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
   const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
 
-  // K and V operands of this lane's key (B operands of S = Q K^T and dP = dO V^T).
-  bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const bool ok = myk < kv_end;
-    kreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(kbase + (int64_t)myk * p.k_sl + kk * 16 + 8 * hi) : zero16());
-    vreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(vbase + (int64_t)myk * p.v_sl + kk * 16 + 8 * hi) : zero16());
-  }
-
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) { dk_acc[mb] = f32x16{}; dv_acc[mb] = f32x16{}; }
-
-  // Query tiles that can see any key of this workgroup.
+  // Query tiles that can see any key of this workgroup; the G heads of the group in turn.
   const int kstop = min(kv_end, j0 + KT);
   const int qt_begin = CAUSAL ? j0 / kQT : 0;
   const int qt_end = (j0 < kstop) ? (q_end + kQT - 1) / kQT : 0;
   const int n_q_tiles = qt_end > qt_begin ? qt_end - qt_begin : 0;
   const int total = n_q_tiles * p.G;
-
   auto tile_rows = [&](int it, int& h, int& i0) {
     h = g * p.G + it / n_q_tiles;
     i0 = (qt_begin + it % n_q_tiles) * kQT;
   };
-  auto load_tile = [&](int it, bf16* Qd, bf16* Gd, float* Sd, bf16* Md) {
+
+  // ---- tiles HBM -> LDS: Q and dO rows (swizzled), lse2 and D rows, mask rows.
+  TileCopy<kQT, D, NW> qcopy, gcopy;
+  qcopy.init(p.q_sl, wave, lane);
+  gcopy.init(p.o_sl, wave, lane);
+  constexpr int MCPR = KT / 8, MPW = kQT * MCPR / 64 / NW;  // mask: 16-byte chunks per row, per wave
+  uint32_t mvoff[MASK ? MPW : 1];
+  if (MASK) {
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int ci = (wave * MPW + i) * 64 + lane;
+      mvoff[i] = (uint32_t)((ci / MCPR) * p.m_si * 2 + (ci % MCPR) * 16);
+    }
+  }
+  auto load_tile = [&](int it, bf16* Qd, bf16* Gd, float* Rd, bf16* Md) {
     int h, i0;
     tile_rows(it, h, i0);
     const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
     const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + b * p.o_sb + h * p.o_sh;
-    tile_to_lds_swz<kQT, D, NW>(qb, p.q_sl, i0, q_end, Qd, wave, lane);
-    tile_to_lds_swz<kQT, D, NW>(dob, p.o_sl, i0, q_end, Gd, wave, lane);
-    if (MASK && p.mask_vec) {
-      // rows past Lq and 8-key chunks past Lk (Lk % 8 == 0 here) repeat valid memory;
-      // the pairs they stand for are masked by the predicates
-      constexpr int CPRM = KT / 8, NBLK = kQT * CPRM / 64;
-      const bf16* mb = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh;
-#pragma unroll
-      for (int i = 0; i < NBLK / NW; ++i) {
-        const int blk = wave * (NBLK / NW) + i;
-        const int ci = blk * 64 + lane;
-        const int row = min(i0 + ci / CPRM, p.Lq - 1);
-        const int col = min(j0 + (ci % CPRM) * 8, p.Lk - 8);
-        global_to_lds16(mb + (int64_t)row * p.m_si + col, Md + blk * 512);
-      }
+    qcopy.copy(rows_rsrc<D, kQT>(qb, p.q_sl, i0, q_end), Qd, wave);
+    gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+    if (uw < 2) {
+      // lse2 (wave 0) and D (wave 1) of the tile's rows; rows past Lq arrive as zeros and
+      // are masked by the predicates
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq + i0;
+      const float* src = (uw ? a.dsum : a.lse2) + rb;
+      buffer_to_lds<4>(raw_rsrc(src, (int64_t)max(min(p.Lq - i0, kQT), 0) * 4), Rd + uw * kQT, lane * 4);
     }
-    if (wave == NW - 1) {
-      // lse2 (lanes 0..31) and D (lanes 32..63) of the tile's rows; rows past Lq repeat
-      // the last row and are masked by the predicates
-      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq;
-      const int row = min(i0 + l32, p.Lq - 1);
-      const float* src = (hi ? a.dsum : a.lse2) + rb + row;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)Sd, 4, 0, 0);
+    if (MASK && p.mask_vec) {
+      // keys past Lk read the next row (or zeros past the end); those pairs are masked
+      const bf16* mb = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh +
+                       (int64_t)i0 * p.m_si + j0;
+      const int nr = min(p.Lq - i0, kQT);
+      const buf_rsrc_t rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
+      const int mw = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+      for (int i = 0; i < MPW; ++i) buffer_to_lds<16>(rs, Md + (mw * MPW + i) * 512, mvoff[i]);
     }
   };
 
-  const float c2 = p.scale_log2;
-  const int qr = perm_row(l32);              // Q / dO row read by this lane (S, dP)
+  // K and V operands of this lane's key (B operands of S = Q K^T and dP = dO V^T).
+  bf16x8 kreg[NS], vreg[NS];
+#pragma unroll
+  for (int kk = 0; kk < NS; ++kk) {
+    const bool ok = myk < kv_end;
+    kreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(kbase + (int64_t)myk * p.k_sl + kk * 16 + 8 * hi) : zero16());
+    vreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(vbase + (int64_t)myk * p.v_sl + kk * 16 + 8 * hi) : zero16());
+  }
+  if (total > 0) load_tile(0, Q0, G0, R0, M0);
+  if (total > 1) load_tile(1, Q1, G1, R1s, M1);
 
+  f32x16 dk_acc[NT], dv_acc[NT];
+#pragma unroll
+  for (int mb = 0; mb < NT; ++mb) { dk_acc[mb] = f32x16{}; dv_acc[mb] = f32x16{}; }
+
+  const float c2 = p.scale_log2;
+  const int qr = perm_row(l32);  // Q / dO row read by this lane (A operands of S, dP)
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
 
-  auto step = [&](int it, const bf16* Qt, const bf16* Gt, const float* St, const bf16* Mt,
-                  bf16* Qn, bf16* Gn, float* Sn, bf16* Mn) __attribute__((always_inline)) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < total) load_tile(it + 1, Qn, Gn, Sn, Mn);
+  // dV, dK of a block run one block late: B operands bf16 P and dS (zero before the first
+  // block), A operands transposed dO and Q read from the block's tile just in time.
+  bf16x8 pd_a[4], pd_b[4];  // P half 0, P half 1, dS half 0, dS half 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { pd_a[i] = bf16x8{}; pd_b[i] = bf16x8{}; }
+  // MFMA j of a block's dV, dK: dV half 0, dK half 0, dV half 1, dK half 1, NT d-blocks each
+  auto tr_op = [&](int j, const bf16* Qt, const bf16* Gt, int kb) {
+    const int half = j / (2 * NT), which = (j / NT) % 2, mb = j % NT;
+    const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
+    return tile_tr8<D>(which ? Qt : Gt, tr, tchunk + 4 * mb, thalf);
+  };
+  auto dvdk_mfma = [&](int j, bf16x8 op, const bf16x8 (&pd)[4]) {
+    const int half = j / (2 * NT), which = (j / NT) % 2, mb = j % NT;
+    if (which == 0) dv_acc[mb] = mfma32(op, pd[half], dv_acc[mb]);
+    else dk_acc[mb] = mfma32(op, pd[2 + half], dk_acc[mb]);
+  };
+
+  // ---- one pipeline phase for block bi (rows kb*32.. of the tile in Qc/Gc/Rc/Mc; the
+  // next block's rows kbn*32.. of Qn/Gn).  Region 1: dV, dK MFMAs of block bi-1 with the
+  // P and dS arithmetic of block bi.  Region 2: S, dP MFMAs of block bi+1 with the rest of
+  // that arithmetic, the A-operand reads of block bi+1 and the transposed reads of block bi.
+  // All blocks of the tiles are computed (pairs a wave cannot see get P = 0), so every
+  // phase has the same shape; S, dP of the block after a wave's last are never used.
+  auto phase = [&](int bi, const bf16* Qp, const bf16* Gp, int kbp, const bf16* Qc, const bf16* Gc,
+                   const float* Rc, const bf16* Mc, int kb, const bf16* Qn, const bf16* Gn, int kbn,
+                   f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx, const bf16x8 (&pd_prev)[4],
+                   bf16x8 (&pd)[4]) __attribute__((always_inline)) {
+    const int it = bi >> 1;
     int h, i0;
     tile_rows(it, h, i0);
-    // this wave's keys [jw, jw + 32) against queries [i0, i0 + 32)
-    if (!(jw < kv_end && (!CAUSAL || i0 + kQT - 1 >= jw))) return;
-
-    // S = Q K^T and dP = dO V^T: A = Q / dO rows (row-permuted), B = K / V in registers.
-    f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-    {
-      bf16x8 op[D / 16];
+    const int r0 = i0 + kb * 32;  // first query row of the block
+    // lane holds key myk and queries r0 + 16*hi + v
+    // lse2 and D of the lane's 16 rows, four at a time, read a few slots ahead of use
+    const f32x4* lr = reinterpret_cast<const f32x4*>(Rc + kb * 32 + 16 * hi);
+    const f32x4* dr = reinterpret_cast<const f32x4*>(Rc + kQT + kb * 32 + 16 * hi);
+    f32x4 l4[4], d4[4];
+    l4[0] = lr[0];
+    d4[0] = dr[0];
+    float mbias[16];
+    if (MASK) {
+      if (p.mask_vec) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        op[kk] = tile_row8<D>(Qt, qr, 2 * kk + hi);
+        for (int v = 0; v < 16; ++v) mbias[v] = bf2f(Mc[(kb * 32 + 16 * hi + v) * KT + wave * 32 + l32]) * kLog2e;
+      } else {
+        const bf16* mrow = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) s_acc = mfma32(op[kk], kreg[kk], s_acc);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        op[kk] = tile_row8<D>(Gt, qr, 2 * kk + hi);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) dp_acc = mfma32(op[kk], vreg[kk], dp_acc);
-    }
-
-    // lane holds key myk and queries i0 + 16*hi + v
-    const bool partial = (jw + 32 > kv_end) || (i0 + kQT > q_end) || (CAUSAL && i0 < jw + 31);
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const f32x4* lrow = reinterpret_cast<const f32x4*>(St + 16 * hi + 8 * half);
-      const f32x4* drow = reinterpret_cast<const f32x4*>(St + kQT + 16 * hi + 8 * half);
-      const f32x4 l_a = lrow[0], l_b = lrow[1], d_a = drow[0], d_b = drow[1];
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        const int v = half * 8 + t8;
-        const int qi = i0 + 16 * hi + v;
-        const float l2 = t8 < 4 ? l_a[t8] : l_b[t8 - 4];
-        const float dd = t8 < 4 ? d_a[t8] : d_b[t8 - 4];
-        float bias = -l2;
-        if (MASK) {
-          if (p.mask_vec) {
-            bias += bf2f(Mt[(16 * hi + v) * KT + wave * 32 + l32]) * kLog2e;
-          } else {
-            const bf16* mrow = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh;
-            const bool in = qi < q_end && myk < kv_end;
-            bias += in ? bf2f(mrow[(int64_t)qi * p.m_si + myk]) * kLog2e : 0.f;
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int qi = r0 + 16 * hi + v;
+          const bool in = qi < q_end && myk < kv_end;
+          mbias[v] = in ? bf2f(mrow[(int64_t)qi * p.m_si + myk]) * kLog2e : 0.f;
         }
-        float x = fmaf(s_acc[v], c2, bias);
-        if (partial) {
-          const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi);
-          x = ok ? x : kNegInf;
-        }
-        const float pv = fast_exp2(x);
-        pb[half][t8] = (bf16)pv;
-        dsb[half][t8] = (bf16)(pv * (dp_acc[v] - dd));
       }
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS   (A operands: transposing LDS reads)
+    const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 < jw + 31);
+    if (partial) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7 (two quads)
-      bf16x8 gT[D / 32], qT[D / 32];
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        gT[mb] = tile_tr8<D>(Gt, tr, tchunk + 4 * mb, thalf);
-        qT[mb] = tile_tr8<D>(Qt, tr, tchunk + 4 * mb, thalf);
+      for (int v = 0; v < 16; ++v) {
+        const int qi = r0 + 16 * hi + v;
+        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi);
+        s[v] = ok ? s[v] : kNegInf;
       }
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        dv_acc[mb] = mfma32(gT[mb], pb[half], dv_acc[mb]);
-        dk_acc[mb] = mfma32(qT[mb], dsb[half], dk_acc[mb]);
+    }
+    // P and dS in three stages one slot apart: A (exp2 argument, dP - D), B (exp2),
+    // C (dS and the bf16 operands)
+    float xv[16], dd[16];
+    auto st_a = [&](int e) {
+      const float l2 = l4[e / 4][e % 4];
+      xv[e] = fmaf(s[e], c2, MASK ? mbias[e] - l2 : -l2);
+      dd[e] = dp[e] - d4[e / 4][e % 4];
+    };
+    auto st_b = [&](int e) { xv[e] = fast_exp2(xv[e]); };
+    auto st_c = [&](int e) {
+      dd[e] = xv[e] * dd[e];
+      if (e & 1) {
+        const int half = e / 8, t = e % 8;
+        f32x2 pp = {xv[e - 1], xv[e]}, ss = {dd[e - 1], dd[e]};
+        const bf16x2 p2 = __builtin_convertvector(pp, bf16x2), s2 = __builtin_convertvector(ss, bf16x2);
+        pd[half][t - 1] = p2[0];
+        pd[half][t] = p2[1];
+        pd[2 + half][t - 1] = s2[0];
+        pd[2 + half][t] = s2[1];
       }
+    };
+    // region 1
+    bf16x8 aop[R2], top[R1];
+    top[0] = tr_op(0, Qp, Gp, kbp);
+    top[1] = tr_op(1, Qp, Gp, kbp);
+#pragma unroll
+    for (int j = 0; j < R1; ++j) {
+      if (j + 2 < R1) top[j + 2] = tr_op(j + 2, Qp, Gp, kbp);
+      if ((j * E1) % 4 == 0 && j * E1 / 4 + 1 < 4) {
+        l4[j * E1 / 4 + 1] = lr[j * E1 / 4 + 1];
+        d4[j * E1 / 4 + 1] = dr[j * E1 / 4 + 1];
+      }
+      dvdk_mfma(j, top[j], pd_prev);
+#pragma unroll
+      for (int e = j * E1; e < (j + 1) * E1; ++e) st_a(e);
+#pragma unroll
+      for (int e = (j - 1) * E1; e < j * E1; ++e)
+        if (e >= 0) st_b(e);
+#pragma unroll
+      for (int e = (j - 2) * E1; e < (j - 1) * E1; ++e)
+        if (e >= 0) st_c(e);
+      if (j >= R1 - 2) {  // the first A operands of block bi+1
+        const int i = j - (R1 - 2);
+        aop[i] = tile_row8<D>((i & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (i >> 1) + hi);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // region 2
+    s_nx = f32x16{};
+    dp_nx = f32x16{};
+#pragma unroll
+    for (int i = 0; i < R2; ++i) {
+      if (i + 2 < R2) {
+        const int n = i + 2;
+        aop[n] = tile_row8<D>((n & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (n >> 1) + hi);
+      }
+      if (i & 1) dp_nx = mfma32(aop[i], vreg[i >> 1], dp_nx);
+      else s_nx = mfma32(aop[i], kreg[i >> 1], s_nx);
+      if (i == 0) {
+#pragma unroll
+        for (int e = (R1 - 1) * E1; e < R1 * E1; ++e) st_b(e);
+#pragma unroll
+        for (int e = (R1 - 2) * E1; e < (R1 - 1) * E1; ++e) st_c(e);
+      }
+      if (i == 1) {
+#pragma unroll
+        for (int e = (R1 - 1) * E1; e < R1 * E1; ++e) st_c(e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (total > 0) load_tile(0, Q0, G0, S0, M0);
-  for (int it = 0; it < total; it += 2) {
-    step(it, Q0, G0, S0, M0, Q1, G1, S1, M1);
-    if (it + 1 < total) step(it + 1, Q1, G1, S1, M1, Q0, G0, S0, M0);
+  // One tile step (two blocks); unrolled by three over the LDS buffers (see the forward).
+  f32x16 s_a = f32x16{}, dp_a = f32x16{}, s_b = f32x16{}, dp_b = f32x16{};
+  // Tile t-1 (the previous block's transposed operands) is only overwritten after the
+  // barrier in the middle of step t.
+  auto step = [&](int t, const bf16* Qp, const bf16* Gp, const bf16* Qc, const bf16* Gc,
+                  const float* Rc, const bf16* Mc, const bf16* Qn, const bf16* Gn, bf16* Ql,
+                  bf16* Gl, float* Rl, bf16* Ml) __attribute__((always_inline)) {
+    phase(2 * t, Qp, Gp, 1, Qc, Gc, Rc, Mc, 0, Qc, Gc, 1, s_a, dp_a, s_b, dp_b, pd_b, pd_a);
+    if (t + 1 < total) wait_vmem();
+    __syncthreads();
+    if (t + 2 < total) load_tile(t + 2, Ql, Gl, Rl, Ml);
+    phase(2 * t + 1, Qc, Gc, 0, Qc, Gc, Rc, Mc, 1, Qn, Gn, 0, s_b, dp_b, s_a, dp_a, pd_a, pd_b);
+  };
+
+  if (total > 0) {
+    // tile 0 landed (tile 1 may be in flight)
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < R2; ++i) {
+      const bf16x8 op = tile_row8<D>((i & 1) ? G0 : Q0, qr, 2 * (i >> 1) + hi);
+      if (i & 1) dp_a = mfma32(op, vreg[i >> 1], dp_a);
+      else s_a = mfma32(op, kreg[i >> 1], s_a);
+    }
+  }
+  for (int t = 0; t < total; t += 3) {
+    step(t, Q2, G2, Q0, G0, R0, M0, Q1, G1, Q2, G2, R2s, M2);
+    if (t + 1 < total) step(t + 1, Q0, G0, Q1, G1, R1s, M1, Q2, G2, Q0, G0, R0, M0);
+    if (t + 2 < total) step(t + 2, Q1, G1, Q2, G2, R2s, M2, Q0, G0, Q1, G1, R1s, M1);
+  }
+  // the last block's dV, dK (second block of tile total-1, buffer (total-1) % 3)
+  if (total > 0) {
+    const int lb = (total - 1) % 3;
+    const bf16* Ql = lb == 0 ? Q0 : (lb == 1 ? Q1 : Q2);
+    const bf16* Gl = lb == 0 ? G0 : (lb == 1 ? G1 : G2);
+#pragma unroll
+    for (int j = 0; j < R1; ++j) dvdk_mfma(j, tr_op(j, Ql, Gl, 1), pd_b);
   }
 
   // Epilogue: lane holds key myk, d = mb*32 + (v/4)*8 + 4*hi + v%4.
@@ -263,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
     bf16* dkrow = reinterpret_cast<bf16*>(a.dk) + b * p.k_sb + g * p.k_sh + (int64_t)myk * p.k_sl;
     bf16* dvrow = reinterpret_cast<bf16*>(a.dv) + b * p.v_sb + g * p.v_sh + (int64_t)myk * p.v_sl;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < NT; ++mb) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         bf16x4 wk, wv;

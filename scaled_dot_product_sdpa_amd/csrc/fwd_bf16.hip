@@ -126,8 +126,8 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   kcopy.init(p.k_sl, wave, lane);
   vcopy.init(p.v_sl, wave, lane);
   auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    kcopy.copy(rows_rsrc<D>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
-    vcopy.copy(rows_rsrc<D>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
+    kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
+    vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
   };
   // ---- Q operand (B of S^T = K Q^T): lane holds query row, 8 consecutive d per k-step.
   const int qrow = wq_lo + l32;

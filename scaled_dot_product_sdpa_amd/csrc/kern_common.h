@@ -161,17 +161,35 @@ typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
 struct buf_rsrc_t { uint32_t w[4]; };
 #endif
 
-// Raw buffer over rows r0 .. stop-1 of a row-major bf16 matrix (row_stride elements, rows
-// of D elements); reads at or past row `stop` return zeros.
-template <int D>
-__device__ __forceinline__ buf_rsrc_t rows_rsrc(const bf16* base, int64_t row_stride, int r0, int stop) {
+// Raw buffer of `bytes` bytes at `base` (stride 0, 32-bit dword format): loads past the
+// end return zeros.
+__device__ __forceinline__ buf_rsrc_t raw_rsrc(const void* base, int64_t bytes) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int64_t bytes = stop > r0 ? (int64_t)(stop - 1 - r0) * row_stride * 2 + D * 2 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)r0 * row_stride),
-                                           (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 #else
   return buf_rsrc_t{};
 #endif
+}
+
+// SIZE bytes per lane from src + voff into LDS at lds + SIZE * lane (lds wave-uniform).
+template <int SIZE>
+__device__ __forceinline__ void buffer_to_lds(buf_rsrc_t src, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
+  auto* l = (__attribute__((address_space(3))) void*)lds;
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 4, voff, 0, 0, 0);
+#endif
+}
+
+// Raw buffer over rows r0 .. min(stop, r0 + ROWS) - 1 of a row-major bf16 matrix
+// (row_stride elements, rows of D elements); reads past those rows return zeros.  The
+// host keeps ROWS * row_stride * 2 bytes below 2^31.
+template <int D, int ROWS>
+__device__ __forceinline__ buf_rsrc_t rows_rsrc(const bf16* base, int64_t row_stride, int r0, int stop) {
+  const int n = min(stop - r0, ROWS);
+  const int64_t bytes = n > 0 ? (int64_t)(n - 1) * row_stride * 2 + D * 2 : 0;
+  return raw_rsrc(base + (int64_t)r0 * row_stride, bytes);
 }
 
 // Per-lane byte offsets of a ROWS x D tile copy by NW waves: instruction i of wave w moves
@@ -194,14 +212,9 @@ struct TileCopy {
     }
   }
   __device__ __forceinline__ void copy(buf_rsrc_t src, bf16* lds_tile, int wave) const {
-#if defined(__HIP_DEVICE_COMPILE__)
     wave = __builtin_amdgcn_readfirstlane(wave);  // the LDS destination is wave-uniform
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          src, (__attribute__((address_space(3))) void*)(lds_tile + (wave * PER_WAVE + i) * 512), 16,
-          voff[i], 0, 0, 0);
-#endif
+    for (int i = 0; i < PER_WAVE; ++i) buffer_to_lds<16>(src, lds_tile + (wave * PER_WAVE + i) * 512, voff[i]);
   }
 };
 
