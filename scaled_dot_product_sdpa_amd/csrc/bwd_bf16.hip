@@ -23,9 +23,12 @@
 //            blocks are software-pipelined: the dV, dK MFMAs of block b-1 run with the P, dS
 //            arithmetic of block b, and the S, dP MFMAs of block b+1 with the rest of it.
 //  3. dq:    query-stationary (the forward's decomposition, 8 waves of 32 rows).  Per
-//            32-key block of a double-buffered 64-key K/V tile:
+//            32-key block of a 64-key K/V tile (three LDS buffers, buffer-load copies):
 //              S^T = K Q^T,  P^T,  dP^T = V dO^T,  dS^T = P^T o (dP^T - D),
 //              dQ^T += K^T dS^T   (K^T via transposing LDS reads).
+//            At D = 64 the blocks are software-pipelined inside each wave like the other
+//            kernels (dQ one block late); at D = 128 that form needs more than the 256
+//            registers two waves per SIMD allow, so each block runs start to finish.
 // Rows and keys past the lengths and pairs above the causal diagonal carry P = 0; blocks
 // that are blocked as a whole are skipped.  LDS tiles are unpadded with XOR-swizzled
 // 16-byte chunks (kern_common.h).
@@ -395,7 +398,294 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kBN = 64;
 
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = NW * 32;
+  constexpr int TILE = kBN * D;
+  constexpr int NS = D / 16;   // MFMAs of one S^T (or dP^T) block
+  constexpr int NT = D / 32;   // MFMAs of one half of a dQ^T block
+  constexpr int R1 = 2 * NT;   // slots of region 1 (dQ MFMAs)
+  constexpr int R2 = 2 * NS;   // slots of region 2 (S^T, dP^T MFMAs)
+  constexpr int E1 = 16 / R1;  // scores per lane per region-1 slot
+  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int bh_count = p.B * p.Hq;
+  const int rank = blockIdx.x / bh_count;
+  const int bh = blockIdx.x % bh_count;
+  const int b = bh / p.Hq;
+  const int h = bh % p.Hq;
+  const int g = h / p.G;
+  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
+  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  // Rows: as in the forward (heavy tiles first, or paired half-tiles for small grids).
+  int wq_lo, row_lo, row_hi;
+  if (CAUSAL && !p.pair_rows) {
+    const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
+    wq_lo = qt * BM + wave * 32;
+    row_lo = qt * BM;
+    row_hi = row_lo + BM;
+  } else if (CAUSAL) {
+    constexpr int HB = BM / 2;
+    const int n_half = (p.Lq + HB - 1) / HB;
+    const int heavy = n_half - 1 - rank;
+    const int mine = wave < NW / 2 ? rank : heavy;
+    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32;
+    row_lo = rank * HB;
+    row_hi = (heavy + 1) * HB;
+  } else {
+    wq_lo = rank * BM + wave * 32;
+    row_lo = rank * BM;
+    row_hi = row_lo + BM;
+  }
+  const int wq_hi = min(wq_lo + 32, q_end) - 1;
+
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
+  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + b * p.o_sb + h * p.o_sh;
+  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
+  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+  const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
+
+  int kv_stop = kv_end;
+  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
+  if (row_lo >= q_end) kv_stop = 0;
+  const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
+  int vis_stop = wq_lo < q_end ? kv_stop : 0;
+  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1);
+  const int nvis = (vis_stop + 31) / 32;  // 32-key blocks this wave works on (a prefix)
+
+  const int qi = wq_lo + l32;  // this lane's query (N index)
+  const bool qok = qi < q_end;
+  bf16x8 qreg[NS], doreg[NS];
+#pragma unroll
+  for (int kk = 0; kk < NS; ++kk) {
+    qreg[kk] = __builtin_bit_cast(bf16x8, qok ? ld16(qb + (int64_t)qi * p.q_sl + kk * 16 + 8 * hi) : zero16());
+    doreg[kk] = __builtin_bit_cast(bf16x8, qok ? ld16(dob + (int64_t)qi * p.o_sl + kk * 16 + 8 * hi) : zero16());
+  }
+  const int64_t rowid = ((int64_t)b * p.Hq + h) * p.Lq + qi;
+  const float nl2 = qok ? -a.lse2[rowid] : kNegInf;  // exp2 offset of this lane's row
+  const float dsum = qok ? a.dsum[rowid] : 0.f;
+
+  TileCopy<kBN, D, NW> kcopy, vcopy;
+  kcopy.init(p.k_sl, wave, lane);
+  vcopy.init(p.v_sl, wave, lane);
+  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
+    kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
+    vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
+  };
+  if (n_tiles > 0) load_tile(0, K0, V0);
+  if (n_tiles > 1) load_tile(kBN, K1, V1);
+
+  f32x16 dq_acc[NT];
+#pragma unroll
+  for (int mb = 0; mb < NT; ++mb) dq_acc[mb] = f32x16{};
+
+  const float c2 = p.scale_log2;
+  const int krow_l = perm_row(l32);
+  const int blk = lane >> 4;
+  const int arow = (lane & 15) >> 2;
+  const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
+  const int thalf = 4 * (lane & 1);
+
+  // mask values of block bi for this lane (keys 32*bi + 16*hi + 0..15), one block ahead
+  auto mask_vec_ok = [&](int bi) { return p.mask_vec && qok && 32 * bi + 16 * hi + 16 <= p.Lk; };
+  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
+    if (MASK && bi < nvis && mask_vec_ok(bi)) {
+      const bf16* mp = mb_ + (int64_t)qi * p.m_si + 32 * bi + 16 * hi;
+      m[0] = ld16(mp);
+      m[1] = ld16(mp + 8);
+    } else {
+      m[0] = zero16();
+      m[1] = zero16();
+    }
+  };
+
+  // dQ^T of a block runs one block late: B operand bf16 dS^T (zero before the first
+  // block), A operand K^T read from the block's tile just in time.
+  bf16x8 ds_a[2], ds_b[2];
+  ds_a[0] = ds_a[1] = ds_b[0] = ds_b[1] = bf16x8{};
+  auto kt_op = [&](int j, const bf16* Kt, int kb) {
+    const int half = j / NT, mb = j % NT;
+    const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
+    return tile_tr8<D>(Kt, tr, tchunk + 4 * mb, thalf);
+  };
+  auto dq_mfma = [&](int j, bf16x8 op, const bf16x8 (&ds)[2]) {
+    const int half = j / NT, mb = j % NT;
+    dq_acc[mb] = mfma32(op, ds[half], dq_acc[mb]);
+  };
+
+  u32x4 mk[2];
+  load_mask(0, mk);
+  // ---- one pipeline phase for block bi (keys kb*32.. of Kc/Vc; the previous block's keys
+  // kbp*32.. of Kp; the next block's keys kbn*32.. of Kn/Vn).  Region 1: dQ MFMAs of block
+  // bi-1 with the P, dS arithmetic of block bi.  Region 2: S^T, dP^T MFMAs of block bi+1
+  // with the rest of it.  The S^T, dP^T of the block after a wave's last are never used.
+  auto phase = [&](int bi, const bf16* Kp, int kbp, const bf16* Kn, const bf16* Vn, int kbn,
+                   f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx, const bf16x8 (&ds_prev)[2],
+                   bf16x8 (&ds)[2]) __attribute__((always_inline)) {
+    if (bi >= nvis) {
+      // the wave's last block: its dQ, while its K tile is still resident
+      if (bi == nvis && bi > 0) {
+#pragma unroll
+        for (int j = 0; j < R1; ++j) dq_mfma(j, kt_op(j, Kp, kbp), ds_prev);
+      }
+      return;
+    }
+    const int key0 = 32 * bi + 16 * hi;  // lane holds query qi and keys key0 + v
+    u32x4 mk_next[2];
+    if (MASK) load_mask(bi + 1, mk_next);
+    float mbias[16];
+    if (MASK) {
+      if (mask_vec_ok(bi)) {
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, mk[0]), b1 = __builtin_bit_cast(bf16x8, mk[1]);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) { mbias[v] = bf2f(b0[v]) * kLog2e; mbias[v + 8] = bf2f(b1[v]) * kLog2e; }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
+      }
+    }
+    const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo) || (wq_lo + 32 > q_end);
+    if (partial) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + v;
+        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi);
+        s[v] = ok ? s[v] : kNegInf;
+      }
+    }
+    float xv[16], dd[16];
+    auto st_a = [&](int e) {
+      xv[e] = fmaf(s[e], c2, MASK ? mbias[e] + nl2 : nl2);
+      dd[e] = dp[e] - dsum;
+    };
+    auto st_b = [&](int e) { xv[e] = fast_exp2(xv[e]); };
+    auto st_c = [&](int e) {
+      dd[e] = xv[e] * dd[e];
+      if (e & 1) {
+        f32x2 ss = {dd[e - 1], dd[e]};
+        const bf16x2 s2 = __builtin_convertvector(ss, bf16x2);
+        ds[e / 8][e % 8 - 1] = s2[0];
+        ds[e / 8][e % 8] = s2[1];
+      }
+    };
+    // region 1
+    bf16x8 aop[R2], top[R1];
+    top[0] = kt_op(0, Kp, kbp);
+#pragma unroll
+    for (int j = 0; j < R1; ++j) {
+      if (j + 1 < R1) top[j + 1] = kt_op(j + 1, Kp, kbp);
+      dq_mfma(j, top[j], ds_prev);
+#pragma unroll
+      for (int e = j * E1; e < (j + 1) * E1; ++e) st_a(e);
+#pragma unroll
+      for (int e = (j - 1) * E1; e < j * E1; ++e)
+        if (e >= 0) st_b(e);
+#pragma unroll
+      for (int e = (j - 2) * E1; e < (j - 1) * E1; ++e)
+        if (e >= 0) st_c(e);
+      if (j == R1 - 1) aop[0] = tile_row8<D>(Kn, kbn * 32 + krow_l, hi);  // first A operand of bi+1
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // region 2
+    s_nx = f32x16{};
+    dp_nx = f32x16{};
+#pragma unroll
+    for (int i = 0; i < R2; ++i) {
+      if (i + 1 < R2) {
+        const int n = i + 1;
+        aop[n] = tile_row8<D>((n & 1) ? Vn : Kn, kbn * 32 + krow_l, 2 * (n >> 1) + hi);
+      }
+      if (i & 1) dp_nx = mfma32(aop[i], doreg[i >> 1], dp_nx);
+      else s_nx = mfma32(aop[i], qreg[i >> 1], s_nx);
+      if (i == 0) {
+#pragma unroll
+        for (int e = (R1 - 1) * E1; e < R1 * E1; ++e) st_b(e);
+#pragma unroll
+        for (int e = (R1 - 2) * E1; e < (R1 - 1) * E1; ++e) st_c(e);
+      }
+      if (i == 1) {
+#pragma unroll
+        for (int e = (R1 - 1) * E1; e < R1 * E1; ++e) st_c(e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MASK) { mk[0] = mk_next[0]; mk[1] = mk_next[1]; }
+  };
+
+  // One tile step (two blocks); unrolled by three over the LDS buffers (see the forward).
+  f32x16 s_a = f32x16{}, dp_a = f32x16{}, s_b = f32x16{}, dp_b = f32x16{};
+  auto step = [&](int t, const bf16* Kp, const bf16* Kc, const bf16* Vc, const bf16* Kn,
+                  const bf16* Vn, bf16* Kl, bf16* Vl) __attribute__((always_inline)) {
+    phase(2 * t, Kp, 1, Kc, Vc, 1, s_a, dp_a, s_b, dp_b, ds_b, ds_a);
+    // tile t+1 has landed for every wave, and no wave still reads tile t-1
+    if (t + 1 < n_tiles) wait_vmem();
+    __syncthreads();
+    if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
+    phase(2 * t + 1, Kc, 0, Kn, Vn, 0, s_b, dp_b, s_a, dp_a, ds_a, ds_b);
+  };
+
+  if (n_tiles > 0) {
+    // tile 0 (and Q, dO) landed; tile 1 may still be in flight
+    if (n_tiles > 1) wait_vmem_le<2 * TileCopy<kBN, D, NW>::PER_WAVE>();
+    else wait_vmem();
+    __syncthreads();
+    if (nvis > 0) {
+#pragma unroll
+      for (int i = 0; i < R2; ++i) {
+        const bf16x8 op = tile_row8<D>((i & 1) ? V0 : K0, krow_l, 2 * (i >> 1) + hi);
+        if (i & 1) dp_a = mfma32(op, doreg[i >> 1], dp_a);
+        else s_a = mfma32(op, qreg[i >> 1], s_a);
+      }
+    }
+  }
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, K2, K0, V0, K1, V1, K2, V2);
+    if (t + 1 < n_tiles) step(t + 1, K0, K1, V1, K2, V2, K0, V0);
+    if (t + 2 < n_tiles) step(t + 2, K1, K2, V2, K0, V0, K1, V1);
+  }
+  // a wave whose last block is the workgroup's last: that block's dQ (second block of
+  // tile n_tiles-1, buffer (n_tiles-1) % 3, never overwritten)
+  if (nvis > 0 && nvis == 2 * n_tiles) {
+    const int lt = (n_tiles - 1) % 3;
+    const bf16* Kl = lt == 0 ? K0 : (lt == 1 ? K1 : K2);
+#pragma unroll
+    for (int j = 0; j < R1; ++j) dq_mfma(j, kt_op(j, Kl, 1), ds_b);
+  }
+
+  if (qi < p.Lq) {
+    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + b * p.q_sb + h * p.q_sh + (int64_t)qi * p.q_sl;
+#pragma unroll
+    for (int mb = 0; mb < NT; ++mb) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(qok ? dq_acc[mb][v4 * 4 + e] * p.scale : 0.f);
+        *reinterpret_cast<bf16x4*>(dqrow + mb * 32 + v4 * 8 + hi * 4) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 3b. dQ, block-sequential form (for head dims where the pipelined form's registers do
+//     not fit two waves per SIMD): each 32-key block's S^T, dP^T, dS^T and dQ^T in turn.
+// ---------------------------------------------------------------------------------------
+
+template <int D, int NW, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_seq_kernel(BwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;
   constexpr int TILE = kBN * D;
@@ -468,9 +758,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) dq_acc[mb] = f32x16{};
 
+  TileCopy<kBN, D, NW> kcopy, vcopy;
+  kcopy.init(p.k_sl, wave, lane);
+  vcopy.init(p.v_sl, wave, lane);
   auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    tile_to_lds_swz<kBN, D, NW>(kb_, p.k_sl, j0, kv_stop, Kd, wave, lane);
-    tile_to_lds_swz<kBN, D, NW>(vb_, p.v_sl, j0, kv_stop, Vd, wave, lane);
+    kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
+    vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
   };
   const float c2 = p.scale_log2;
   const int krow_l = perm_row(l32);
@@ -575,8 +868,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
 // Waves per workgroup of the two main kernels.
 template <int D> struct BwdShape;
-template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; };
-template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; };
+// PIPE_DQ: the software-pipelined dQ kernel fits two waves per SIMD (D = 64); at D = 128
+// its registers do not, and the block-sequential form is faster.
+template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; static constexpr bool PIPE_DQ = true; };
+template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; static constexpr bool PIPE_DQ = false; };
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
@@ -594,8 +889,12 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
   const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
   if ((stages & kBwdDq) && n_wg > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_wg * a.p.B * a.p.Hq),
-                       dim3(64 * QNW), 0, s, args);
+    if constexpr (BwdShape<D>::PIPE_DQ)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_wg * a.p.B * a.p.Hq),
+                         dim3(64 * QNW), 0, s, args);
+    else
+      hipLaunchKernelGGL((bwd_dq_seq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_wg * a.p.B * a.p.Hq),
+                         dim3(64 * QNW), 0, s, args);
   }
   return hipGetLastError();
 }
