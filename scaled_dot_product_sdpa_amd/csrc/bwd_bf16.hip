@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // are masked by the predicates
       const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq + i0;
       const float* src = (uw ? a.dsum : a.lse2) + rb;
-      buffer_to_lds<4>(raw_rsrc(src, (int64_t)max(min(p.Lq - i0, kQT), 0) * 4), Rd + uw * kQT, lane * 4);
+      buffer_to_lds<4>(raw_rsrc(src, (int64_t)max(min(p.Lq - i0, kQT), 0) * 4), Rd, uw * kQT * 4, lane * 4);
     }
     if (MASK && p.mask_vec) {
       // keys past Lk read the next row (or zeros past the end); those pairs are masked
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const buf_rsrc_t rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
       const int mw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-      for (int i = 0; i < MPW; ++i) buffer_to_lds<16>(rs, Md + (mw * MPW + i) * 512, mvoff[i]);
+      for (int i = 0; i < MPW; ++i) buffer_to_lds<16>(rs, Md, (mw * MPW + i) * 1024, mvoff[i]);
     }
   };
 

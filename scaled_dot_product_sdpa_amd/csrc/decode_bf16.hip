@@ -9,9 +9,9 @@
 //    head map);
 //  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
 //    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> LDS with
-//    global_load_lds (no staging registers, so several such workgroups share a CU and
-//    many bytes are in flight), double-buffered; splits past the sequence length exit at
-//    once; each split writes a partial (O_c normalised, lse_c);
+//    buffer loads (no staging registers and no address arithmetic per copy) through three
+//    LDS buffers, two tiles in flight while one is computed; splits past the sequence
+//    length exit at once; each split writes a partial (O_c normalised, lse_c);
 //  - a combine kernel merges the partials exactly:  LSE = ln sum_c exp(lse_c),
 //    O = sum_c exp(lse_c - LSE) O_c  (the log-sum-exp merge of split-KV partial results
 //    that cuDNN "Attention", SDPA FP16/BF16 Forward, Python API describes for its stats).
@@ -24,14 +24,16 @@ namespace {
 constexpr int kDT = 32;  // keys per tile
 
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
-void decode_split_kernel(DecodeArgs a) {
-  constexpr int CPR = D / 8;
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kDT * D;
+  // buffer loads per K+V tile (this one-wave workgroup copies whole tiles)
+  constexpr int LOADS_PER_TILE = 2 * TileCopy<kDT, D, 1>::PER_WAVE;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
   const Problem& p = a.p;
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -53,16 +55,21 @@ void decode_split_kernel(DecodeArgs a) {
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
   const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
 
-  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    tile_to_lds_swz<kDT, D, 1>(kbase, p.k_sl, j0, k1, Kd, 0, lane);
-    tile_to_lds_swz<kDT, D, 1>(vbase, p.v_sl, j0, k1, Vd, 0, lane);
-  };
-  load_tile(k0, K0, V0);
-
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 16 + 8 * hi) : zero16());
+
+  // K/V tiles HBM -> LDS, two tiles ahead (rows past the split arrive as zeros)
+  TileCopy<kDT, D, 1> kcopy, vcopy;
+  kcopy.init(p.k_sl, 0, lane);
+  vcopy.init(p.v_sl, 0, lane);
+  auto load_tile = [&](int t, bf16* Kd, bf16* Vd) {
+    kcopy.copy(rows_rsrc<D, kDT>(kbase, p.k_sl, k0 + t * kDT, k1), Kd, 0);
+    vcopy.copy(rows_rsrc<D, kDT>(vbase, p.v_sl, k0 + t * kDT, k1), Vd, 0);
+  };
+  load_tile(0, K0, V0);
+  if (n_tiles > 1) load_tile(1, K1, V1);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -77,21 +84,31 @@ void decode_split_kernel(DecodeArgs a) {
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
 
-  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
+  // One tile; unrolled by three over the LDS buffers so the reads of tile t and the copies
+  // into the other buffers are distinct LDS objects at compile time.  The buffer refilled
+  // with tile t+2 held tile t-1, whose reads all completed before its MFMAs.
+  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kl, bf16* Vl)
                   __attribute__((always_inline)) {
     const int j0 = k0 + t * kDT;
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(j0 + kDT, Kn, Vn);
+    if (t + 1 < n_tiles) wait_vmem_le<LOADS_PER_TILE>();  // tile t landed, t+1 in flight
+    else wait_vmem();
+    if (t + 2 < n_tiles) load_tile(t + 2, Kl, Vl);
 
     f32x16 sacc = f32x16{};
     {
       bf16x8 kop[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
+      for (int kk = 0; kk < D / 16; ++kk) kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(kop[kk], qreg[kk], sacc);
+    }
+    // V^T operands (transposing reads), issued before the softmax arithmetic
+    bf16x8 vop[2][D / 32];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
     }
     const bool partial = j0 + kDT > k1;
     float s[16];
@@ -130,24 +147,16 @@ void decode_split_kernel(DecodeArgs a) {
     frow = frow * corr + fsum;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
-    // V^T operands (transposing reads)
-    bf16x8 vop[2][D / 32];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
-    }
-
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(vop[half][mb], pop[half], oacc[mb]);
   };
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, K0, V0, K1, V1);
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, K0, V0, K2, V2);
     if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
+    if (t + 2 < n_tiles) step(t + 2, K2, V2, K1, V1);
   }
 
   const float lt = xhalf_sum(lrow);

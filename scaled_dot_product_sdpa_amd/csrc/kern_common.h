@@ -171,12 +171,14 @@ __device__ __forceinline__ buf_rsrc_t raw_rsrc(const void* base, int64_t bytes) 
 #endif
 }
 
-// SIZE bytes per lane from src + voff into LDS at lds + SIZE * lane (lds wave-uniform).
+// SIZE bytes per lane from src + voff into LDS at lds + byte_off + SIZE * lane (wave-uniform
+// destination).  The offset is applied after the cast to the LDS address space, so that a
+// constant destination stays a plain LDS address.
 template <int SIZE>
-__device__ __forceinline__ void buffer_to_lds(buf_rsrc_t src, void* lds, uint32_t voff) {
+__device__ __forceinline__ void buffer_to_lds(buf_rsrc_t src, void* lds, uint32_t byte_off, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
-  auto* l = (__attribute__((address_space(3))) void*)lds;
+  auto* l = (__attribute__((address_space(3))) char*)lds + byte_off;
   if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 16, voff, 0, 0, 0);
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 4, voff, 0, 0, 0);
 #endif
@@ -212,9 +214,10 @@ struct TileCopy {
     }
   }
   __device__ __forceinline__ void copy(buf_rsrc_t src, bf16* lds_tile, int wave) const {
-    wave = __builtin_amdgcn_readfirstlane(wave);  // the LDS destination is wave-uniform
+    if constexpr (NW > 1) wave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform LDS destination
+    else wave = 0;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) buffer_to_lds<16>(src, lds_tile + (wave * PER_WAVE + i) * 512, voff[i]);
+    for (int i = 0; i < PER_WAVE; ++i) buffer_to_lds<16>(src, lds_tile, (wave * PER_WAVE + i) * 1024, voff[i]);
   }
 };
 
