@@ -9,9 +9,10 @@
 //    head map);
 //  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
 //    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> LDS with
-//    buffer loads (no staging registers and no address arithmetic per copy) through three
-//    LDS buffers, two tiles in flight while one is computed; splits past the sequence
-//    length exit at once; each split writes a partial (O_c normalised, lse_c);
+//    buffer loads (no staging registers and no address arithmetic per copy), double
+//    buffered; the small LDS and register footprint keeps two such waves per SIMD; splits
+//    past the sequence length exit at once; each split writes a partial (O_c normalised,
+//    lse_c);
 //  - a combine kernel merges the partials exactly:  LSE = ln sum_c exp(lse_c),
 //    O = sum_c exp(lse_c - LSE) O_c  (the log-sum-exp merge of split-KV partial results
 //    that cuDNN "Attention", SDPA FP16/BF16 Forward, Python API describes for its stats).
@@ -24,16 +25,12 @@ namespace {
 constexpr int kDT = 32;  // keys per tile
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kDT * D;
-  // buffer loads per K+V tile (this one-wave workgroup copies whole tiles)
-  constexpr int LOADS_PER_TILE = 2 * TileCopy<kDT, D, 1>::PER_WAVE;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
   const Problem& p = a.p;
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -60,7 +57,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (int kk = 0; kk < D / 16; ++kk)
     qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 16 + 8 * hi) : zero16());
 
-  // K/V tiles HBM -> LDS, two tiles ahead (rows past the split arrive as zeros)
+  // K/V tiles HBM -> LDS, one tile ahead (rows past the split arrive as zeros)
   TileCopy<kDT, D, 1> kcopy, vcopy;
   kcopy.init(p.k_sl, 0, lane);
   vcopy.init(p.v_sl, 0, lane);
@@ -69,12 +66,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     vcopy.copy(rows_rsrc<D, kDT>(vbase, p.v_sl, k0 + t * kDT, k1), Vd, 0);
   };
   load_tile(0, K0, V0);
-  if (n_tiles > 1) load_tile(1, K1, V1);
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
-  float mrow = kNegInf, lrow = 0.f, frow = 0.f;  // max, rounded-weight sum, fp32-weight sum
+  // reference max (log2 units; moved only when a tile's max exceeds it by more than 2^8, so
+  // weights stay <= 256), rounded-weight sum, fp32-weight sum
+  float mref = kNegInf, lrow = 0.f, frow = 0.f;
 
   const float c2 = p.scale_log2;
   const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
@@ -84,15 +82,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
 
-  // One tile; unrolled by three over the LDS buffers so the reads of tile t and the copies
-  // into the other buffers are distinct LDS objects at compile time.  The buffer refilled
-  // with tile t+2 held tile t-1, whose reads all completed before its MFMAs.
+  // One tile; unrolled by two over the LDS buffers so the reads of tile t and the copies
+  // into the other buffer are distinct LDS objects at compile time.  The buffer refilled
+  // with tile t+1 held tile t-1, whose reads all completed before its MFMAs.  The copy is
+  // unconditional: past the split every row is out of the buffer's range and the copy
+  // writes zeros without touching memory.
   auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kl, bf16* Vl)
                   __attribute__((always_inline)) {
     const int j0 = k0 + t * kDT;
-    if (t + 1 < n_tiles) wait_vmem_le<LOADS_PER_TILE>();  // tile t landed, t+1 in flight
-    else wait_vmem();
-    if (t + 2 < n_tiles) load_tile(t + 2, Kl, Vl);
+    wait_vmem();  // tile t landed
+    load_tile(t + 1, Kl, Vl);
 
     f32x16 sacc = f32x16{};
     {
@@ -101,14 +100,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       for (int kk = 0; kk < D / 16; ++kk) kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(kop[kk], qreg[kk], sacc);
-    }
-    // V^T operands (transposing reads), issued before the softmax arithmetic
-    bf16x8 vop[2][D / 32];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
     }
     const bool partial = j0 + kDT > k1;
     float s[16];
@@ -121,12 +112,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       mx = fmaxf(mx, x);
     }
     mx = xhalf_max(mx) * c2;
-    const float m_new = fmaxf(mrow, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float corr = fast_exp2(mrow - m_use);
-    mrow = m_new;
+    const bool need = mx > mref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? mx : mref;
+      const float corr = need ? fast_exp2(mref - mnew) : 1.f;
+      mref = mnew;
+      lrow *= corr;
+      frow *= corr;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+    }
+    const float m_use = (mref == kNegInf) ? 0.f : mref;
     bf16x8 pop[2];
-    float psum = 0.f, fsum = 0.f;
+    float psum = lrow, fsum = frow;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -143,21 +141,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         pop[half][2 * t2 + 1] = e2[1];
       }
     }
-    lrow = lrow * corr + psum;
-    frow = frow * corr + fsum;
+    lrow = psum;
+    frow = fsum;
+    // V^T operands (transposing reads)
+    bf16x8 vop[2][D / 32];
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+    for (int half = 0; half < 2; ++half) {
+      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(vop[half][mb], pop[half], oacc[mb]);
   };
 
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(t, K0, V0, K2, V2);
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, K0, V0, K1, V1);
     if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
-    if (t + 2 < n_tiles) step(t + 2, K2, V2, K1, V1);
   }
+  wait_vmem();  // the last (empty) copy has landed before the workgroup's LDS is released
 
   const float lt = xhalf_sum(lrow);
   const float ft = xhalf_sum(frow);
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(po + mb * 32 + v4 * 8 + hi * 4) = w;
       }
     }
-    if (hi == 0) a.part_lse[prow] = lt > 0.f ? (mrow * kLn2 + logf(ft)) : kNegInf;
+    if (hi == 0) a.part_lse[prow] = lt > 0.f ? (mref * kLn2 + logf(ft)) : kNegInf;
   }
 }
 
@@ -229,7 +233,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 void decode_split_plan(int B, int Hkv, int Lk, int* split_keys, int* n_split) {
   // Enough splits that the (batch, KV head) pairs times splits fill the chip several
   // times over, without partial-result traffic becoming noticeable.
-  int sk = 256;
+  int sk = 512;
   const int64_t pairs = (int64_t)B * Hkv;
   while (sk > kDT && pairs * ((Lk + sk - 1) / sk) < 2048) sk /= 2;
   *split_keys = sk;

@@ -184,6 +184,15 @@ __device__ __forceinline__ void buffer_to_lds(buf_rsrc_t src, void* lds, uint32_
 #endif
 }
 
+// 16 bytes from src + voff into registers (zeros past the end of the buffer).
+__device__ __forceinline__ u32x4 buffer_ld16(buf_rsrc_t src, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, 0, 0));
+#else
+  return u32x4{0u, 0u, 0u, 0u};
+#endif
+}
+
 // Raw buffer over rows r0 .. min(stop, r0 + ROWS) - 1 of a row-major bf16 matrix
 // (row_stride elements, rows of D elements); reads past those rows return zeros.  The
 // host keeps ROWS * row_stride * 2 bytes below 2^31.
