@@ -197,6 +197,80 @@ def traffic_for(stage, launches_per_step=1):
     return ent.get("bytes_per_launch")
 
 
+# ---- profile helpers (no GPU): turn rocprofv3 output into the committed summaries ----
+
+COPY_KERNELS = ("__amd_rocclr_copyBuffer", "copy_kernel")
+CALIBRATION_BYTES = 1 << 30  # the --calibrate device copy: 1 GiB read and 1 GiB written
+
+
+def _pmc_rows(directory, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, command):
+    """profiles/traffic.json: HBM bytes per launch of each headline kernel, from a
+    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by what the same
+    counter reads for the --calibrate copy of known size."""
+    out = {"note": "HBM bytes per launch = counter KiB * 1024 * scale, scale = known bytes of "
+                   "the calibration copy / its counter bytes", "command": command}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        cal = [v for n, v in rows if any(c in n for c in COPY_KERNELS)]
+        if not cal:
+            raise SystemExit(f"no calibration copy kernel in {d}")
+        scale = CALIBRATION_BYTES / (max(cal) * 1024.0)
+        out[counter.lower() + "_scale"] = round(scale, 4)
+        for stage, frag in KERNEL_NAMES.items():
+            vals = [v for n, v in rows if frag in n and "sdpa::" in n]
+            if vals:
+                per.setdefault(stage, {})[counter] = (sum(vals) / len(vals), len(vals), scale)
+    for stage, c in per.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        (fk, fn, fs), (wk, wn, ws) = c["FETCH_SIZE"], c["WRITE_SIZE"]
+        out[stage] = {"kernel": KERNEL_NAMES[stage], "source_hash": source_hash(stage),
+                      "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                      "dispatches": min(fn, wn),
+                      "bytes_per_launch": int(fk * 1024 * fs + wk * 1024 * ws)}
+    path = ROOT / "profiles" / "traffic.json"
+    path.write_text(json.dumps(out, indent=1) + "\n")
+    print(path.read_text())
+
+
+def summarize_trace(stats_csv, out_md, command):
+    """Short markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    rows = []
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6))
+    lines = ["# rocprofv3 kernel trace summary", "",
+             "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | total ms |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for n, c, a, mn, mx, tot in sorted(rows, key=lambda r: -r[5]):
+        if "sdpa::" not in n:
+            continue
+        n = n.replace("void sdpa::(anonymous namespace)::", "")
+        for t in ("(sdpa::BwdArgs)", "(sdpa::FwdArgs)", "(sdpa::DecodeArgs)"):
+            n = n.replace(t, "")
+        lines.append(f"| `{n}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {tot:.3f} |")
+    Path(out_md).write_text("\n".join(lines) + "\n")
+    print(Path(out_md).read_text())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,7 +279,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, help="comma list of extra workloads to run")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run one 1 GiB device copy (the reference for HBM counters)")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 kernel_stats.csv (no GPU)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
@@ -222,6 +308,13 @@ def main():
     load_library()
     timer = Timer(torch)
     w = WORKLOADS[HEADLINE]
+    if args.calibrate:
+        src = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     # ---- headline: the whole step, graph-replayed
     log(f"headline {HEADLINE}: building inputs")
