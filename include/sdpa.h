@@ -83,8 +83,10 @@ typedef struct {
 /*
  * Supported by the kernels (SDPA_ERR_UNSUPPORTED otherwise):
  *   bf16: Dqk == Dv in {64, 128};  fp32: Dqk == Dv in {32, 64, 128}.
- *   Base pointers 16-byte aligned; (b, h, l) strides multiples of 8 elements (bf16) or
- *   4 elements (fp32); mask (b, h, i) strides likewise.
+ *   bf16: q/k/v/o (and dO, dq, dk, dv) base pointers 16-byte aligned and their (b, h, l)
+ *   strides multiples of 8 elements along every dimension of size > 1; row strides (l, and
+ *   the mask's i) below 2^24 elements.  fp32: 4-byte aligned, any strides.
+ *   The mask may have any (b, h, i) strides (16-byte copies are used when its rows allow).
  */
 
 /* Device workspace (bytes) the forward needs: 0 for prefill; split-KV partial results
@@ -121,7 +123,8 @@ sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, c
 /*
  * The three stages sdpa_backward runs, in this order, for callers that schedule them
  * themselves.  Same arguments, validation and workspace as sdpa_backward.
- *   prep: D_i = rowsum(dO o O)_i (fp32, into the workspace; 0 for empty rows);
+ *   prep: D_i = rowsum(dO o O)_i and LSE_i * log2(e) (fp32, into the workspace; D = 0 and
+ *         +inf for empty rows);
  *   dkdv: dK and dV (reads D from the workspace);
  *   dq:   dQ       (reads D from the workspace).
  * Once prep has finished, dkdv and dq are independent of each other and may run

@@ -78,6 +78,12 @@ sdpa_status check_problem(const sdpa_problem* p) {
         return fail(SDPA_ERR_UNSUPPORTED, "%s stride %d (%lld) is not a multiple of %lld elements",
                     names[t], a, (long long)strides[t][a], (long long)vec);
     }
+  // bf16 kernels copy 64-row tiles through buffer resources whose byte range is 32-bit.
+  if (p->dtype == SDPA_DTYPE_BF16)
+    for (int t = 0; t < 5; ++t)
+      if (strides[t][2] >= ((int64_t)1 << 24))
+        return fail(SDPA_ERR_UNSUPPORTED, "%s row stride (%lld) must be below 2^24 elements", names[t],
+                    (long long)strides[t][2]);
   // Rows of one (b, h) must not overlap: the row stride covers the row.
   if (p->Lq > 1 && p->q_stride[2] < p->Dqk) return fail(SDPA_ERR_INVALID_ARGUMENT, "q rows overlap");
   if (p->Lk > 1 && p->k_stride[2] < p->Dqk) return fail(SDPA_ERR_INVALID_ARGUMENT, "k rows overlap");

@@ -79,6 +79,8 @@ def _bwd(lib, p, lse=FAKE, dq=FAKE, ws=FAKE, nws=1 << 20, stage="sdpa_backward")
     (lambda p: p.k_stride.__setitem__(2, 60), SDPA_ERR_UNSUPPORTED),     # not a multiple of 8
     (lambda p: p.q_stride.__setitem__(1, -64), SDPA_ERR_INVALID_ARGUMENT),
     (lambda p: p.o_stride.__setitem__(2, 32), SDPA_ERR_INVALID_ARGUMENT),  # rows overlap
+    (lambda p: p.v_stride.__setitem__(2, 1 << 24), SDPA_ERR_UNSUPPORTED),  # 64-row tile > 2 GiB
+    (lambda p: p.mask_stride.__setitem__(2, 1 << 24), SDPA_ERR_UNSUPPORTED),
 ])
 def test_forward_rejects(lib, mutate, status):
     p = _problem()
