@@ -169,14 +169,16 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16* mb = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh +
                        (int64_t)i0 * p.m_si + j0;
       const int nr = min(p.Lq - i0, kQT);
-      const buf_rsrc_t rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
+      const i32x4 rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
       const int mw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
       for (int i = 0; i < MPW; ++i) buffer_to_lds<16>(rs, Md, (mw * MPW + i) * 1024, mvoff[i]);
     }
   };
 
-  // K and V operands of this lane's key (B operands of S = Q K^T and dP = dO V^T).
+  // Tile 0 and the K, V operands of this lane's key (B operands of S = Q K^T and
+  // dP = dO V^T) land first; tile 1 streams in behind the first block.
+  if (total > 0) load_tile(0, Q0, G0, R0, M0);
   bf16x8 kreg[NS], vreg[NS];
 #pragma unroll
   for (int kk = 0; kk < NS; ++kk) {
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
     kreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(kbase + (int64_t)myk * p.k_sl + kk * 16 + 8 * hi) : zero16());
     vreg[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(vbase + (int64_t)myk * p.v_sl + kk * 16 + 8 * hi) : zero16());
   }
-  if (total > 0) load_tile(0, Q0, G0, R0, M0);
+  wait_vmem();
   if (total > 1) load_tile(1, Q1, G1, R1s, M1);
 
   f32x16 dk_acc[NT], dv_acc[NT];
@@ -347,9 +349,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   if (total > 0) {
-    // tile 0 landed (tile 1 may be in flight)
-    wait_vmem();
-    __syncthreads();
+    // the first phase runs the dV, dK MFMAs of "block -1" (rows 32..63 of buffer 2) with
+    // zero weights: those rows are zeroed so the products are exactly zero
+    lds_zero<32 * D * 2, 64 * NW>(Q2 + 32 * D, tid);
+    lds_zero<32 * D * 2, 64 * NW>(G2 + 32 * D, tid);
+    __syncthreads();  // every wave's share of tile 0 has landed; the zeros are visible
 #pragma unroll
     for (int i = 0; i < R2; ++i) {
       const bf16x8 op = tile_row8<D>((i & 1) ? G0 : Q0, qr, 2 * (i >> 1) + hi);
@@ -464,6 +468,15 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
   if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1);
   const int nvis = (vis_stop + 31) / 32;  // 32-key blocks this wave works on (a prefix)
 
+  TileCopy<kBN, D, NW> kcopy, vcopy;
+  kcopy.init(p.k_sl, wave, lane);
+  vcopy.init(p.v_sl, wave, lane);
+  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
+    kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
+    vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
+  };
+  // tile 0 and this lane's row operands land first; tile 1 streams in behind
+  if (n_tiles > 0) load_tile(0, K0, V0);
   const int qi = wq_lo + l32;  // this lane's query (N index)
   const bool qok = qi < q_end;
   bf16x8 qreg[NS], doreg[NS];
@@ -475,15 +488,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
   const int64_t rowid = ((int64_t)b * p.Hq + h) * p.Lq + qi;
   const float nl2 = qok ? -a.lse2[rowid] : kNegInf;  // exp2 offset of this lane's row
   const float dsum = qok ? a.dsum[rowid] : 0.f;
-
-  TileCopy<kBN, D, NW> kcopy, vcopy;
-  kcopy.init(p.k_sl, wave, lane);
-  vcopy.init(p.v_sl, wave, lane);
-  auto load_tile = [&](int j0, bf16* Kd, bf16* Vd) {
-    kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
-    vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
-  };
-  if (n_tiles > 0) load_tile(0, K0, V0);
+  wait_vmem();
   if (n_tiles > 1) load_tile(kBN, K1, V1);
 
   f32x16 dq_acc[NT];
@@ -637,10 +642,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
   };
 
   if (n_tiles > 0) {
-    // tile 0 (and Q, dO) landed; tile 1 may still be in flight
-    if (n_tiles > 1) wait_vmem_le<2 * TileCopy<kBN, D, NW>::PER_WAVE>();
-    else wait_vmem();
-    __syncthreads();
+    // the first phase runs the dQ MFMAs of "block -1" (rows 32..63 of buffer 2) with zero
+    // weights: those rows are zeroed so the products are exactly zero
+    lds_zero<32 * D * 2, 64 * NW>(K2 + 32 * D, tid);
+    __syncthreads();  // every wave's share of tile 0 has landed; the zeros are visible
     if (nvis > 0) {
 #pragma unroll
       for (int i = 0; i < R2; ++i) {

@@ -3,10 +3,10 @@
 // Same operation as the prefill forward for one query position per head.  The work is
 // bound by reading the KV cache from HBM ("Understanding PyTorch Scaled Dot-Product
 // Attention" section 5: the KV cache dominates decode), so:
-//  - the G = Hq/Hkv query heads that share a KV head are packed into the N columns of one
-//    MFMA tile (lane l%32 < G is query head g*G + l%32), so each K/V byte is read once for
-//    all of them ("Understanding PyTorch Scaled Dot-Product Attention" section 4 for the
-//    head map);
+//  - the G = Hq/Hkv (at most 16) query heads that share a KV head are packed into the N
+//    columns of a 16x16x32 MFMA tile (lane l%16 < G is query head g*G + l%16), so each K/V
+//    byte is read once for all of them ("Understanding PyTorch Scaled Dot-Product
+//    Attention" section 4 for the head map);
 //  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
 //    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> LDS with
 //    buffer loads (no staging registers and no address arithmetic per copy), double
@@ -24,17 +24,29 @@ namespace {
 
 constexpr int kDT = 32;  // keys per tile
 
+// 16x16x32 MFMAs: the N columns are the (at most 16) query heads of the group, so a quarter
+// of the columns do useful work where a 32-wide tile would use an eighth, and each lane holds
+// 8 scores per 32-key tile instead of 16.
+//   S^T (16 keys x heads) = K (16 keys x 32 d) . Q^T, twice per tile: lane (g4 = l/16,
+//       i16 = l%16) ends with keys 4*g4 + v (first block) and 16 + 4*g4 + v (second) of head
+//       i16;
+//   O^T (16 d x heads) += V^T (16 d x 32 keys) . P^T: the 32 keys in the order lane g4
+//       holds them (4*g4 + 0..3, 16 + 4*g4 + 0..3), so bf16(P) feeds the B operand as is and
+//       V^T comes from two transposing reads per d block.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kDT * D;
+  constexpr int NK = D / 32;  // k-steps of one S^T block
+  constexpr int NM = D / 16;  // 16-row d blocks of O^T
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
   const Problem& p = a.p;
   const int lane = threadIdx.x;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int g4 = lane >> 4;
+  const int i16 = lane & 15;
 
   const int c = blockIdx.x % a.n_split;
   const int bg = blockIdx.x / a.n_split;
@@ -46,19 +58,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int k1 = min(k0 + a.split_keys, kv_end);
   const int n_tiles = (k1 - k0 + kDT - 1) / kDT;
 
-  const bool qvalid = l32 < p.G;
-  const int h = g * p.G + (qvalid ? l32 : 0);
+  const bool qvalid = i16 < p.G;
+  const int h = g * p.G + (qvalid ? i16 : 0);
   const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
   const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
 
-  bf16x8 qreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 16 + 8 * hi) : zero16());
-
-  // K/V tiles HBM -> LDS, one tile ahead (rows past the split arrive as zeros)
-  TileCopy<kDT, D, 1> kcopy, vcopy;
+  // K/V tiles HBM -> LDS, one tile ahead (rows past the split arrive as zeros), each with
+  // the swizzle of the way it is read
+  TileCopy<kDT, D, 1, 1> kcopy;
+  TileCopy<kDT, D, 1, 2> vcopy;
   kcopy.init(p.k_sl, 0, lane);
   vcopy.init(p.v_sl, 0, lane);
   auto load_tile = [&](int t, bf16* Kd, bf16* Vd) {
@@ -67,20 +76,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   };
   load_tile(0, K0, V0);
 
-  f32x16 oacc[D / 32];
+  // Q^T operand: lane (g4, i16) holds d = 32*kk + 8*g4 .. +7 of head i16
+  bf16x8 qreg[NK];
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
+  for (int kk = 0; kk < NK; ++kk)
+    qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 32 + 8 * g4) : zero16());
+
+  f32x4 oacc[NM];
+#pragma unroll
+  for (int mb = 0; mb < NM; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // reference max (log2 units; moved only when a tile's max exceeds it by more than 2^8, so
-  // weights stay <= 256), rounded-weight sum, fp32-weight sum
+  // weights stay <= 256), rounded-weight sum, fp32-weight sum (per lane: its 8 keys)
   float mref = kNegInf, lrow = 0.f, frow = 0.f;
 
   const float c2 = p.scale_log2;
   const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
-  const int kr = perm_row(l32);
-  const int blk = lane >> 4;
-  const int arow = (lane & 15) >> 2;
-  const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
-  const int thalf = 4 * (lane & 1);
+  // transposing reads: lane j of a 16-lane block supplies row base + j/4, d 4*(j%4) .. +3
+  const int trow = i16 >> 2;
+  const int tchunk = (i16 & 3) >> 1;
+  const int thalf = 4 * (i16 & 1);
+
+  // max / sum over the four lanes l, l^16, l^32, l^48 (one head)
+  auto max4 = [](float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  };
+  auto sum4 = [](float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+  };
 
   // One tile; unrolled by two over the LDS buffers so the reads of tile t and the copies
   // into the other buffer are distinct LDS objects at compile time.  The buffer refilled
@@ -93,25 +117,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     wait_vmem();  // tile t landed
     load_tile(t + 1, Kl, Vl);
 
-    f32x16 sacc = f32x16{};
-    {
-      bf16x8 kop[D / 16];
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) kop[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(kop[kk], qreg[kk], sacc);
+    for (int kk = 0; kk < NK; ++kk) {
+      s0 = mfma16(tile_row8<D, 1>(Kt, i16, 4 * kk + g4), qreg[kk], s0);
+      s1 = mfma16(tile_row8<D, 1>(Kt, 16 + i16, 4 * kk + g4), qreg[kk], s1);
     }
-    const bool partial = j0 + kDT > k1;
-    float s[16];
-    float mx = kNegInf;
+    float x[8];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = sacc[v];
-      if (partial) x = (j0 + 16 * hi + v < k1) ? x : kNegInf;
-      s[v] = x;
-      mx = fmaxf(mx, x);
+    for (int v = 0; v < 4; ++v) { x[v] = s0[v]; x[4 + v] = s1[v]; }
+    if (j0 + kDT > k1) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int key = j0 + (v < 4 ? 0 : 16) + 4 * g4 + (v & 3);
+        x[v] = key < k1 ? x[v] : kNegInf;
+      }
     }
-    mx = xhalf_max(mx) * c2;
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = max4(mx) * c2;
     const bool need = mx > mref + 8.f;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float mnew = need ? mx : mref;
@@ -120,41 +143,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       lrow *= corr;
       frow *= corr;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
+      for (int mb = 0; mb < NM; ++mb) oacc[mb] *= corr;
     }
     const float m_use = (mref == kNegInf) ? 0.f : mref;
-    bf16x8 pop[2];
+    bf16x8 pop;
     float psum = lrow, fsum = frow;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-        const int v = half * 8 + 2 * t2;
-        f32x2 e;
-        e[0] = fast_exp2(fmaf(s[v], c2, -m_use));
-        e[1] = fast_exp2(fmaf(s[v + 1], c2, -m_use));
-        const bf16x2 e2 = __builtin_convertvector(e, bf16x2);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, psum, false);
-        fsum += e[0];
-        fsum += e[1];
-        pop[half][2 * t2] = e2[0];
-        pop[half][2 * t2 + 1] = e2[1];
-      }
+    for (int t2 = 0; t2 < 4; ++t2) {
+      f32x2 e;
+      e[0] = fast_exp2(fmaf(x[2 * t2], c2, -m_use));
+      e[1] = fast_exp2(fmaf(x[2 * t2 + 1], c2, -m_use));
+      const bf16x2 e2 = __builtin_convertvector(e, bf16x2);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, psum, false);
+      fsum += e[0];
+      fsum += e[1];
+      pop[2 * t2] = e2[0];
+      pop[2 * t2 + 1] = e2[1];
     }
     lrow = psum;
     frow = fsum;
-    // V^T operands (transposing reads)
-    bf16x8 vop[2][D / 32];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tr = 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) vop[half][mb] = tile_tr8<D>(Vt, tr, tchunk + 4 * mb, thalf);
+    for (int mb = 0; mb < NM; ++mb) {
+      const bf16x8 vop = join_tr(tile_tr4<D, 2>(Vt, 4 * g4 + trow, 2 * mb + tchunk, thalf),
+                                 tile_tr4<D, 2>(Vt, 16 + 4 * g4 + trow, 2 * mb + tchunk, thalf));
+      oacc[mb] = mfma16(vop, pop, oacc[mb]);
     }
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(vop[half][mb], pop[half], oacc[mb]);
   };
 
   for (int t = 0; t < n_tiles; t += 2) {
@@ -163,23 +176,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
   wait_vmem();  // the last (empty) copy has landed before the workgroup's LDS is released
 
-  const float lt = xhalf_sum(lrow);
-  const float ft = xhalf_sum(frow);
+  const float lt = sum4(lrow);
+  const float ft = sum4(frow);
   if (qvalid) {
-    const int64_t prow = ((int64_t)b * p.Hq + h) * a.n_split + c;
+    const int64_t prow = ((int64_t)b * p.Hq + h) * a.n_split + c;  // partial row
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = oacc[mb][v4 * 4 + e] * inv;
-        *reinterpret_cast<f32x4*>(po + mb * 32 + v4 * 8 + hi * 4) = w;
-      }
-    }
-    if (hi == 0) a.part_lse[prow] = lt > 0.f ? (mref * kLn2 + logf(ft)) : kNegInf;
+    for (int mb = 0; mb < NM; ++mb) *reinterpret_cast<f32x4*>(po + 16 * mb + 4 * g4) = oacc[mb] * inv;
+    if (g4 == 0) a.part_lse[prow] = lt > 0.f ? (mref * kLn2 + logf(ft)) : kNegInf;
   }
 }
 

@@ -52,8 +52,6 @@ template <int D, int NW, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
-  // global_load_lds instructions per wave for one K+V tile
-  constexpr int LOADS_PER_TILE = 2 * (kBN * D / 8 / 64) / NW;
   __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
@@ -129,7 +127,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     kcopy.copy(rows_rsrc<D, kBN>(kb_, p.k_sl, j0, kv_stop), Kd, wave);
     vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
   };
-  // ---- Q operand (B of S^T = K Q^T): lane holds query row, 8 consecutive d per k-step.
+  // ---- tile 0 and the Q operand (B of S^T = K Q^T: lane holds query row, 8 consecutive d
+  // per k-step) land first; tile 1 streams in behind the first block.
+  if (n_tiles > 0) load_tile(0, K0, V0);
   const int qrow = wq_lo + l32;
   bf16x8 qreg[D / 16];
 #pragma unroll
@@ -137,8 +137,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     u32x4 x = qrow < q_end ? ld16(qb + (int64_t)qrow * p.q_sl + kk * 16 + 8 * hi) : zero16();
     qreg[kk] = __builtin_bit_cast(bf16x8, x);
   }
-  // first two tiles in flight behind Q
-  if (n_tiles > 0) load_tile(0, K0, V0);
+  wait_vmem();
   if (n_tiles > 1) load_tile(kBN, K1, V1);
 
   // reference max (log2 units), sum of bf16 weights (normalises O), sum of fp32 weights
@@ -350,10 +349,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   if (n_tiles > 0) {
-    // tile 0 (and Q) landed; tile 1 may still be in flight
-    if (n_tiles > 1) wait_vmem_le<LOADS_PER_TILE>();
-    else wait_vmem();
-    __syncthreads();
+    __syncthreads();  // every wave's share of tile 0 has landed
     if (nvis > 0) {
 #pragma unroll
       for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(K0, 0, kk), qreg[kk], sacc_a);

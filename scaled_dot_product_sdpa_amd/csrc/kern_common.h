@@ -39,6 +39,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16  D(16x16) += A(16x32) * B(32x16)  (measured on gfx950):
+//   A: lane l holds A[l%16][8*(l/16) + t];  B: lane l holds B[8*(l/16) + t][l%16];
+//   D: lane l holds D[4*(l/16) + v][l%16], v = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Token placed at M-row r of a 32-row MFMA block (see the header comment).
 __device__ __forceinline__ int perm_row(int r) {
   return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
@@ -84,17 +91,19 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Global -> LDS without registers: lane L's 16 bytes from `src` land at lds_base + 16 * L
-// (measured on gfx950).  lds_base must be the same for every lane of the wave.
-__device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
-}
-
-// Wait until this wave's global loads (including global -> LDS copies) have landed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// ... until at most N of them are outstanding (loads complete in issue order).
+// Wait until at most N of this wave's vector-memory operations (loads, stores, copies to
+// LDS) are outstanding; they complete in issue order.  The s_waitcnt builtin (not inline
+// assembly) lets the compiler see the wait, so it knows its own earlier loads have landed
+// and adds no waits of its own later; the empty assembly keeps memory accesses from moving
+// above it.
 template <int N>
-__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt 11:8
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
 // XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded).
 // gfx950 LDS has 64 four-byte banks (measured: a conflict-free pattern reads ~245 B/clk per
@@ -112,10 +121,23 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
 }
 
+// Swizzles for the 16x16x32 MFMA operands, chosen by SW:
+//  1: 16-byte reads by 16-lane phases on sixteen consecutive rows at one chunk;
+//  2: ds_read_b64_tr_b16 by 32-lane phases on eight consecutive rows (r % 8 == 0) at the
+//     chunk pair {2m, 2m + 1}.
+// Each maps a phase onto sixteen distinct 16-byte bank groups (a D = 64 row spans half
+// the banks, so its row parity is part of the bank group).
+template <int D, int SW>
+__device__ __forceinline__ int swz_sel(int r) {
+  if constexpr (SW == 0) return swz<D>(r);
+  else if constexpr (SW == 1) return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  else return D == 128 ? ((r & 7) << 1) : (r & 6);
+}
+
 // MFMA operand from a swizzled tile: 16 bytes (8 elements) of row r at logical chunk c.
-template <int D>
+template <int D, int SW = 0>
 __device__ __forceinline__ bf16x8 tile_row8(const bf16* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ swz<D>(r)) * 8));
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + ((c ^ swz_sel<D, SW>(r)) * 8));
 }
 
 // Transposed MFMA operand from a swizzled tile: this lane's element column of rows
@@ -128,76 +150,69 @@ __device__ __forceinline__ bf16x8 tile_tr8(const bf16* tile, int tr, int c, int 
   return join_tr(lds_read_tr4(tile + o0), lds_read_tr4(tile + o1));
 }
 
-// HBM -> LDS copy of one tile of ROWS rows x D bf16 (rows r0.. of `g`, clamped to the row
-// below `stop`, so a clamped row repeats finite data whose pairs the caller masks) by the
-// NW waves of the workgroup.  LDS chunk ci of the tile holds logical chunk
-// (ci % CPR) ^ swz<D>(row) of row ci / CPR.
-template <int ROWS, int D, int NW>
-__device__ __forceinline__ void tile_to_lds_swz(const bf16* g, int64_t row_stride, int r0,
-                                                int stop, bf16* lds_tile, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int NBLK = ROWS * CPR / 64;  // 1 KB wave-instructions per tile
-  static_assert(NBLK % NW == 0, "tile must split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < NBLK / NW; ++i) {
-    const int blk = wave * (NBLK / NW) + i;
-    const int ci = blk * 64 + lane;
-    const int r = ci / CPR;
-    const int c = (ci % CPR) ^ swz<D>(r);
-    const int row = min(r0 + r, stop - 1);
-    global_to_lds16(g + (int64_t)row * row_stride + c * 8, lds_tile + blk * 512);
-  }
+// One transposing read (four bf16) of row r, logical chunk c, 4-element half h of a tile.
+template <int D, int SW>
+__device__ __forceinline__ i16x4 tile_tr4(const bf16* tile, int r, int c, int h) {
+  return lds_read_tr4(tile + r * D + ((c ^ swz_sel<D, SW>(r)) * 8) + h);
 }
 
 // ---- HBM -> LDS through a buffer resource (buffer_load ... lds): the per-lane byte offset
 // inside a tile is fixed, so after set-up a tile copy costs no vector instructions; the
 // tile's first row moves with the (scalar) resource base.
 
-// The resource type exists only for the GPU target; the host pass of this single-source
-// file parses the device functions with a placeholder.
-#if defined(__HIP_DEVICE_COMPILE__)
-typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
-#else
-struct buf_rsrc_t { uint32_t w[4]; };
-#endif
-
-// Raw buffer of `bytes` bytes at `base` (stride 0, 32-bit dword format): loads past the
-// end return zeros.
-__device__ __forceinline__ buf_rsrc_t raw_rsrc(const void* base, int64_t bytes) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-#else
-  return buf_rsrc_t{};
-#endif
+// Raw buffer resource (stride 0, 32-bit dword format) over `bytes` bytes at `base`, as the
+// four scalar registers the buffer instructions take; loads past the end return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
 // SIZE bytes per lane from src + voff into LDS at lds + byte_off + SIZE * lane (wave-uniform
-// destination).  The offset is applied after the cast to the LDS address space, so that a
-// constant destination stays a plain LDS address.
+// destination).  Written as inline assembly on purpose: the compiler then does not treat the
+// copy as an LDS store that may alias the LDS reads after it, and does not make those reads
+// wait for every copy in flight; each kernel instead waits for its copies (s_waitcnt vmcnt)
+// before the barrier that publishes a tile.  The copy takes its LDS address from M0, and an
+// SALU write of M0 needs one wait state before an LDS-DMA buffer load reads it (the CDNA
+// ISA's table of manually inserted wait states), hence the s_nop; without it the load can
+// see the previous copy's M0 and land in the wrong place.  M0 is a reserved register that
+// cannot be named as clobbered; nothing else in these kernels uses it.
 template <int SIZE>
-__device__ __forceinline__ void buffer_to_lds(buf_rsrc_t src, void* lds, uint32_t byte_off, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void buffer_to_lds(i32x4 src, void* lds, uint32_t byte_off, uint32_t voff) {
   static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
-  auto* l = (__attribute__((address_space(3))) char*)lds + byte_off;
-  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 16, voff, 0, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(src, l, 4, voff, 0, 0, 0);
-#endif
+  const uint32_t addr = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds + byte_off));
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(addr),
+                 "v"(voff), "s"(src) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(addr),
+                 "v"(voff), "s"(src) : "memory");
 }
 
-// 16 bytes from src + voff into registers (zeros past the end of the buffer).
-__device__ __forceinline__ u32x4 buffer_ld16(buf_rsrc_t src, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src, voff, 0, 0));
-#else
-  return u32x4{0u, 0u, 0u, 0u};
-#endif
+// Zero BYTES bytes of LDS at dst (16-byte aligned) with the NT threads of the workgroup.
+// The pipelined kernels run a block's trailing MFMAs one block late, so their first block
+// multiplies zero weights by the previous buffer's rows; those rows must hold finite values
+// (uninitialised LDS may hold NaN or Inf bit patterns, and 0 * NaN = NaN).
+template <int BYTES, int NT>
+__device__ __forceinline__ void lds_zero(bf16* dst, int tid) {
+  static_assert(BYTES % 16 == 0, "whole 16-byte stores");
+  constexpr int N16 = BYTES / 16;
+#pragma unroll
+  for (int i = 0; i < (N16 + NT - 1) / NT; ++i)
+    if (N16 % NT == 0 || i * NT + tid < N16) reinterpret_cast<u32x4*>(dst)[i * NT + tid] = zero16();
 }
 
 // Raw buffer over rows r0 .. min(stop, r0 + ROWS) - 1 of a row-major bf16 matrix
 // (row_stride elements, rows of D elements); reads past those rows return zeros.  The
 // host keeps ROWS * row_stride * 2 bytes below 2^31.
 template <int D, int ROWS>
-__device__ __forceinline__ buf_rsrc_t rows_rsrc(const bf16* base, int64_t row_stride, int r0, int stop) {
+__device__ __forceinline__ i32x4 rows_rsrc(const bf16* base, int64_t row_stride, int r0, int stop) {
   const int n = min(stop - r0, ROWS);
   const int64_t bytes = n > 0 ? (int64_t)(n - 1) * row_stride * 2 + D * 2 : 0;
   return raw_rsrc(base + (int64_t)r0 * row_stride, bytes);
@@ -205,8 +220,8 @@ __device__ __forceinline__ buf_rsrc_t rows_rsrc(const bf16* base, int64_t row_st
 
 // Per-lane byte offsets of a ROWS x D tile copy by NW waves: instruction i of wave w moves
 // LDS chunks (w * NBLK/NW + i) * 64 + lane, chunk ci holding logical chunk
-// (ci % CPR) ^ swz<D>(row) of row ci / CPR (the layout tile_to_lds_swz writes).
-template <int ROWS, int D, int NW>
+// (ci % CPR) ^ swz_sel<D, SW>(row) of row ci / CPR (the layout tile_row8 reads).
+template <int ROWS, int D, int NW, int SW = 0>
 struct TileCopy {
   static constexpr int CPR = D / 8;
   static constexpr int NBLK = ROWS * CPR / 64;  // 1 KB wave-instructions per tile
@@ -218,11 +233,11 @@ struct TileCopy {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int ci = (wave * PER_WAVE + i) * 64 + lane;
       const int r = ci / CPR;
-      const int c = (ci % CPR) ^ swz<D>(r);
+      const int c = (ci % CPR) ^ swz_sel<D, SW>(r);
       voff[i] = (uint32_t)(r * row_stride * 2 + c * 16);
     }
   }
-  __device__ __forceinline__ void copy(buf_rsrc_t src, bf16* lds_tile, int wave) const {
+  __device__ __forceinline__ void copy(i32x4 src, bf16* lds_tile, int wave) const {
     if constexpr (NW > 1) wave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform LDS destination
     else wave = 0;
 #pragma unroll

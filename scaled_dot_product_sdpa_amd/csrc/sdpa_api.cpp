@@ -94,7 +94,7 @@ sdpa_status check_problem(const sdpa_problem* p) {
 
 bool use_decode(const sdpa_problem* p, bool has_mask) {
   return p->dtype == SDPA_DTYPE_BF16 && p->Lq == 1 && !p->is_causal && !has_mask &&
-         p->Hq / p->Hkv <= 32;
+         p->Hq / p->Hkv <= 16;
 }
 
 sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_t* lq,

@@ -43,6 +43,11 @@ CASES = {
     # decode (Lq = 1) against a KV cache with lengths and NaN-poisoned padding
     "decode_gqa_d128": W["gqa_decode_8k"].scaled(B=4, Hq=8, Hkv=2, Lk=1100, len_range=(1, 1100), seed=17),
     "decode_mha_d64": W["gqa_decode_8k"].scaled(B=3, Hq=4, Hkv=4, Lk=700, D=64, len_range=(30, 700), seed=18),
+    # the widest query-head group the decode kernel takes (16), one not a power of two (6,
+    # several key splits), and a wider one (32) that the engine sends down the prefill path
+    "decode_g16_d64": W["gqa_decode_8k"].scaled(B=2, Hq=16, Hkv=1, Lk=600, D=64, len_range=(1, 600), seed=19),
+    "decode_g6_d128": W["gqa_decode_8k"].scaled(B=2, Hq=12, Hkv=2, Lk=2100, len_range=(500, 2100), seed=20),
+    "decode_g32_d128": W["gqa_decode_8k"].scaled(B=2, Hq=32, Hkv=1, Lk=300, len_range=(1, 300), seed=21),
 }
 
 
