@@ -110,10 +110,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Low key tiles see the most (causal) queries: they are launched first.
-  const int bg_count = p.B * p.Hkv;
-  const int kt = blockIdx.x / bg_count;
-  const int bg = blockIdx.x % bg_count;
+  // Work item: (batch, KV head) group, then key tile kt; low key tiles see the most
+  // (causal) queries and are launched first.
+  int bg, kt;
+  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), 1, !CAUSAL, bg, kt);
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
@@ -424,12 +424,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int bh_count = p.B * p.Hq;
-  const int rank = blockIdx.x / bh_count;
-  const int bh = blockIdx.x % bh_count;
-  const int b = bh / p.Hq;
-  const int h = bh % p.Hq;
-  const int g = h / p.G;
+  // Work item: (batch, KV head) group, then query tile `rank` of head h of the group.
+  int gi, r;
+  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
+  const int b = gi / p.Hkv;
+  const int g = gi % p.Hkv;
+  const int h = g * p.G + r % p.G;
+  const int rank = r / p.G;
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
   // Rows: as in the forward (heavy tiles first, or paired half-tiles for small grids).
@@ -706,12 +707,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_seq_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int bh_count = p.B * p.Hq;
-  const int rank = blockIdx.x / bh_count;
-  const int bh = blockIdx.x % bh_count;
-  const int b = bh / p.Hq;
-  const int h = bh % p.Hq;
-  const int g = h / p.G;
+  // Work item: (batch, KV head) group, then query tile `rank` of head h of the group.
+  int gi, r;
+  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
+  const int b = gi / p.Hkv;
+  const int g = gi % p.Hkv;
+  const int h = g * p.G + r % p.G;
+  const int rank = r / p.G;
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
   // Rows: as in the forward (heavy tiles first, or paired half-tiles for small grids).

@@ -9,10 +9,12 @@
 // Work decomposition: a workgroup of NW waves owns BM = NW * 32 query rows of one
 // (batch, head); each wave owns 32 query rows and keeps their Q operand, O accumulator
 // and running statistics in registers.  K/V tiles of 64 keys stream HBM -> LDS with
-// global_load_lds (16 bytes per lane, no staging registers) through three LDS buffers:
-// while tile t is computed, tile t+1 is resident or landing and tile t+2 is requested,
-// one barrier per tile.  Tiles are stored unpadded with XOR-swizzled 16-byte chunks
-// (kern_common.h) so the MFMA operand reads are free of bank conflicts.
+// buffer loads straight into LDS (16 bytes per lane, no staging registers): while tile t
+// is computed, tile t+1 is landing and tile t+2 is requested after the one barrier of the
+// step, into two K and three V buffers.  Tiles are stored unpadded with XOR-swizzled
+// 16-byte chunks (kern_common.h) so the MFMA operand reads are free of bank conflicts.
+// The (batch, KV head) groups are spread over the XCDs so that a group's K/V stay in one
+// L2 while all of its query tiles stream them.
 //
 //   S^T = K Q^T   (keys x queries): A = K rows from LDS (row-permuted, see kern_common.h),
 //                 B = Q held in registers; lane l ends up with 16 consecutive keys of
@@ -48,16 +50,15 @@ namespace {
 constexpr int kBN = 64;             // keys per K/V tile (two 32-key MFMA blocks)
 constexpr float kRescaleLog2 = 8.f; // move the reference max only past this growth
 
-template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, int NW, int WPE, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
-  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
+  // Tile t's K is read by the phases of blocks 2t-1 (the next block's scores) and 2t; its V
+  // by those of blocks 2t and 2t+1.  Tile t+2 is requested after the barrier in the middle
+  // of step t, so K needs two buffers (tile t's is free by then) and V three.
+  __shared__ __attribute__((aligned(16))) bf16 Kb[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vb[3][TILE];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -66,13 +67,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
 
-  // ---- work item; the heads of one KV group are adjacent in launch order.
-  const int bh_count = p.B * p.Hq;
-  const int rank = blockIdx.x / bh_count;
-  const int bh = blockIdx.x % bh_count;
-  const int b = bh / p.Hq;
-  const int h = bh % p.Hq;
-  const int g = h / p.G;
+  // ---- work item: (batch, KV head) group, then query tile `rank` of head h of the group
+  // (the G heads of one rank adjacent in launch order).
+  int gi, r;
+  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
+  const int b = gi / p.Hkv;
+  const int g = gi % p.Hkv;
+  const int h = g * p.G + r % p.G;
+  const int rank = r / p.G;
 
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   };
   // ---- tile 0 and the Q operand (B of S^T = K Q^T: lane holds query row, 8 consecutive d
   // per k-step) land first; tile 1 streams in behind the first block.
-  if (n_tiles > 0) load_tile(0, K0, V0);
+  if (n_tiles > 0) load_tile(0, Kb[0], Vb[0]);
   const int qrow = wq_lo + l32;
   bf16x8 qreg[D / 16];
 #pragma unroll
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     qreg[kk] = __builtin_bit_cast(bf16x8, x);
   }
   wait_vmem();
-  if (n_tiles > 1) load_tile(kBN, K1, V1);
+  if (n_tiles > 1) load_tile(kBN, Kb[1], Vb[1]);
 
   // reference max (log2 units), sum of bf16 weights (normalises O), sum of fp32 weights
   // (gives LSE); both sums are relative to the reference max.
@@ -306,6 +308,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
     const float m_use = post_max(mx);
     // region 2
+
     snext = f32x16{};
     constexpr int P = 8 / NS;  // score pairs per slot
     f32x2 t[8];
@@ -333,14 +336,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     if (bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext);
   };
 
-  // One tile step; the loop below is unrolled by three so that the buffers being read,
-  // the next tile's and the one being filled are distinct LDS objects at compile time
-  // (the compiler then does not make the reads wait for the copies in flight).
+  // One tile step; the loop below is unrolled by six (two K buffers, three V buffers) so
+  // that every buffer index is a compile-time constant.
   auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl)
                   __attribute__((always_inline)) {
     // block 2t: V from this tile, K of block 2t+1 from this tile
     phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b);
-    // tile t+1 has landed for every wave, and no wave still reads tile t-1
+    // tile t+1 has landed for every wave, and no wave still reads K of tile t or V of
+    // tile t-1
     if (t + 1 < n_tiles) wait_vmem();
     __syncthreads();
     if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
@@ -352,13 +355,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();  // every wave's share of tile 0 has landed
     if (nvis > 0) {
 #pragma unroll
-      for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(K0, 0, kk), qreg[kk], sacc_a);
+      for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(Kb[0], 0, kk), qreg[kk], sacc_a);
     }
   }
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(t, K0, V0, K1, K2, V2);
-    if (t + 1 < n_tiles) step(t + 1, K1, V1, K2, K0, V0);
-    if (t + 2 < n_tiles) step(t + 2, K2, V2, K0, K1, V1);
+  for (int t = 0; t < n_tiles; t += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u)
+      if (t + u < n_tiles)
+        step(t + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3]);
   }
   // the last block's PV
 #pragma unroll
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int WPE, bool CAUSAL, bool MASK>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   constexpr int BM = NW * 32;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
@@ -394,15 +398,19 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
   const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
   const int grid = n_wg * a.p.B * a.p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, WPE, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_shape(const FwdArgs& a, hipStream_t s) {
-  // 8 waves of 32 query rows per workgroup: two waves per SIMD hide each other's LDS and
-  // MFMA latencies.
-  return launch_t<D, 8, CAUSAL, MASK>(a, s);
+  // Two waves per SIMD hide each other's LDS and MFMA latencies.  Causal: one workgroup of
+  // 8 waves (256 query rows) per CU, which halves the K/V tile traffic per query row and
+  // suits the heavy-first and paired-row schedules.  Otherwise two independent workgroups
+  // of 4 waves per CU (measured faster on padded batches: the two workgroups' barriers do
+  // not wait for each other, and 128-row tiles waste less past a length).
+  if (CAUSAL) return launch_t<D, 8, 1, CAUSAL, MASK>(a, s);
+  return launch_t<D, 4, 2, CAUSAL, MASK>(a, s);
 }
 
 template <int D>

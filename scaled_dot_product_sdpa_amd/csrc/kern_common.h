@@ -195,6 +195,34 @@ __device__ __forceinline__ void buffer_to_lds(i32x4 src, void* lds, uint32_t byt
                  "v"(voff), "s"(src) : "memory");
 }
 
+// Work item of workgroup `bid` in a grid of NG groups x M items (group gi, item r).  A
+// group is one (batch, KV head); its items share the K/V (or Q/dO) rows that they stream.
+// Order: item-major (heavy items first where the caller numbers them so; runs of `inner`
+// items of one group adjacent), or group-major (all items of a group in a row) when the
+// items of a group carry equal work.  Workgroups are handed to the chip's 8 XCDs
+// round-robin (workgroup i runs on XCD i % 8) and each XCD has its own L2: when the groups
+// divide evenly over the XCDs, XCD x takes only the groups gi % 8 == x, in the same order,
+// so the rows a group streams are fetched into one L2 and reused there.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ void xcd_item(int bid, int NG, int M, int inner, bool group_major,
+                                         int& gi, int& r) {
+  int k = bid, ng = NG, x = 0, step = 1;
+  if (NG % kNumXcd == 0) {
+    k = bid / kNumXcd;
+    x = bid % kNumXcd;
+    ng = NG / kNumXcd;
+    step = kNumXcd;
+  }
+  if (group_major) {
+    gi = (k / M) * step + x;
+    r = k % M;
+  } else {
+    const int outer = k / (ng * inner), rem = k % (ng * inner);
+    gi = (rem / inner) * step + x;
+    r = outer * inner + rem % inner;
+  }
+}
+
 // Zero BYTES bytes of LDS at dst (16-byte aligned) with the NT threads of the workgroup.
 // The pipelined kernels run a block's trailing MFMAs one block late, so their first block
 // multiplies zero weights by the previous buffer's rows; those rows must hold finite values
