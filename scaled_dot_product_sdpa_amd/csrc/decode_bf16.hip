@@ -8,11 +8,10 @@
 //    byte is read once for all of them ("Understanding PyTorch Scaled Dot-Product
 //    Attention" section 4 for the head map);
 //  - the keys of one (batch, KV head) are cut into splits of split_keys keys; every split
-//    is an independent one-wave workgroup that streams 32-key K/V tiles HBM -> LDS with
-//    buffer loads (no staging registers and no address arithmetic per copy), double
-//    buffered; the small LDS and register footprint keeps two such waves per SIMD; splits
-//    past the sequence length exit at once; each split writes a partial (O_c normalised,
-//    lse_c);
+//    is an independent one-wave workgroup that streams 32-key K/V tiles from HBM into
+//    registers with buffer loads (rows past the split read as zeros), two tiles in flight;
+//    two such waves run per SIMD; splits past the sequence length exit at once; each split
+//    writes a partial (O_c normalised, lse_c);
 //  - a combine kernel merges the partials exactly:  LSE = ln sum_c exp(lse_c),
 //    O = sum_c exp(lse_c - LSE) O_c  (the log-sum-exp merge of split-KV partial results
 //    that cuDNN "Attention", SDPA FP16/BF16 Forward, Python API describes for its stats).
@@ -24,32 +23,58 @@ namespace {
 
 constexpr int kDT = 32;  // keys per tile
 
+// Raw buffer resource over `bytes` bytes at `base` for loads into registers (reads past the
+// end return zeros).  The resource type exists only for the GPU target; the host pass of
+// this single-source file parses the device code with a placeholder.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t reg_rsrc_t;
+__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset voff + soff of the buffer; the compiler tracks the load like any
+// other (it inserts the wait before the first use of the result).  The KV cache is read
+// once, so the loads carry the non-temporal cache policy (measured: 12 % more bandwidth
+// than the default policy on the 8k-key GQA decode).
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
+}
+#else
+struct reg_rsrc_t { uint32_t w[4]; };
+__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void*, int64_t) { return reg_rsrc_t{}; }
+__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t, uint32_t, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
+#endif
+
 // 16x16x32 MFMAs: the N columns are the (at most 16) query heads of the group, so a quarter
 // of the columns do useful work where a 32-wide tile would use an eighth, and each lane holds
 // 8 scores per 32-key tile instead of 16.
 //   S^T (16 keys x heads) = K (16 keys x 32 d) . Q^T, twice per tile: lane (g4 = l/16,
 //       i16 = l%16) ends with keys 4*g4 + v (first block) and 16 + 4*g4 + v (second) of head
-//       i16;
+//       i16.  The K operand is loaded from HBM straight into registers in the MFMA layout
+//       (lane: key i16 of the block, d = 32*kk + 8*g4 .. +7).
 //   O^T (16 d x heads) += V^T (16 d x 32 keys) . P^T: the 32 keys in the order lane g4
-//       holds them (4*g4 + 0..3, 16 + 4*g4 + 0..3), so bf16(P) feeds the B operand as is and
-//       V^T comes from two transposing reads per d block.
+//       holds them (4*g4 + 0..3, 16 + 4*g4 + 0..3), so bf16(P) feeds the B operand as is.
+//       V rows are loaded into registers whole (coalesced), written to LDS and read back
+//       transposed (ds_read_b64_tr_b16).
+// Two register sets of K and V rows: while tile t is computed, tile t+1 is in flight and
+// tile t+2 is requested as soon as tile t's K operands and V rows have been consumed.
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kDT * D;
-  constexpr int NK = D / 32;  // k-steps of one S^T block
-  constexpr int NM = D / 16;  // 16-row d blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
+  constexpr int NK = D / 32;          // k-steps of one S^T block
+  constexpr int NM = D / 16;          // 16-row d blocks of O^T
+  constexpr int LPR = D / 8;          // lanes per V row (16 bytes each)
+  constexpr int RPL = 64 / LPR;       // V rows per load instruction
+  constexpr int VLD = kDT / RPL;      // V load instructions per tile
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TILE];
   const Problem& p = a.p;
   const int lane = threadIdx.x;
   const int g4 = lane >> 4;
   const int i16 = lane & 15;
 
-  const int c = blockIdx.x % a.n_split;
-  const int bg = blockIdx.x / a.n_split;
+  const int c = blockIdx.x / (p.B * p.Hkv);  // split-major: every live split of split c
+  const int bg = blockIdx.x % (p.B * p.Hkv); // precedes the (mostly empty) higher splits
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
@@ -64,23 +89,47 @@ void decode_split_kernel(DecodeArgs a) {
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
   const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
 
-  // K/V tiles HBM -> LDS, one tile ahead (rows past the split arrive as zeros), each with
-  // the swizzle of the way it is read
-  TileCopy<kDT, D, 1, 1> kcopy;
-  TileCopy<kDT, D, 1, 2> vcopy;
-  kcopy.init(p.k_sl, 0, lane);
-  vcopy.init(p.v_sl, 0, lane);
-  auto load_tile = [&](int t, bf16* Kd, bf16* Vd) {
-    kcopy.copy(rows_rsrc<D, kDT>(kbase, p.k_sl, k0 + t * kDT, k1), Kd, 0);
-    vcopy.copy(rows_rsrc<D, kDT>(vbase, p.v_sl, k0 + t * kDT, k1), Vd, 0);
-  };
-  load_tile(0, K0, V0);
+  // Per-lane byte offsets inside a tile (the tile's first row moves with the resource; the
+  // whole offset is in the vector operand, which is what the range check covers): K operand
+  // of block kb, k-step kk at koff[kb] + 64 * kk; V row load i at voff[i].
+  uint32_t koff[2], voff[VLD];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) koff[kb] = (uint32_t)((16 * kb + i16) * p.k_sl * 2 + 16 * g4);
+  const int vr = lane / LPR, vc = lane % LPR;
+  // LDS element offset of V row vr + RPL*i, chunk vc, in the layout the transposing reads use
+  int vlds[VLD];
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int r = vr + RPL * i;
+    voff[i] = (uint32_t)(r * p.v_sl * 2 + 16 * vc);
+    vlds[i] = r * D + ((vc ^ swz_sel<D, 2>(r)) * 8);
+  }
 
-  // Q^T operand: lane (g4, i16) holds d = 32*kk + 8*g4 .. +7 of head i16
+  u32x4 kr[2][2][NK], vrg[2][VLD];
+  // Tile t into register set `set`: rows of the split only (past them the loads return 0).
+  auto load_tile = [&](int t, int set) __attribute__((always_inline)) {
+    const int j0 = min(k0 + t * kDT, k1);
+    const int n = min(kDT, k1 - j0);
+    const reg_rsrc_t kr_ = reg_rsrc(kbase + (int64_t)j0 * p.k_sl, n > 0 ? (int64_t)(n - 1) * p.k_sl * 2 + D * 2 : 0);
+    const reg_rsrc_t vr_ = reg_rsrc(vbase + (int64_t)j0 * p.v_sl, n > 0 ? (int64_t)(n - 1) * p.v_sl * 2 + D * 2 : 0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) kr[set][kb][kk] = reg_ld16(kr_, koff[kb] + 64 * kk, 0);
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) vrg[set][i] = reg_ld16(vr_, voff[i], 0);
+  };
+  // Q^T operand (lane (g4, i16) holds d = 32*kk + 8*g4 .. +7 of head i16), loaded before
+  // the tiles so that it is never the youngest load in flight at the top of the loop.
   bf16x8 qreg[NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
     qreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? ld16(qrow + kk * 32 + 8 * g4) : zero16());
+  // The loads are unconditional: a tile past the split has an empty range and reads zeros
+  // without touching memory, and every path then has the same loads in flight, so the
+  // compiler's waits before each tile's first use stay exact (tile t+1 keeps streaming).
+  load_tile(0, 0);
+  load_tile(1, 1);
 
   f32x4 oacc[NM];
 #pragma unroll
@@ -106,23 +155,22 @@ void decode_split_kernel(DecodeArgs a) {
     return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
   };
 
-  // One tile; unrolled by two over the LDS buffers so the reads of tile t and the copies
-  // into the other buffer are distinct LDS objects at compile time.  The buffer refilled
-  // with tile t+1 held tile t-1, whose reads all completed before its MFMAs.  The copy is
-  // unconditional: past the split every row is out of the buffer's range and the copy
-  // writes zeros without touching memory.
-  auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kl, bf16* Vl)
-                  __attribute__((always_inline)) {
+  // One tile from register set `set` (unrolled by two so the set is a compile-time index).
+  auto step = [&](int t, int set) __attribute__((always_inline)) {
     const int j0 = k0 + t * kDT;
-    wait_vmem();  // tile t landed
-    load_tile(t + 1, Kl, Vl);
-
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      s0 = mfma16(tile_row8<D, 1>(Kt, i16, 4 * kk + g4), qreg[kk], s0);
-      s1 = mfma16(tile_row8<D, 1>(Kt, 16 + i16, 4 * kk + g4), qreg[kk], s1);
+      s0 = mfma16(__builtin_bit_cast(bf16x8, kr[set][0][kk]), qreg[kk], s0);
+      s1 = mfma16(__builtin_bit_cast(bf16x8, kr[set][1][kk]), qreg[kk], s1);
     }
+    // V rows to LDS (the same wave reads them back below; LDS operations of one wave
+    // complete in order), then the register set takes tile t+2
+    bf16* vt = Vs[set];
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(vt + vlds[i]) = vrg[set][i];
+    load_tile(t + 2, set);
+
     float x[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) { x[v] = s0[v]; x[4 + v] = s1[v]; }
@@ -164,17 +212,20 @@ void decode_split_kernel(DecodeArgs a) {
     frow = fsum;
 #pragma unroll
     for (int mb = 0; mb < NM; ++mb) {
-      const bf16x8 vop = join_tr(tile_tr4<D, 2>(Vt, 4 * g4 + trow, 2 * mb + tchunk, thalf),
-                                 tile_tr4<D, 2>(Vt, 16 + 4 * g4 + trow, 2 * mb + tchunk, thalf));
+      const bf16x8 vop = join_tr(tile_tr4<D, 2>(vt, 4 * g4 + trow, 2 * mb + tchunk, thalf),
+                                 tile_tr4<D, 2>(vt, 16 + 4 * g4 + trow, 2 * mb + tchunk, thalf));
       oacc[mb] = mfma16(vop, pop, oacc[mb]);
     }
   };
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, K0, V0, K1, V1);
-    if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
+  // Both steps in every trip (an odd last tile after the loop), so that at the top of the
+  // loop tile t's set is always the older one in flight.
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, 0);
+    step(t + 1, 1);
   }
-  wait_vmem();  // the last (empty) copy has landed before the workgroup's LDS is released
+  if (t < n_tiles) step(t, 0);
 
   const float lt = sum4(lrow);
   const float ft = sum4(frow);
@@ -188,37 +239,59 @@ void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup of D/4 threads per (batch, query head): merge the live splits.
+// One wave per (batch, query head), four per workgroup: merge the live splits.  Every
+// lane reads the lse of its splits at once; the partial rows are then read 8 splits at a
+// time (independent loads), each lane owning D/64 consecutive elements of the row.
+constexpr int kCombineWaves = 4;
 template <int D>
-__global__ __launch_bounds__(D / 4) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int E = D / 64;  // elements per lane
   const Problem& p = a.p;
-  const int bh = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (bh >= p.B * p.Hq) return;
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
   const int n_live = (kv_end + a.split_keys - 1) / a.split_keys;
   const float* pl = a.part_lse + (int64_t)bh * a.n_split;
-  const float* po = a.part_o + (int64_t)bh * a.n_split * D;
+  const float* po = a.part_o + (int64_t)bh * a.n_split * D + E * lane;
+  // M = max_c lse_c, L = sum_c exp(lse_c - M) over the live splits
   float M = kNegInf;
-  for (int c = 0; c < n_live; ++c) M = fmaxf(M, pl[c]);
+  for (int c = lane; c < n_live; c += 64) M = fmaxf(M, pl[c]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
   float L = 0.f;
-  const int d0 = threadIdx.x * 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   if (M != kNegInf) {
-    for (int c = 0; c < n_live; ++c) {
-      const float w = expf(pl[c] - M);
-      L += w;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(po + (int64_t)c * D + d0);
-      acc += w * x;
+    for (int c0 = 0; c0 < n_live; c0 += 64) {
+      const int nc = min(64, n_live - c0);
+      const float wl = lane < nc ? expf(pl[c0 + lane] - M) : 0.f;  // weight of split c0 + lane
+      L += wl;
+      for (int c = 0; c < nc; c += 8) {
+        float x[8][E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[u][e] = c + u < nc ? po[(int64_t)(c0 + c + u) * D + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = __shfl(wl, c + u);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);
+        }
+      }
     }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) L += __shfl_xor(L, w);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  bf16x4 out;
+  bf16* orow = reinterpret_cast<bf16*>(a.o) + b * p.o_sb + h * p.o_sh + E * lane;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = (bf16)(acc[e] * inv);
-  bf16* orow = reinterpret_cast<bf16*>(a.o) + b * p.o_sb + h * p.o_sh;
-  *reinterpret_cast<bf16x4*>(orow + d0) = out;
-  if (a.lse && threadIdx.x == 0) a.lse[bh] = (L > 0.f) ? M + logf(L) : kNegInf;
+  for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
+  if (a.lse && lane == 0) a.lse[bh] = (L > 0.f) ? M + logf(L) : kNegInf;
 }
 
 template <int D>
@@ -229,7 +302,9 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.p.B * a.p.Hq), dim3(D / 4), 0, s, a);
+  const int rows = a.p.B * a.p.Hq;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((rows + kCombineWaves - 1) / kCombineWaves),
+                     dim3(64 * kCombineWaves), 0, s, a);
   return hipGetLastError();
 }
 
