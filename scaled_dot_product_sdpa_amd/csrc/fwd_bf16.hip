@@ -31,11 +31,12 @@
 // block b follow.
 //
 // Softmax arithmetic per score: one FMA folds scale * log2(e) and the reference max into
-// the exp2 argument; v_exp_f32; v_cvt_pk_bf16_f32; the bf16 weights are summed with
-// v_dot2 (this sum normalises O, so each output row is an exact convex combination of
-// value rows) and the fp32 weights with one add (this sum gives LSE).  The reference max
-// is only moved when a row's max grows by more than 2^8 (weights stay <= 256, exact in
-// fp32 sums and in bf16 range), so the O rescale runs on a few blocks only.
+// the exp2 argument; v_exp_f32; v_cvt_pk_bf16_f32 (the B operand of the PV product); one
+// add into the fp32 row sum, which both normalises O and gives LSE.  (The PV product
+// weighs V with the bf16-rounded weights, so O's row weights sum to 1 within the bf16
+// rounding of the weights, |error| <= 2^-9 of |O|.)  The reference max is only moved when
+// a row's max grows by more than 2^8 (weights stay <= 256, exact in fp32 sums and in bf16
+// range), so the O rescale runs on a few blocks only.
 //
 // Tiles entirely above the causal diagonal or past the key length are never visited, and
 // a wave works only on the 32-key blocks that some of its rows can see (a prefix of the
@@ -142,16 +143,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   wait_vmem();
   if (n_tiles > 1) load_tile(kBN, Kb[1], Vb[1]);
 
-  // reference max (log2 units), sum of bf16 weights (normalises O), sum of fp32 weights
-  // (gives LSE); both sums are relative to the reference max.
+  // reference max (log2 units) and the sum of the fp32 weights relative to it (normalises
+  // O and gives LSE), kept as two partial sums (even / odd scores) so the adds form two
+  // chains.
   f32x16 oacc[D / 32];
-  // frow is kept as two partial sums (even / odd scores) so the adds form two chains
-  float mref = kNegInf, lrow = 0.f, frow = 0.f, frow2 = 0.f;
+  float mref = kNegInf, frow = 0.f, frow2 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
 
   const float c2 = p.scale_log2;
-  const bf16x2 ones2 = {(bf16)1.f, (bf16)1.f};
   // K operand read: row kb*32 + perm_row(l32), logical chunk 2*kk + hi
   const int krow_l = perm_row(l32);
   // V^T operand (transposing read): row key_base + arow, logical chunk vchunk, half vhalf
@@ -232,7 +232,6 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       const float mnew = need ? mt : mref;
       const float corr = need ? fast_exp2(mref - mnew) : 1.f;
       mref = mnew;
-      lrow *= corr;
       frow *= corr;
       frow2 *= corr;
 #pragma unroll
@@ -259,7 +258,6 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   };
   auto stage_c = [&](int pr, const f32x2 (&t)[8], bf16x8 (&pop)[2]) {
     const bf16x2 e2 = __builtin_convertvector(t[pr], bf16x2);
-    lrow = __builtin_amdgcn_fdot2_f32_bf16(e2, ones2, lrow, false);
     frow += t[pr][0];
     frow2 += t[pr][1];
     pop[pr / 4][2 * (pr % 4)] = e2[0];
@@ -368,11 +366,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) pv_mfma1(j);
 
-  // ---- epilogue: O = O^T / l (0 for empty rows), LSE = ln2 * (mref + log2 f).
-  const float lt = xhalf_sum(lrow);
+  // ---- epilogue: O = O^T / f (0 for empty rows), LSE = ln2 * (mref + log2 f).
   const float ft = xhalf_sum(frow + frow2);
-  const bool rowlive = qrow < q_end && lt > 0.f;
-  const float inv = rowlive ? 1.f / lt : 0.f;
+  const bool rowlive = qrow < q_end && ft > 0.f;
+  const float inv = rowlive ? 1.f / ft : 0.f;
   if (qrow < p.Lq) {
     bf16* orow = ob + (int64_t)qrow * p.o_sl;
 #pragma unroll
