@@ -22,7 +22,7 @@
 //            with dO^T and Q^T read from LDS by ds_read_b64_tr_b16.  Inside a wave the
 //            blocks are software-pipelined: the dV, dK MFMAs of block b-1 run with the P, dS
 //            arithmetic of block b, and the S, dP MFMAs of block b+1 with the rest of it.
-//  3. dq:    query-stationary (the forward's decomposition, 8 waves of 32 rows).  Per
+//  3. dq:    query-stationary (the forward's decomposition, 4 waves of 32 rows).  Per
 //            32-key block of a 64-key K/V tile (three LDS buffers, buffer-load copies):
 //              S^T = K Q^T,  P^T,  dP^T = V dO^T,  dS^T = P^T o (dP^T - D),
 //              dQ^T += K^T dS^T   (K^T via transposing LDS reads).
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kBN = 64;
 
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
   constexpr int NS = D / 16;   // MFMAs of one S^T (or dP^T) block
@@ -433,26 +433,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
   const int rank = r / p.G;
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  // Rows: as in the forward (heavy tiles first, or paired half-tiles for small grids).
-  int wq_lo, row_lo, row_hi;
-  if (CAUSAL && !p.pair_rows) {
-    const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
-    wq_lo = qt * BM + wave * 32;
-    row_lo = qt * BM;
-    row_hi = row_lo + BM;
-  } else if (CAUSAL) {
-    constexpr int HB = BM / 2;
-    const int n_half = (p.Lq + HB - 1) / HB;
-    const int heavy = n_half - 1 - rank;
-    const int mine = wave < NW / 2 ? rank : heavy;
-    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32;
-    row_lo = rank * HB;
-    row_hi = (heavy + 1) * HB;
-  } else {
-    wq_lo = rank * BM + wave * 32;
-    row_lo = rank * BM;
-    row_hi = row_lo + BM;
-  }
+  // Rows: query tile `rank` of BM rows, heavy tiles first on causal grids (as the forward).
+  const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
+  const int wq_lo = qt * BM + wave * 32;  // this wave's first row
+  const int row_lo = qt * BM, row_hi = row_lo + BM;
   const int wq_hi = min(wq_lo + 32, q_end) - 1;
 
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
@@ -691,7 +675,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_seq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;
   constexpr int TILE = kBN * D;
@@ -716,26 +700,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_seq_kernel(BwdArgs a) {
   const int rank = r / p.G;
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  // Rows: as in the forward (heavy tiles first, or paired half-tiles for small grids).
-  int wq_lo, row_lo, row_hi;
-  if (CAUSAL && !p.pair_rows) {
-    const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
-    wq_lo = qt * BM + wave * 32;
-    row_lo = qt * BM;
-    row_hi = row_lo + BM;
-  } else if (CAUSAL) {
-    constexpr int HB = BM / 2;
-    const int n_half = (p.Lq + HB - 1) / HB;
-    const int heavy = n_half - 1 - rank;
-    const int mine = wave < NW / 2 ? rank : heavy;
-    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32;
-    row_lo = rank * HB;
-    row_hi = (heavy + 1) * HB;
-  } else {
-    wq_lo = rank * BM + wave * 32;
-    row_lo = rank * BM;
-    row_hi = row_lo + BM;
-  }
+  // Rows: query tile `rank` of BM rows, heavy tiles first on causal grids (as the forward).
+  const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
+  const int wq_lo = qt * BM + wave * 32;  // this wave's first row
+  const int row_lo = qt * BM, row_hi = row_lo + BM;
   const int wq_hi = min(wq_lo + 32, q_end) - 1;
 
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
@@ -873,12 +841,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_seq_kernel(BwdArgs a) {
   }
 }
 
-// Waves per workgroup of the two main kernels.
+// Waves per workgroup of the two main kernels.  dQ runs two 4-wave workgroups per CU (two
+// waves per SIMD; the workgroups' barriers are independent), measured faster than one
+// 8-wave workgroup on the MHA 1k and padded 2k workloads and equal on GQA 4k.
 template <int D> struct BwdShape;
 // PIPE_DQ: the software-pipelined dQ kernel fits two waves per SIMD (D = 64); at D = 128
 // its registers do not, and the block-sequential form is faster.
-template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; static constexpr bool PIPE_DQ = true; };
-template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 8; static constexpr bool PIPE_DQ = false; };
+template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = true; };
+template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = false; };
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
@@ -892,16 +862,13 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   }
   constexpr int BM = 32 * QNW;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
-  BwdArgs args = a;
-  args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
-  const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
-  if ((stages & kBwdDq) && n_wg > 0) {
+  if ((stages & kBwdDq) && n_qt > 0) {
     if constexpr (BwdShape<D>::PIPE_DQ)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_wg * a.p.B * a.p.Hq),
-                         dim3(64 * QNW), 0, s, args);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
+                         dim3(64 * QNW), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_seq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_wg * a.p.B * a.p.Hq),
-                         dim3(64 * QNW), 0, s, args);
+      hipLaunchKernelGGL((bwd_dq_seq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
+                         dim3(64 * QNW), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -240,8 +240,9 @@ void decode_split_kernel(DecodeArgs a) {
 }
 
 // One wave per (batch, query head), four per workgroup: merge the live splits.  Every
-// lane reads the lse of its splits at once; the partial rows are then read 8 splits at a
-// time (independent loads), each lane owning D/64 consecutive elements of the row.
+// lane reads the lse of its splits at once; the partial rows are then read 16 splits at a
+// time (independent loads, so one memory latency covers up to 16 splits), each lane owning
+// D/64 consecutive elements of the row.
 constexpr int kCombineWaves = 4;
 template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
@@ -270,14 +271,14 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
       const int nc = min(64, n_live - c0);
       const float wl = lane < nc ? expf(pl[c0 + lane] - M) : 0.f;  // weight of split c0 + lane
       L += wl;
-      for (int c = 0; c < nc; c += 8) {
-        float x[8][E];
+      for (int c = 0; c < nc; c += 16) {
+        float x[16][E];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
 #pragma unroll
           for (int e = 0; e < E; ++e) x[u][e] = c + u < nc ? po[(int64_t)(c0 + c + u) * D + e] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const float w = __shfl(wl, c + u);
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[u][e], acc[e]);

@@ -79,30 +79,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 
   const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  // Rows of this workgroup.  Non-causal: query tile `rank` of BM rows.  Causal, large
-  // grids: tile n_qt - 1 - rank (heavy tiles launch first and the scheduler evens the
-  // load).  Causal, grids of about one round (pair_rows): the half-tiles (BM/2 rows)
-  // `rank` and `n_half - 1 - rank`, one per half of the waves, so every workgroup carries
-  // the same causal work (a middle half-tile pairs with nothing).
-  int wq_lo, row_lo, row_hi;  // this wave's first row; the workgroup's row span
-  if (CAUSAL && !p.pair_rows) {
-    const int qt = (p.Lq + BM - 1) / BM - 1 - rank;
-    wq_lo = qt * BM + wave * 32;
-    row_lo = qt * BM;
-    row_hi = row_lo + BM;
-  } else if (CAUSAL) {
-    constexpr int HB = BM / 2;
-    const int n_half = (p.Lq + HB - 1) / HB;
-    const int heavy = n_half - 1 - rank;
-    const int mine = wave < NW / 2 ? rank : heavy;
-    wq_lo = (wave >= NW / 2 && heavy == rank) ? p.Lq : mine * HB + (wave % (NW / 2)) * 32;
-    row_lo = rank * HB;
-    row_hi = (heavy + 1) * HB;
-  } else {
-    wq_lo = rank * BM + wave * 32;
-    row_lo = rank * BM;
-    row_hi = row_lo + BM;
-  }
+  // Rows of this workgroup: query tile `rank` of BM rows; causal grids run the tiles
+  // heavy first (tile n_qt - 1 - rank) and the scheduler evens the load.
+  const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
+  const int wq_lo = qt * BM + wave * 32;  // this wave's first row
+  const int row_lo = qt * BM, row_hi = row_lo + BM;  // the workgroup's row span
   const int wq_hi = min(wq_lo + 32, q_end) - 1;  // this wave's last live row
 
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
@@ -390,23 +371,17 @@ template <int D, int NW, int WPE, bool CAUSAL, bool MASK>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   constexpr int BM = NW * 32;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
-  FwdArgs args = a;
-  // pair half-tiles when whole tiles would give about one round of workgroups
-  args.p.pair_rows = CAUSAL && (int64_t)n_qt * a.p.B * a.p.Hq <= 512;
-  const int n_wg = args.p.pair_rows ? ((a.p.Lq + BM / 2 - 1) / (BM / 2) + 1) / 2 : n_qt;
-  const int grid = n_wg * a.p.B * a.p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, WPE, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, args);
+  const int grid = n_qt * a.p.B * a.p.Hq;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, WPE, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_shape(const FwdArgs& a, hipStream_t s) {
-  // Two waves per SIMD hide each other's LDS and MFMA latencies.  Causal: one workgroup of
-  // 8 waves (256 query rows) per CU, which halves the K/V tile traffic per query row and
-  // suits the heavy-first and paired-row schedules.  Otherwise two independent workgroups
-  // of 4 waves per CU (measured faster on padded batches: the two workgroups' barriers do
-  // not wait for each other, and 128-row tiles waste less past a length).
-  if (CAUSAL) return launch_t<D, 8, 1, CAUSAL, MASK>(a, s);
+  // Two independent workgroups of 4 waves (128 query rows) per CU: two waves per SIMD hide
+  // each other's LDS and MFMA latencies, and the two workgroups' barriers do not wait for
+  // each other (measured faster than one 8-wave workgroup per CU on every workload here:
+  // causal MHA 1k 26.3 -> 23.1 us, causal GQA 4k 318 -> 309 us, padded 2k 217 -> 205 us).
   return launch_t<D, 4, 2, CAUSAL, MASK>(a, s);
 }
 

@@ -22,7 +22,6 @@ struct Problem {
   const int32_t* len_kv;  // may be null
   const void* mask;       // may be null (additive, io dtype)
   int mask_vec;           // mask rows may be read with 16-byte vector loads
-  int pair_rows;          // causal query-stationary kernels: pair light and heavy half-tiles
 };
 
 struct FwdArgs {
