@@ -50,6 +50,19 @@ _DP = ctypes.POINTER(ctypes.c_double)
 _IP = ctypes.POINTER(ctypes.c_int32)
 
 
+# Causal modes (the ``is_causal`` argument): False/0 none, True/1 top-left diagonal,
+# 2 bottom-right diagonal (aligned with the per-batch actual lengths).
+CAUSAL_TOP_LEFT = 1
+CAUSAL_BOTTOM_RIGHT = 2
+
+
+def causal_mode(is_causal) -> int:
+    mode = int(is_causal)
+    if mode not in (0, 1, 2):
+        raise ValueError("is_causal must be False/True (0/1) or 2 (bottom-right)")
+    return mode
+
+
 def _f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -86,7 +99,7 @@ class Oracle:
         p = _Problem()
         p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.Dk, p.Dv = B, Hq, Hkv, Lq, Lk, Dk, Dv
         p.scale = math.nan if scale is None else float(scale)
-        p.is_causal = 1 if is_causal else 0
+        p.is_causal = causal_mode(is_causal)
         m = None
         if mask is not None:
             m = _f64(mask)

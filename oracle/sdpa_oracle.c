@@ -28,6 +28,10 @@
  *    Python API return values (stats = max + ln sum exp(s - max), natural log, fp32).
  *  - torch "flex_attention", parameters (scale defaults to 1/sqrt(E), E = query/key
  *    width; lse has shape (B, Hq, L)).
+ *  - cuDNN "Attention", forward Configurable Options, diagonal masking: with the
+ *    BOTTOM_RIGHT alignment the diagonal ends at the bottom-right corner of the actual
+ *    (per-batch) sequence lengths, and right bound 0 masks every column past it, so query
+ *    i sees key j iff j <= i + (len_kv - len_q).
  *
  * Readings where the pages are silent: a query row at or past len_q is empty (O = 0,
  * LSE = -inf, no gradient); an empty or fully blocked row has LSE = -inf (ln 0);
@@ -49,6 +53,7 @@ static int check_problem(const oracle_problem* p, const int32_t* len_q, const in
     return -1;
   if (p->Hq % p->Hkv != 0) return -1;
   if (isinf(p->scale)) return -1;
+  if (p->is_causal < 0 || p->is_causal > 2) return -1;
   for (int b = 0; b < p->B; ++b) {
     if (len_q && (len_q[b] < 0 || len_q[b] > p->Lq)) return -1;
     if (len_kv && (len_kv[b] < 0 || len_kv[b] > p->Lk)) return -1;
@@ -64,8 +69,9 @@ static double resolve_scale(const oracle_problem* p) {
 /*
  * One query row (b, h, i): fills P[0..Lk) with the attention weights and returns the
  * row's LSE through *lse.  Returns 0, or -2 for an undefined mask entry.
- *   allowed(j) = (j < len_kv[b]) and (not causal or j <= i), and the row itself must
- *   satisfy i < len_q[b];
+ *   allowed(j) = (j < len_kv[b]) and (not causal or j <= i + off), and the row itself
+ *   must satisfy i < len_q[b]; off = 0 for the top-left diagonal and len_kv[b] - len_q[b]
+ *   for the bottom-right one;
  *   s_j = alpha * (q_i . k_g,j) + M[b,h,i,j]   if allowed, else -inf;
  *   m = max_j s_j; a row with m = -inf (or an empty row) has P = 0 and LSE = -inf;
  *   otherwise P_j = exp(s_j - m) / sum_t exp(s_t - m) and LSE = m + ln sum_t exp(s_t - m).
@@ -76,12 +82,14 @@ static int row_weights(const oracle_problem* p, double alpha, const double* q, c
   const int G = p->Hq / p->Hkv;
   const int g = h / G;
   const int kv_len = len_kv ? len_kv[b] : p->Lk;
-  const int row_valid = len_q ? (i < len_q[b]) : 1;
+  const int q_len = len_q ? len_q[b] : p->Lq;
+  const int row_valid = i < q_len;
+  const int off = (p->is_causal == 2) ? kv_len - q_len : 0;
   const double* qi = q + IDX4(b, h, i, 0, p->Hq, p->Lq, p->Dk);
 
   double m = -INFINITY;
   for (int j = 0; j < p->Lk; ++j) {
-    int allowed = row_valid && j < kv_len && (!p->is_causal || j <= i);
+    int allowed = row_valid && j < kv_len && (!p->is_causal || j <= i + off);
     if (!allowed) {
       s[j] = -INFINITY;
       continue;

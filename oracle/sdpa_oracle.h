@@ -29,7 +29,8 @@ typedef struct {
   int32_t B, Hq, Hkv, Lq, Lk, Dk, Dv;
   int64_t mask_stride[4];
   double scale;      /* NaN selects the default 1/sqrt(Dk) */
-  int32_t is_causal; /* top-left: key j visible to query i iff j <= i */
+  int32_t is_causal; /* 0: none; 1 top-left: key j visible to query i iff j <= i;
+                        2 bottom-right: iff j <= i + (len_kv - len_q) of the batch */
 } oracle_problem;
 
 int oracle_sdpa_forward(const oracle_problem* p, const double* q, const double* k,

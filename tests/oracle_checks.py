@@ -407,6 +407,101 @@ def check_torch_library(orc):
         assert np.abs(tv.grad.numpy() - dv).max() <= 1e-10
 
 
+# ---------------------------------------------------------------------------------
+# Bottom-right causal alignment (cuDNN "Attention", forward Configurable Options,
+# diagonal masking: BOTTOM_RIGHT with right bound 0)
+# ---------------------------------------------------------------------------------
+def check_bottom_right_chunked_prefill(orc):
+    """The last c queries of a top-left causal problem over n tokens equal the
+    bottom-right causal problem of those c queries against all n keys (a prefill chunk
+    against its KV cache): same O, LSE and dQ, and the same dK, dV when the other rows
+    carry no output gradient.  Per batch, with lengths: the chunk is the last len_q rows
+    of the batch's len_kv tokens."""
+    rng = _rng(401)
+    B, Hq, Hkv, n, c, Dk, Dv = 3, 4, 2, 11, 4, 5, 3
+    q = _randn(rng, B, Hq, n, Dk)
+    k = _randn(rng, B, Hkv, n, Dk)
+    v = _randn(rng, B, Hkv, n, Dv)
+    dO = _randn(rng, B, Hq, n, Dv)
+    # full sequences: the last c rows
+    o_full, l_full = orc.forward(q, k, v, is_causal=True)
+    dO_c = np.zeros_like(dO)
+    dO_c[:, :, n - c:] = dO[:, :, n - c:]
+    gq_f, gk_f, gv_f, _ = orc.backward(q, k, v, dO_c, is_causal=True)
+    o, l = orc.forward(q[:, :, n - c:], k, v, is_causal=2)
+    gq, gk, gv, _ = orc.backward(q[:, :, n - c:], k, v, dO[:, :, n - c:], is_causal=2)
+    assert np.abs(o - o_full[:, :, n - c:]).max() <= 1e-12
+    assert np.abs(l - l_full[:, :, n - c:]).max() <= 1e-12
+    assert np.abs(gq - gq_f[:, :, n - c:]).max() <= 1e-12
+    assert np.abs(gk - gk_f).max() <= 1e-12 and np.abs(gv - gv_f).max() <= 1e-12
+    # per-batch lengths: batch b has len_kv tokens and its chunk is the last len_q of them
+    lk = np.array([11, 7, 3], np.int32)
+    lq = np.array([4, 2, 3], np.int32)
+    qc = np.zeros((B, Hq, c, Dk))
+    for b in range(B):
+        qc[b, :, :lq[b]] = q[b, :, lk[b] - lq[b]:lk[b]]
+    o, l = orc.forward(qc, k, v, is_causal=2, len_q=lq, len_kv=lk)
+    for b in range(B):
+        ob, lb = orc.forward(q[b:b + 1, :, :lk[b]], k[b:b + 1, :, :lk[b]], v[b:b + 1, :, :lk[b]],
+                             is_causal=True)
+        assert np.abs(o[b, :, :lq[b]] - ob[0, :, lk[b] - lq[b]:]).max() <= 1e-12
+        assert np.abs(l[b, :, :lq[b]] - lb[0, :, lk[b] - lq[b]:]).max() <= 1e-12
+        assert np.all(o[b, :, lq[b]:] == 0) and np.all(np.isneginf(l[b, :, lq[b]:]))
+
+
+def check_bottom_right_is_shifted_tril(orc):
+    """Bottom-right causal equals an additive mask from numpy's tril with the diagonal
+    offset Lk - Lq (the diagonal ends in the bottom-right corner), bit for bit, for Lq < Lk,
+    Lq = Lk (where it equals top-left) and Lq > Lk (whose first Lq - Lk rows see no key)."""
+    for Lq, Lk in ((4, 7), (6, 6), (7, 4)):
+        c = _case(411 + Lq, Lq=Lq, Lk=Lk, mask=False)
+        tril = np.tril(np.ones((Lq, Lk), bool), k=Lk - Lq)
+        m = np.where(tril, 0.0, -np.inf).reshape(1, 1, Lq, Lk)
+        o1, l1 = _fwd(orc, c, is_causal=2)
+        o2, l2 = _fwd(orc, c, mask=m)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        g1 = _bwd(orc, c, is_causal=2)
+        g2 = _bwd(orc, c, mask=m)
+        for a, b in zip(g1, g2):
+            assert np.array_equal(a, b)
+        if Lq == Lk:
+            o3, l3 = _fwd(orc, c, is_causal=True)
+            assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+        if Lq > Lk:
+            assert np.all(o1[:, :, :Lq - Lk] == 0) and np.all(np.isneginf(l1[:, :, :Lq - Lk]))
+    # one query row against its whole cache: every key is visible (decode)
+    c = _case(419, Lq=1, Lk=9, mask=False)
+    o1, l1 = _fwd(orc, c, is_causal=2)
+    o2, l2 = _fwd(orc, c, is_causal=False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def check_bottom_right_torch(orc):
+    """Library pin: torch's CPU fp64 scaled_dot_product_attention with its lower-right
+    causal bias (torch.nn.attention.bias.causal_lower_right) and autograd, Lq < Lk, GQA."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+
+    for seed, Lq, Lk, Hq, Hkv in ((431, 5, 9, 4, 2), (432, 3, 3, 2, 2)):
+        c = _case(seed, Lq=Lq, Lk=Lk, Hq=Hq, Hkv=Hkv, mask=False)
+        tq = torch.tensor(c["q"], requires_grad=True)
+        tk = torch.tensor(c["k"], requires_grad=True)
+        tv = torch.tensor(c["v"], requires_grad=True)
+        bias = causal_lower_right(Lq, Lk)._materialize()
+        tm = torch.zeros(Lq, Lk, dtype=torch.float64).masked_fill(~bias, float("-inf"))
+        G = Hq // Hkv
+        out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1),
+                                             attn_mask=tm, scale=0.7)
+        out.backward(torch.tensor(c["dO"]))
+        o, _ = _fwd(orc, c, is_causal=2, scale=0.7)
+        dq, dk, dv, _ = _bwd(orc, c, is_causal=2, scale=0.7)
+        assert np.abs(out.detach().numpy() - o).max() <= 1e-10
+        assert np.abs(tq.grad.numpy() - dq).max() <= 1e-10
+        assert np.abs(tk.grad.numpy() - dk).max() <= 1e-10
+        assert np.abs(tv.grad.numpy() - dv).max() <= 1e-10
+
+
 ALL_CHECKS = [
     check_hand_forward, check_hand_lse, check_hand_backward, check_rowsum_identity,
     check_rows_sum_to_one, check_key_shift_invariance, check_gradcheck,
@@ -414,4 +509,6 @@ ALL_CHECKS = [
     check_masked_keys, check_fully_masked_row, check_large_scores, check_default_scale,
     check_causal_is_tril, check_gqa_is_repeat_interleave, check_score_variance,
     check_single_key, check_identical_keys, check_lengths_are_masks, check_torch_library,
+    check_bottom_right_chunked_prefill, check_bottom_right_is_shifted_tril,
+    check_bottom_right_torch,
 ]

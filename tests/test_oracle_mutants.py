@@ -39,7 +39,11 @@ MUTANTS = {
     "gqa_modulo_map": [("  const int g = h / G;\n", "  const int g = h % p->Hkv;\n"),
                        ("row_output(p, v, P, b, h / G, o + r * p->Dv);",
                         "row_output(p, v, P, b, h % p->Hkv, o + r * p->Dv);")],
-    "causal_strict": [("(!p->is_causal || j <= i)", "(!p->is_causal || j < i)")],
+    "causal_strict": [("(!p->is_causal || j <= i + off)", "(!p->is_causal || j < i + off)")],
+    # bottom-right alignment: offset with the wrong sign, or from the padded shapes
+    # instead of the batch's actual lengths
+    "bottom_right_sign": [("? kv_len - q_len : 0;", "? q_len - kv_len : 0;")],
+    "bottom_right_padded_shapes": [("? kv_len - q_len : 0;", "? p->Lk - p->Lq : 0;")],
     "dv_uses_dS": [("for (int t = 0; t < p->Dv; ++t) dvj[t] += P[j] * dOi[t];",
                     "for (int t = 0; t < p->Dv; ++t) dvj[t] += dS * dOi[t];")],
     "len_kv_inclusive": [("j < kv_len &&", "j <= kv_len &&")],
