@@ -17,7 +17,12 @@
  * Which keys a row may attend to (all conditions at once):
  *  - additive mask: an entry of -inf blocks the pair, a finite entry is added as a bias
  *    (Lucid ScaledDotProductAttentionBackward, Notes; cuDNN "Attention", Bias mask);
- *  - is_causal: top-left aligned, key j is visible to query i iff j <= i
+ *  - is_causal = 1 (SDPA_CAUSAL_TOP_LEFT): key j is visible to query i iff j <= i;
+ *    is_causal = 2 (SDPA_CAUSAL_BOTTOM_RIGHT): iff j <= i + (len_kv - len_q), with the
+ *    batch's actual lengths, so the diagonal ends in the bottom-right corner (cuDNN
+ *    "Attention", forward Configurable Options, diagonal masking: BOTTOM_RIGHT alignment
+ *    with right bound 0 -- a prefill chunk against its KV cache; rows that end up with no
+ *    key are empty);
  *    ("Understanding PyTorch Scaled Dot-Product Attention" section 3, tril);
  *  - per-batch lengths: keys j >= seq_lens_kv[b] are blocked and query rows
  *    i >= seq_lens_q[b] are empty (cuDNN "Attention", Support Matrix glossary note on
@@ -67,6 +72,8 @@ typedef enum {
 } sdpa_status;
 
 typedef enum { SDPA_DTYPE_F32 = 0, SDPA_DTYPE_BF16 = 1 } sdpa_dtype;
+/* values of sdpa_problem.is_causal */
+typedef enum { SDPA_CAUSAL_NONE = 0, SDPA_CAUSAL_TOP_LEFT = 1, SDPA_CAUSAL_BOTTOM_RIGHT = 2 } sdpa_causal;
 
 typedef struct {
   int32_t dtype;                    /* sdpa_dtype */
@@ -77,7 +84,7 @@ typedef struct {
   int64_t o_stride[3];              /* of o (and dO) */
   int64_t mask_stride[3];           /* (b, h, i) of the mask; keys have unit stride */
   float scale;                      /* NaN selects 1/sqrt(Dqk); else finite and > 0 */
-  int32_t is_causal;                /* nonzero: top-left causal */
+  int32_t is_causal;                /* 0 none, 1 top-left, 2 bottom-right (see above) */
 } sdpa_problem;
 
 /*

@@ -162,6 +162,20 @@ def _vp(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ``is_causal`` values (the C ABI's sdpa_causal): False/0 none, True/1 top-left diagonal
+# (key j visible to query i iff j <= i), 2 bottom-right diagonal (iff j <= i + len_kv - len_q
+# of the batch: a prefill chunk against its KV cache).
+CAUSAL_TOP_LEFT = 1
+CAUSAL_BOTTOM_RIGHT = 2
+
+
+def causal_code(is_causal) -> int:
+    code = int(is_causal)
+    if code not in (0, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT):
+        raise ValueError("sdpa: is_causal must be False/True (0/1) or 2 (bottom-right)")
+    return code
+
+
 def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
     B, Hq, Lq, Dqk = q.shape
     Bk, Hkv, Lk, Dk2 = k.shape
@@ -180,7 +194,7 @@ def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
     p.o_stride[:] = o_strides
     p.mask_stride[:] = mask_strides
     p.scale = math.nan if scale is None else float(scale)
-    p.is_causal = 1 if is_causal else 0
+    p.is_causal = causal_code(is_causal)
     return p
 
 

@@ -18,10 +18,11 @@ constexpr int kTpb = 64;
 struct RowCtx {
   int b, h, g, i;
   int q_end, kv_end, stop;  // stop: keys [0, stop) are candidates
+  int coff;                 // causal diagonal offset: key j visible iff j <= i + coff
 };
 
 __device__ __forceinline__ bool key_visible(const Problem& p, const RowCtx& r, int j) {
-  return j < r.kv_end && r.i < r.q_end && (!p.causal || j <= r.i);
+  return j < r.kv_end && r.i < r.q_end && (!p.causal || j <= r.i + r.coff);
 }
 
 __device__ __forceinline__ RowCtx row_ctx(const Problem& p, int64_t row) {
@@ -32,7 +33,8 @@ __device__ __forceinline__ RowCtx row_ctx(const Problem& p, int64_t row) {
   r.g = r.h / p.G;
   r.q_end = p.len_q ? min(p.len_q[r.b], p.Lq) : p.Lq;
   r.kv_end = p.len_kv ? min(p.len_kv[r.b], p.Lk) : p.Lk;
-  r.stop = (r.i < r.q_end) ? (p.causal ? min(r.kv_end, r.i + 1) : r.kv_end) : 0;
+  r.coff = causal_offset(p.causal, r.q_end, r.kv_end);
+  r.stop = (r.i < r.q_end) ? (p.causal ? max(0, min(r.kv_end, r.i + 1 + r.coff)) : r.kv_end) : 0;
   return r;
 }
 
@@ -176,7 +178,8 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
     dv[t] = 0.f;
   }
   if (j < kv_end) {
-    const int i_begin = p.causal ? j : 0;
+    // first query row that sees key j (row i sees it iff i >= j - offset)
+    const int i_begin = p.causal ? max(0, j - causal_offset(p.causal, q_end, kv_end)) : 0;
     for (int hh = 0; hh < p.G; ++hh) {
       const int h = g * p.G + hh;
       for (int i = i_begin; i < q_end; ++i) {

@@ -127,7 +127,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Query tiles that can see any key of this workgroup; the G heads of the group in turn.
   const int kstop = min(kv_end, j0 + KT);
-  const int qt_begin = CAUSAL ? j0 / kQT : 0;
+  // first query tile with a row that sees key j0 (row i sees it iff i >= j0 - coff)
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;
+  const int qt_begin = CAUSAL ? max(j0 - coff, 0) / kQT : 0;
   const int qt_end = (j0 < kstop) ? (q_end + kQT - 1) / kQT : 0;
   const int n_q_tiles = qt_end > qt_begin ? qt_end - qt_begin : 0;
   const int total = n_q_tiles * p.G;
@@ -253,12 +255,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 < jw + 31);
+    const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 + coff < jw + 31);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int qi = r0 + 16 * hi + v;
-        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi);
+        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff);
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -446,12 +448,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
   const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
 
   int kv_stop = kv_end;
-  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;  // diagonal offset
+  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
   int vis_stop = wq_lo < q_end ? kv_stop : 0;
-  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1);
-  const int nvis = (vis_stop + 31) / 32;  // 32-key blocks this wave works on (a prefix)
+  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1 + coff);
+  const int nvis = vis_stop > 0 ? (vis_stop + 31) / 32 : 0;  // 32-key blocks this wave works on (a prefix)
 
   TileCopy<kBN, D, NW> kcopy, vcopy;
   kcopy.init(p.k_sl, wave, lane);
@@ -546,12 +549,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
           mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
       }
     }
-    const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo) || (wq_lo + 32 > q_end);
+    const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo + coff) || (wq_lo + 32 > q_end);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi);
+        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff);
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -713,7 +716,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
 
   int kv_stop = kv_end;
-  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;  // diagonal offset
+  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
 
@@ -753,12 +757,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
-    const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo) ||
+    const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo + coff) ||
                            (wq_lo + 32 > q_end);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key_lo = j0 + kb * 32;
-      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi))) continue;
+      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi + coff))) continue;
       // S^T = K Q^T and dP^T = V dO^T for keys key_lo + perm
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
@@ -800,7 +804,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
           float x = fmaf(s_acc[v], c2, MASK ? mv[v] - lse2 : -lse2);
           if (partial_t) {
             const int key = key0 + v;
-            const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi);
+            const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff);
             x = ok ? x : kNegInf;
           }
           const float pv = fast_exp2(x);

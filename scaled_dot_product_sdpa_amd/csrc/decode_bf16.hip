@@ -79,7 +79,9 @@ void decode_split_kernel(DecodeArgs a) {
   const int g = bg % p.Hkv;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
   const int k0 = c * a.split_keys;
-  if (k0 >= kv_end) return;  // the combine reads only splits that hold keys
+  // the combine reads only splits that hold keys, and none of a batch whose query row is
+  // past its length (an empty row)
+  if (k0 >= kv_end || (p.len_q && p.len_q[b] < 1)) return;
   const int k1 = min(k0 + a.split_keys, kv_end);
   const int n_tiles = (k1 - k0 + kDT - 1) / kDT;
 
@@ -254,7 +256,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
   const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  const int n_live = (kv_end + a.split_keys - 1) / a.split_keys;
+  const bool row_live = !p.len_q || p.len_q[b] >= 1;  // else the row is empty: O = 0, LSE = -inf
+  const int n_live = row_live ? (kv_end + a.split_keys - 1) / a.split_keys : 0;
   const float* pl = a.part_lse + (int64_t)bh * a.n_split;
   const float* po = a.part_o + (int64_t)bh * a.n_split * D + E * lane;
   // M = max_c lse_c, L = sum_c exp(lse_c - M) over the live splits

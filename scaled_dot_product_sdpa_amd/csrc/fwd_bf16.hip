@@ -95,13 +95,14 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 
   // Keys this tile of queries can see.
   int kv_stop = kv_end;
-  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end));
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;  // diagonal offset
+  if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
   // 32-key blocks this wave works on: a prefix of the keys.
   int vis_stop = wq_lo < q_end ? kv_stop : 0;
-  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1);
-  const int nvis = (vis_stop + 31) / 32;
+  if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1 + coff);
+  const int nvis = vis_stop > 0 ? (vis_stop + 31) / 32 : 0;
 
   // ---- K/V tiles: HBM -> LDS (rows past kv_stop arrive as zeros).
   TileCopy<kBN, D, NW> kcopy, vcopy;
@@ -191,13 +192,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], c2, mv[v] * kLog2e);
     }
-    const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo) ||
+    const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo + coff) ||
                          (wq_lo + 32 > q_end);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow);
+        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow + coff);
         x[v] = ok ? x[v] : kNegInf;
       }
     }

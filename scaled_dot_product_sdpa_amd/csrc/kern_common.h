@@ -223,6 +223,13 @@ __device__ __forceinline__ void xcd_item(int bid, int NG, int M, int inner, bool
   }
 }
 
+// Offset of the causal diagonal of a batch: query i sees key j iff j <= i + offset.  0 for
+// the top-left diagonal; len_kv - len_q for the bottom-right one, whose diagonal ends at
+// the last (query, key) pair of the batch's actual lengths.
+__device__ __forceinline__ int causal_offset(int causal, int q_end, int kv_end) {
+  return causal == 2 ? kv_end - q_end : 0;
+}
+
 // Zero BYTES bytes of LDS at dst (16-byte aligned) with the NT threads of the workgroup.
 // The pipelined kernels run a block's trailing MFMAs one block late, so their first block
 // multiplies zero weights by the previous buffer's rows; those rows must hold finite values

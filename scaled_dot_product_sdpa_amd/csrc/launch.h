@@ -17,7 +17,7 @@ struct Problem {
   int64_t m_sb, m_sh, m_si;
   float scale;       // resolved scale
   float scale_log2;  // scale * log2(e)
-  int causal;
+  int causal;  // 0 none, 1 top-left, 2 bottom-right diagonal
   const int32_t* len_q;   // may be null
   const int32_t* len_kv;  // may be null
   const void* mask;       // may be null (additive, io dtype)

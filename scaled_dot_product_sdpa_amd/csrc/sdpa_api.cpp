@@ -54,6 +54,10 @@ sdpa_status check_problem(const sdpa_problem* p) {
                 p->B, p->Hq, p->Hkv, p->Lq, p->Lk, p->Dqk, p->Dv);
   if (p->Hq % p->Hkv != 0)
     return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->is_causal != SDPA_CAUSAL_NONE && p->is_causal != SDPA_CAUSAL_TOP_LEFT &&
+      p->is_causal != SDPA_CAUSAL_BOTTOM_RIGHT)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "is_causal must be 0, 1 (top-left) or 2 (bottom-right), got %d",
+                p->is_causal);
   if (!std::isnan(p->scale) && !(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be NaN (default) or finite and > 0");
   if (p->Dqk != p->Dv)
@@ -92,9 +96,12 @@ sdpa_status check_problem(const sdpa_problem* p) {
   return SDPA_OK;
 }
 
+// One query row per head: a bottom-right diagonal leaves every key of the row visible
+// (j <= 0 + len_kv - 1), so that case is the non-causal decode too.
 bool use_decode(const sdpa_problem* p, bool has_mask) {
-  return p->dtype == SDPA_DTYPE_BF16 && p->Lq == 1 && !p->is_causal && !has_mask &&
-         p->Hq / p->Hkv <= 16;
+  return p->dtype == SDPA_DTYPE_BF16 && p->Lq == 1 &&
+         (p->is_causal == SDPA_CAUSAL_NONE || p->is_causal == SDPA_CAUSAL_BOTTOM_RIGHT) &&
+         !has_mask && p->Hq / p->Hkv <= 16;
 }
 
 sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_t* lq,
@@ -109,7 +116,7 @@ sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_
   k.m_sb = p->mask_stride[0]; k.m_sh = p->mask_stride[1]; k.m_si = p->mask_stride[2];
   k.scale = std::isnan(p->scale) ? 1.0f / std::sqrt((float)p->Dqk) : p->scale;
   k.scale_log2 = k.scale * 1.4426950408889634f;
-  k.causal = p->is_causal ? 1 : 0;
+  k.causal = p->is_causal;
   k.len_q = lq;
   k.len_kv = lk;
   k.mask = mask;

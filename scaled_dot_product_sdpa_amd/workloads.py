@@ -27,10 +27,12 @@ class Workload:
     Lk: int
     D: int
     dtype: str                 # "f32" or "bf16"
-    causal: bool
+    causal: int                # 0 none, 1 (True) top-left, 2 bottom-right diagonal
     scale: float
     seed: int
-    lens: str = "none"         # "none" | "qkv" (same length for q and kv) | "kv"
+    lens: str = "none"         # "none" | "qkv" (same length for q and kv) | "kv" | "chunk"
+                               # (kv lengths, then query lengths <= min(Lq, len_kv): a chunk
+                               # of queries at the end of each sequence)
     len_range: tuple = (0, 0)  # inclusive range of the uniform length draw
     mask: str = "none"         # "none" | "padded_random" (B,1,Lq,Lk) additive mask
     mask_drop: float = 0.0     # Bernoulli rate of extra -inf entries inside the lengths
@@ -86,6 +88,10 @@ def make_inputs(w: Workload, device="cpu") -> dict:
         len_kv = lens.clone()
         if w.lens == "qkv":
             len_q = lens.clone()
+        elif w.lens == "chunk":
+            u = torch.rand(w.B, **kw)
+            cap = torch.clamp(lens, max=w.Lq).to(torch.float32)
+            len_q = torch.minimum(torch.floor(u * (cap + 1)), cap).to(torch.int32)
 
     mask = None
     if w.mask == "padded_random":

@@ -81,6 +81,8 @@ def _bwd(lib, p, lse=FAKE, dq=FAKE, ws=FAKE, nws=1 << 20, stage="sdpa_backward")
     (lambda p: p.o_stride.__setitem__(2, 32), SDPA_ERR_INVALID_ARGUMENT),  # rows overlap
     (lambda p: p.v_stride.__setitem__(2, 1 << 24), SDPA_ERR_UNSUPPORTED),  # 64-row tile > 2 GiB
     (lambda p: p.mask_stride.__setitem__(2, 1 << 24), SDPA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "is_causal", 3), SDPA_ERR_INVALID_ARGUMENT),    # 0, 1 or 2 only
+    (lambda p: setattr(p, "is_causal", -1), SDPA_ERR_INVALID_ARGUMENT),
 ])
 def test_forward_rejects(lib, mutate, status):
     p = _problem()
@@ -104,9 +106,12 @@ def test_decode_workspace(lib):
     assert need > 0
     assert _fwd(lib, p, ws=FAKE, nws=need - 1) == SDPA_ERR_WORKSPACE_TOO_SMALL
     assert _fwd(lib, p, ws=None, nws=need) == SDPA_ERR_WORKSPACE_TOO_SMALL
-    # a causal single-query problem runs on the prefill kernel and needs none
+    # a top-left causal single-query problem runs on the prefill kernel and needs none; a
+    # bottom-right one sees its whole cache, so it is a decode and needs the same workspace
     pc = _problem(B=64, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128, causal=1)
     assert lib.sdpa_forward_workspace_bytes(ctypes.byref(pc)) == 0
+    pb = _problem(B=64, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128, causal=2)
+    assert lib.sdpa_forward_workspace_bytes(ctypes.byref(pb)) == need
 
 
 def test_prefill_and_backward_workspace(lib):

@@ -40,6 +40,16 @@ CASES = {
     # the same inputs, mask only (no length arrays)
     "padded_mask_only_d128": W["padded_mask_2k"].scaled(B=3, Hq=2, Hkv=2, Lq=260, Lk=260,
                                                         len_range=(64, 260), seed=16, lens="none_keep"),
+    # bottom-right causal diagonal (a chunk of queries against its KV cache): Lq < Lk,
+    # per-batch query and key lengths, Lq > Lk (leading rows see no key), with a mask, fp32
+    "chunk_br_d64": W["mha_causal_1k"].scaled(B=2, Hq=3, Hkv=3, Lq=200, Lk=333, causal=2, seed=40),
+    "chunk_br_gqa_lens_d128": W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=2, Lq=150, Lk=400, causal=2,
+                                                        lens="chunk", len_range=(100, 400), seed=41),
+    "br_lq_gt_lk_d128": W["gqa_causal_4k"].scaled(B=1, Hq=2, Hkv=1, Lq=300, Lk=200, causal=2, seed=42),
+    "br_mask_lens_d128": W["padded_mask_2k"].scaled(B=2, Hq=2, Hkv=2, Lq=200, Lk=260, causal=2,
+                                                    lens="chunk", len_range=(64, 260), seed=43),
+    "fp32_br_gqa": W["tiny_fp32"].scaled(B=2, Hq=4, Hkv=2, Lq=40, Lk=70, D=64, causal=2,
+                                         lens="chunk", len_range=(30, 70), seed=44),
     # decode (Lq = 1) against a KV cache with lengths and NaN-poisoned padding
     "decode_gqa_d128": W["gqa_decode_8k"].scaled(B=4, Hq=8, Hkv=2, Lk=1100, len_range=(1, 1100), seed=17),
     "decode_mha_d64": W["gqa_decode_8k"].scaled(B=3, Hq=4, Hkv=4, Lk=700, D=64, len_range=(30, 700), seed=18),

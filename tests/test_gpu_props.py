@@ -194,3 +194,44 @@ def test_stale_lds_does_not_leak(D):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.isfinite(a).all() and torch.equal(a, b)
+
+
+def test_bottom_right_chunk_equals_full_causal_rows():
+    """A prefill chunk (the last c queries against the whole KV cache, bottom-right
+    diagonal) reproduces the last c rows of the top-left causal forward over the full
+    sequence, and their dQ; dK, dV equal the full backward's when the other rows carry no
+    output gradient."""
+    banner("bottom-right chunk == rows of the full causal problem")
+    for D, n, c, Hq, Hkv in ((64, 700, 180, 4, 4), (128, 520, 130, 8, 2)):
+        w = MID.scaled(B=2, Hq=Hq, Hkv=Hkv, Lq=n, Lk=n, D=D, seed=50 + D)
+        d = to_dev(make_inputs(w))
+        o_f, l_f = gpu_forward(d)
+        dO_c = d["dO"].clone()
+        dO_c[:, :, : n - c] = 0
+        gq_f, gk_f, gv_f = gpu_backward(dict(d, dO=dO_c), o_f, l_f)
+        dc = dict(d, q=d["q"][:, :, n - c:].contiguous(), dO=d["dO"][:, :, n - c:].contiguous(),
+                  is_causal=2)
+        o, l = gpu_forward(dc)
+        gq, gk, gv = gpu_backward(dc, o, l)
+        assert (o.float() - o_f[:, :, n - c:].float()).abs().max().item() <= 1e-2
+        assert (l - l_f[:, :, n - c:]).abs().max().item() <= 1e-4
+        assert rel_fro(f64(gq), f64(gq_f[:, :, n - c:])) <= 1e-2
+        assert rel_fro(f64(gk), f64(gk_f)) <= 1e-2 and rel_fro(f64(gv), f64(gv_f)) <= 1e-2
+
+
+@pytest.mark.parametrize("causal", [0, 2])
+def test_decode_with_query_lengths(orc, causal):
+    """Single-query decode (non-causal, or bottom-right, which sees the whole cache) with a
+    query-length array: batches of query length 0 give O = 0 and LSE = -inf; the others
+    match the oracle."""
+    banner(f"decode with query lengths (is_causal={causal})")
+    w = WORKLOADS["gqa_decode_8k"].scaled(B=4, Hq=8, Hkv=2, Lk=900, len_range=(100, 900),
+                                          causal=causal, seed=55)
+    inp = make_inputs(w)
+    inp["len_q"] = torch.tensor([1, 0, 1, 0], dtype=torch.int32)
+    d = to_dev(inp)
+    o, lse = gpu_forward(d)
+    assert torch.all(o[1] == 0) and torch.all(o[3] == 0)
+    assert torch.all(torch.isneginf(lse[1])) and torch.all(torch.isneginf(lse[3]))
+    o_ref, lse_ref = oracle_forward(orc, inp)
+    compare_forward(inp, o, lse, o_ref, lse_ref)
