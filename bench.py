@@ -140,6 +140,25 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
         nbytes = lk * w.Hkv * 2 * w.D * 2 + w.B * w.Hq * (2 * w.D * 2 + 4)
         gbs = nbytes / (t["fwd"] * 1e-3) / 1e9
         res.update(ms={"fwd": t["fwd"]}, bytes=nbytes, GBps=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
+        if inp["len_kv"] is not None and w.dtype == "bf16":
+            # the same cache stored in 64-key pages in a random page order (paged decode)
+            from scaled_dot_product_sdpa_amd import PagedDecodeCall
+            ps = 64
+            max_pages = (w.Lk + ps - 1) // ps
+            g = torch.Generator(device="cuda").manual_seed(w.seed)
+            table = torch.randperm(w.B * max_pages, generator=g, device="cuda").view(w.B, max_pages)
+            pages = lambda t: t.new_empty(w.B * max_pages, w.Hkv, ps, w.D).index_copy_(
+                0, table.reshape(-1),
+                t.view(w.B, w.Hkv, max_pages, ps, w.D).transpose(1, 2).reshape(-1, w.Hkv, ps, w.D))
+            pc = PagedDecodeCall(inp["q"][:, :, 0], pages(inp["k"]), pages(inp["v"]),
+                                 table.to(torch.int32), inp["len_kv"], inp["scale"])
+            pc.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(pc.o, fc.o[:, :, 0]), "paged decode differs from the contiguous one"
+            t_p = kernel_ms(timer, pc.launch, reps=10, iters=iters)
+            res["ms"]["paged_fwd"] = t_p
+            res["GBps_paged"] = nbytes / (t_p * 1e-3) / 1e9
+            res["paged"] = {"page_size": ps, "page_order": "random permutation"}
         return res, inp, fc, None
     pairs = visible_pairs(w, inp["len_q"], inp["len_kv"])
     fl = flops(w, pairs)

@@ -154,6 +154,45 @@ sdpa_status sdpa_backward_dq(const sdpa_problem* p, const void* q, const void* k
                              const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Single-query decode against a paged KV cache.  The operation is that of sdpa_forward with
+ * Lq = 1, no mask, not causal (equivalently the bottom-right diagonal, which leaves every
+ * cached key visible), with per-batch KV lengths; only the cache's storage differs.  The
+ * keys and values of sequence b live in fixed-size pages of two containers, located through
+ * a page table (cuDNN "Attention", forward Configurable Options, Paged attention, offset
+ * calculation):
+ *   K_cache[b, h, s, d] = k_pages[page_table[b, s / page_size], h, s mod page_size, d]
+ *   V_cache[b, h, s, d] = v_pages[page_table[b, s / page_size], h, s mod page_size, d]
+ * for s < seq_lens_kv[b].
+ *   q (B, Hq, D), o (B, Hq, D) bf16 with (b, h) strides; lse (B, Hq) fp32 or NULL;
+ *   k_pages, v_pages (num_pages, Hkv, page_size, D) bf16 with (page, h, s) strides;
+ *   page_table (B, max_pages) int32 device array, row-major; seq_lens_kv (B) int32 device
+ *   array, 0 <= len <= max_pages * page_size.
+ * Device-resident preconditions are not checked: a page-table entry outside
+ * [0, num_pages) is clamped into it (the result is then meaningless, but no memory outside
+ * the containers is read).  A length of 0 gives O = 0, LSE = -inf.  Bitwise repeatable,
+ * and bitwise equal to sdpa_forward on the same cache stored contiguously.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, D;     /* bf16 only; D in {64, 128}; Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t page_size;         /* keys per page: a positive multiple of 32 */
+  int32_t num_pages;         /* pages in each container */
+  int32_t max_pages;         /* page-table entries per sequence */
+  int64_t q_stride[2];       /* (b, h) element strides of q */
+  int64_t o_stride[2];       /* (b, h) element strides of o */
+  int64_t k_stride[3];       /* (page, h, s) element strides of k_pages */
+  int64_t v_stride[3];       /* (page, h, s) element strides of v_pages */
+  float scale;               /* NaN selects 1/sqrt(D); else finite and > 0 */
+} sdpa_paged_decode;
+
+/* Device workspace (bytes) of sdpa_decode_paged: the split-KV partial results. */
+size_t sdpa_decode_paged_workspace_bytes(const sdpa_paged_decode* p);
+
+sdpa_status sdpa_decode_paged(const sdpa_paged_decode* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table,
+                              const int32_t* seq_lens_kv, void* o, float* lse_or_null,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 const char* sdpa_status_string(sdpa_status s);
 
 /* Text of the last failure on the calling thread ("" if none). */

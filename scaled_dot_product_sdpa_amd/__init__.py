@@ -12,9 +12,10 @@ has not been built (``python -m scaled_dot_product_sdpa_amd.build``).
 """
 
 from .api import (BACKWARD_STAGES, CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, EXPORTS, LIB_PATH,
-                  BackwardCall, ForwardCall, Problem, SdpaError, load_library, sdpa_backward,
-                  sdpa_forward)
+                  BackwardCall, ForwardCall, PagedDecode, PagedDecodeCall, Problem, SdpaError,
+                  load_library, sdpa_backward, sdpa_decode_paged, sdpa_forward)
 
-__all__ = ["sdpa_forward", "sdpa_backward", "ForwardCall", "BackwardCall", "BACKWARD_STAGES",
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode_paged", "ForwardCall", "BackwardCall",
+           "PagedDecodeCall", "PagedDecode", "BACKWARD_STAGES",
            "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "load_library", "LIB_PATH", "EXPORTS",
            "Problem", "SdpaError"]

@@ -32,7 +32,8 @@ SDPA_DTYPE_BF16 = 1
 EXPORTS = (
     "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes", "sdpa_forward",
     "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
-    "sdpa_status_string", "sdpa_last_error", "sdpa_version",
+    "sdpa_status_string", "sdpa_last_error", "sdpa_version", "sdpa_decode_paged_workspace_bytes",
+    "sdpa_decode_paged",
 )
 BACKWARD_STAGES = ("prep", "dkdv", "dq")
 
@@ -50,6 +51,18 @@ class Problem(ctypes.Structure):
         ("mask_stride", ctypes.c_int64 * 3),
         ("scale", ctypes.c_float),
         ("is_causal", ctypes.c_int32),
+    ]
+
+
+class PagedDecode(ctypes.Structure):
+    """Mirror of ``sdpa_paged_decode``."""
+
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 2), ("o_stride", ctypes.c_int64 * 2),
+        ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -86,6 +99,10 @@ def load_library(path: Path | str | None = None):
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.restype = ctypes.c_int
+    lib.sdpa_decode_paged_workspace_bytes.argtypes = [ctypes.POINTER(PagedDecode)]
+    lib.sdpa_decode_paged_workspace_bytes.restype = sz
+    lib.sdpa_decode_paged.argtypes = [ctypes.POINTER(PagedDecode), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sdpa_decode_paged.restype = ctypes.c_int
     if path is None:
         _LIB = lib
     return lib
@@ -316,3 +333,64 @@ def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, s
     call = BackwardCall(q, k, v, o, dO, lse, mask, scale, is_causal, seq_lens_q, seq_lens_kv)
     call.launch()
     return call.result()
+
+
+class PagedDecodeCall:
+    """Marshalled single-query decode against a paged KV cache (see ``sdpa_decode_paged`` in
+    include/sdpa.h): q (B, Hq, D); k_pages, v_pages (num_pages, Hkv, page_size, D);
+    page_table (B, max_pages) int32; seq_lens_kv (B) int32; all on one GPU."""
+
+    def __init__(self, q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True):
+        self.lib = load_library()
+        if q.dim() == 4 and q.shape[2] == 1:
+            q = q[:, :, 0]
+        if q.dim() != 3 or k_pages.dim() != 4 or v_pages.dim() != 4:
+            raise ValueError("sdpa_decode_paged: q (B, Hq, D), k/v pages (num_pages, Hkv, page_size, D)")
+        _check_io(q, k_pages, v_pages)
+        B, Hq, D = q.shape
+        num_pages, Hkv, page_size, Dk = k_pages.shape
+        if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
+            raise ValueError("sdpa_decode_paged: k/v pages must share one shape with width D")
+        if page_table.dim() != 2 or page_table.shape[0] != B:
+            raise ValueError("sdpa_decode_paged: page_table must be (B, max_pages)")
+        for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+            if t.stride(-1) != 1:
+                raise ValueError(f"sdpa_decode_paged: {n} must have unit stride along D")
+        self.page_table = page_table.to(device=q.device, dtype=torch.int32).contiguous()
+        self.lens = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
+        if self.lens is None:
+            raise ValueError("sdpa_decode_paged: seq_lens_kv is required")
+        self.o = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+        p = PagedDecode()
+        p.B, p.Hq, p.Hkv, p.D = B, Hq, Hkv, D
+        p.page_size, p.num_pages, p.max_pages = page_size, num_pages, self.page_table.shape[1]
+        p.q_stride[:] = (q.stride(0), q.stride(1))
+        p.o_stride[:] = (self.o.stride(0), self.o.stride(1))
+        p.k_stride[:] = (k_pages.stride(0), k_pages.stride(1), k_pages.stride(2))
+        p.v_stride[:] = (v_pages.stride(0), v_pages.stride(1), v_pages.stride(2))
+        p.scale = math.nan if scale is None else float(scale)
+        self.p = p
+        nws = self.lib.sdpa_decode_paged_workspace_bytes(ctypes.byref(p))
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k_pages, v_pages)
+        self.device = q.device
+        self.args = [ctypes.byref(p), _vp(q), _vp(k_pages), _vp(v_pages), _vp(self.page_table),
+                     _vp(self.lens), _vp(self.o), _vp(self.lse), _vp(self.ws), nws]
+
+    def launch(self):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        st = self.lib.sdpa_decode_paged(*self.args, stream)
+        if st != SDPA_OK:
+            raise_status(self.lib, st)
+
+    def result(self):
+        return self.o, self.lse
+
+
+def sdpa_decode_paged(q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True):
+    """O (B, Hq, D) (and LSE (B, Hq)) of single-query attention over a paged KV cache."""
+    call = PagedDecodeCall(q, k_pages, v_pages, page_table, seq_lens_kv, scale, return_lse)
+    call.launch()
+    o, lse = call.result()
+    return (o, lse) if return_lse else o

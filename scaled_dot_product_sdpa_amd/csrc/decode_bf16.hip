@@ -58,7 +58,10 @@ __device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t, uint32_t, uint32_t) { retu
 //       transposed (ds_read_b64_tr_b16).
 // Two register sets of K and V rows: while tile t is computed, tile t+1 is in flight and
 // tile t+2 is requested as soon as tile t's K operands and V rows have been consumed.
-template <int D>
+// PAGED: the cache lives in pages (a 32-key tile never straddles two, since the page size
+// is a multiple of 32); each lane first reads the page index of one tile of the split,
+// and a tile's rows are then addressed from its page like the rows of a contiguous cache.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kDT * D;
@@ -88,8 +91,17 @@ void decode_split_kernel(DecodeArgs a) {
   const bool qvalid = i16 < p.G;
   const int h = g * p.G + (qvalid ? i16 : 0);
   const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
-  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + (PAGED ? 0 : b * p.v_sb) + g * p.v_sh;
+  // page index of tile `lane` of the split (the table column and the page are clamped into
+  // the table row and the containers, so a length or entry out of range reads no memory
+  // outside them); a split has at most 512 / 32 = 16 tiles
+  int lane_page = 0;
+  if (PAGED && lane < n_tiles) {
+    const int col = min((k0 + kDT * lane) / a.page_size, a.max_pages - 1);
+    const int pg = a.page_table[(int64_t)b * a.max_pages + col];
+    lane_page = min(max(pg, 0), a.num_pages - 1);
+  }
 
   // Per-lane byte offsets inside a tile (the tile's first row moves with the resource; the
   // whole offset is in the vector operand, which is what the range check covers): K operand
@@ -112,8 +124,18 @@ void decode_split_kernel(DecodeArgs a) {
   auto load_tile = [&](int t, int set) __attribute__((always_inline)) {
     const int j0 = min(k0 + t * kDT, k1);
     const int n = min(kDT, k1 - j0);
-    const reg_rsrc_t kr_ = reg_rsrc(kbase + (int64_t)j0 * p.k_sl, n > 0 ? (int64_t)(n - 1) * p.k_sl * 2 + D * 2 : 0);
-    const reg_rsrc_t vr_ = reg_rsrc(vbase + (int64_t)j0 * p.v_sl, n > 0 ? (int64_t)(n - 1) * p.v_sl * 2 + D * 2 : 0);
+    const bf16* kt = kbase;
+    const bf16* vt = vbase;
+    int row = j0;
+    if (PAGED) {
+      // tiles past the split (t >= n_tiles, empty range) read lane t's 0
+      const int page = __builtin_amdgcn_readlane(lane_page, min(t, 63));
+      kt += (int64_t)page * a.kp_stride;
+      vt += (int64_t)page * a.vp_stride;
+      row = j0 % a.page_size;
+    }
+    const reg_rsrc_t kr_ = reg_rsrc(kt + (int64_t)row * p.k_sl, n > 0 ? (int64_t)(n - 1) * p.k_sl * 2 + D * 2 : 0);
+    const reg_rsrc_t vr_ = reg_rsrc(vt + (int64_t)row * p.v_sl, n > 0 ? (int64_t)(n - 1) * p.v_sl * 2 + D * 2 : 0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -302,7 +324,10 @@ template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const int grid = a.p.B * a.p.Hkv * a.n_split;
   if (grid > 0) {
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(grid), dim3(64), 0, s, a);
+    if (a.page_table)
+      hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(grid), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(grid), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

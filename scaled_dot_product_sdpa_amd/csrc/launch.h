@@ -59,6 +59,15 @@ struct DecodeArgs {
   float* part_lse;  // workspace (B, Hq, n_split) fp32
   int split_keys;   // keys per split
   int n_split;
+  // paged KV cache (page_table non-null): K of sequence b, key s is row s % page_size of
+  // page page_table[b * max_pages + s / page_size] (page stride kp_stride, v: vp_stride;
+  // head and row strides in p.k_sh / p.k_sl, p.v_sh / p.v_sl)
+  const int32_t* page_table;
+  int page_size;
+  int max_pages;
+  int num_pages;
+  int64_t kp_stride;
+  int64_t vp_stride;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

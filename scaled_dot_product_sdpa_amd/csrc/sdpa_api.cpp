@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <utility>
 #include <cstring>
 #include <string>
 
@@ -270,6 +271,105 @@ sdpa_status sdpa_backward(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdAll,
 sdpa_status sdpa_backward_prep(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdPrep, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dkdv(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDkdv, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dq(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDq, SDPA_BWD_PASS); }
+
+}  // extern "C"
+
+namespace {
+sdpa_status check_paged(const sdpa_paged_decode* p) {
+  if (!p) return fail(SDPA_ERR_INVALID_ARGUMENT, "problem pointer is null");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->num_pages < 1 || p->max_pages < 1 ||
+      p->page_size < 1)
+    return fail(SDPA_ERR_INVALID_ARGUMENT,
+                "sizes must satisfy B, Hq, Hkv, page_size, num_pages, max_pages >= 1 (got B=%d "
+                "Hq=%d Hkv=%d page_size=%d num_pages=%d max_pages=%d)",
+                p->B, p->Hq, p->Hkv, p->page_size, p->num_pages, p->max_pages);
+  if (p->Hq % p->Hkv != 0)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!std::isnan(p->scale) && !(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be NaN (default) or finite and > 0");
+  if (p->D != 64 && p->D != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", p->D);
+  if (p->Hq / p->Hkv > 16)
+    return fail(SDPA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", p->Hq / p->Hkv);
+  if (p->page_size % 32 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "page_size (%d) must be a multiple of 32", p->page_size);
+  if ((int64_t)p->max_pages * p->page_size > (1 << 30))
+    return fail(SDPA_ERR_UNSUPPORTED, "max_pages * page_size must not exceed 2^30 keys");
+  const int64_t* st[4] = {p->q_stride, p->o_stride, p->k_stride, p->v_stride};
+  const int nd[4] = {2, 2, 3, 3};
+  const char* names[4] = {"q", "o", "k_pages", "v_pages"};
+  for (int t = 0; t < 4; ++t)
+    for (int a = 0; a < nd[t]; ++a) {
+      if (st[t][a] < 0) return fail(SDPA_ERR_INVALID_ARGUMENT, "%s stride %d is negative", names[t], a);
+      if (st[t][a] % 8 != 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "%s stride %d (%lld) is not a multiple of 8 elements",
+                    names[t], a, (long long)st[t][a]);
+    }
+  if (p->k_stride[2] >= ((int64_t)1 << 24) || p->v_stride[2] >= ((int64_t)1 << 24))
+    return fail(SDPA_ERR_UNSUPPORTED, "page row strides must be below 2^24 elements");
+  if (p->page_size > 1 && (p->k_stride[2] < p->D || p->v_stride[2] < p->D))
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "page rows overlap");
+  return SDPA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t sdpa_decode_paged_workspace_bytes(const sdpa_paged_decode* p) {
+  if (check_paged(p) != SDPA_OK) return 0;
+  int sk = 0, ns = 0;
+  sdpa::decode_split_plan(p->B, p->Hkv, p->max_pages * p->page_size, &sk, &ns);
+  const size_t rows = (size_t)p->B * p->Hq * ns;
+  return round_up(rows * p->D * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+sdpa_status sdpa_decode_paged(const sdpa_paged_decode* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table,
+                              const int32_t* seq_lens_kv, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa_status st = check_paged(p);
+  if (st != SDPA_OK) return st;
+  for (auto x : {std::make_pair(q, "q"), std::make_pair(k_pages, "k_pages"),
+                 std::make_pair((const void*)v_pages, "v_pages"), std::make_pair((const void*)o, "o")}) {
+    st = check_ptr(x.first, x.second, true, 16);
+    if (st != SDPA_OK) return st;
+  }
+  st = check_ptr(page_table, "page_table", true, 4);
+  if (st == SDPA_OK) st = check_ptr(seq_lens_kv, "seq_lens_kv", true, 4);
+  if (st == SDPA_OK) st = check_ptr(lse, "lse", false, 4);
+  if (st != SDPA_OK) return st;
+  const size_t need = sdpa_decode_paged_workspace_bytes(p);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "paged decode needs %zu workspace bytes, got %zu",
+                need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SDPA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+
+  sdpa::DecodeArgs a{};
+  sdpa::Problem& k = a.p;
+  k.B = p->B; k.Hq = p->Hq; k.Hkv = p->Hkv; k.G = p->Hq / p->Hkv;
+  k.Lq = 1; k.Lk = p->max_pages * p->page_size; k.D = p->D;
+  k.q_sb = p->q_stride[0]; k.q_sh = p->q_stride[1]; k.q_sl = p->D;
+  k.o_sb = p->o_stride[0]; k.o_sh = p->o_stride[1]; k.o_sl = p->D;
+  k.k_sb = 0; k.k_sh = p->k_stride[1]; k.k_sl = p->k_stride[2];
+  k.v_sb = 0; k.v_sh = p->v_stride[1]; k.v_sl = p->v_stride[2];
+  k.scale = std::isnan(p->scale) ? 1.0f / std::sqrt((float)p->D) : p->scale;
+  k.scale_log2 = k.scale * 1.4426950408889634f;
+  k.causal = 0;
+  k.len_kv = seq_lens_kv;
+  a.q = q; a.k = k_pages; a.v = v_pages; a.o = o; a.lse = lse;
+  a.page_table = page_table;
+  a.page_size = p->page_size;
+  a.max_pages = p->max_pages;
+  a.num_pages = p->num_pages;
+  a.kp_stride = p->k_stride[0];
+  a.vp_stride = p->v_stride[0];
+  sdpa::decode_split_plan(p->B, p->Hkv, k.Lk, &a.split_keys, &a.n_split);
+  const size_t rows = (size_t)p->B * p->Hq * a.n_split;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                        round_up(rows * p->D * sizeof(float)));
+  return hip_result(sdpa::launch_decode_bf16(a, reinterpret_cast<hipStream_t>(stream)),
+                    "paged decode launch");
+}
 
 const char* sdpa_status_string(sdpa_status s) {
   switch (s) {

@@ -145,3 +145,47 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sd.sdpa_forward(q, q, q)
+
+
+def _paged(B=2, Hq=8, Hkv=2, D=128, page_size=64, num_pages=10, max_pages=4):
+    p = sd.PagedDecode()
+    p.B, p.Hq, p.Hkv, p.D = B, Hq, Hkv, D
+    p.page_size, p.num_pages, p.max_pages = page_size, num_pages, max_pages
+    p.q_stride[:] = (Hq * D, D)
+    p.o_stride[:] = (Hq * D, D)
+    p.k_stride[:] = (Hkv * page_size * D, page_size * D, D)
+    p.v_stride[:] = (Hkv * page_size * D, page_size * D, D)
+    p.scale = math.nan
+    return p
+
+
+def _dec(lib, p, table=FAKE, lens=FAKE, ws=FAKE, nws=1 << 20):
+    return lib.sdpa_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, table, lens, FAKE, FAKE, ws, nws, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "page_size", 48), SDPA_ERR_UNSUPPORTED),   # not a multiple of 32
+    (lambda p: setattr(p, "page_size", 0), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "num_pages", 0), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: setattr(p, "Hq", 3), SDPA_ERR_INVALID_ARGUMENT),      # Hq % Hkv != 0
+    (lambda p: setattr(p, "Hq", 64), SDPA_ERR_UNSUPPORTED),          # 32 heads per KV head
+    (lambda p: setattr(p, "D", 96), SDPA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "scale", -1.0), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: p.k_stride.__setitem__(2, 60), SDPA_ERR_UNSUPPORTED),
+    (lambda p: p.v_stride.__setitem__(2, 64), SDPA_ERR_INVALID_ARGUMENT),  # rows overlap
+])
+def test_paged_decode_rejects(lib, mutate, status):
+    p = _paged()
+    mutate(p)  # every case fails validation, so the FAKE pointers are never used
+    assert _dec(lib, p) == status
+    assert lib.sdpa_decode_paged_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_paged_decode_pointers_and_workspace(lib):
+    p = _paged()
+    need = lib.sdpa_decode_paged_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert _dec(lib, p, table=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _dec(lib, p, lens=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _dec(lib, p, ws=FAKE, nws=need - 1) == SDPA_ERR_WORKSPACE_TOO_SMALL
+    assert _dec(lib, p, ws=None, nws=need) == SDPA_ERR_WORKSPACE_TOO_SMALL
