@@ -155,6 +155,45 @@ sdpa_status sdpa_backward_dq(const sdpa_problem* p, const void* q, const void* k
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged (packed) sequences.  The operation and every argument shared with sdpa_forward /
+ * sdpa_backward are theirs; what changes is where a batch's rows live.  Variable-length
+ * sequences are stored one after another without padding, the THD layout (cuDNN
+ * "Attention", Support Matrix glossary note 3, Ragged Layout): with offsets_q,
+ *   q[b, h, i, :] is row offsets_q[b] + i of the packed tensor, at element offset
+ *   (offsets_q[b] + i) * q_stride[2] + h * q_stride[1],
+ * likewise o, dO and dq with their own row stride (o_stride[2]); with offsets_kv the same
+ * for k, v, dk, dv.  The batch strides of a ragged side are ignored.  Either side may be
+ * ragged alone (the other keeps its (b, h, l) strides).
+ *   offsets_q, offsets_kv: (B + 1) int32 device arrays of starting ROWS (tokens), not
+ *   elements: the page's offsets divided by the row stride, which this layout takes per
+ *   tensor (the page's offset multiplier).  NULL = that side is padded; at least one is
+ *   non-NULL.
+ *   Lengths: seq_lens_q / seq_lens_kv when given (batches may then leave gaps between them,
+ *   the page's partially packed layout), else offsets[b + 1] - offsets[b], the cumulative
+ *   sequence lengths of a fully packed batch.  Lq, Lk are the maximum lengths: longer
+ *   batches are cut to Lq, Lk rows.
+ *   Output rows of a ragged side are written only for each batch's valid rows (a gap row
+ *   is the caller's and is left as it is); lse stays padded (B, Hq, Lq), -inf past a
+ *   batch's length; the mask, when given, is the padded (B, Hq, Lq, Lk) one; the workspace
+ *   is the one sdpa_forward_workspace_bytes / sdpa_backward_workspace_bytes give for p.
+ * Device-resident preconditions (not checked): offsets non-decreasing within the packed
+ * tensors, and every batch's rows inside them.  Bitwise equal to the padded entry points
+ * on the same data.
+ */
+sdpa_status sdpa_forward_ragged(const sdpa_problem* p, const void* q, const void* k,
+                                const void* v, const void* mask_or_null,
+                                const int32_t* seq_lens_q_or_null,
+                                const int32_t* seq_lens_kv_or_null, const int32_t* offsets_q,
+                                const int32_t* offsets_kv, void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+sdpa_status sdpa_backward_ragged(const sdpa_problem* p, const void* q, const void* k,
+                                 const void* v, const void* o, const void* dO, const float* lse,
+                                 const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                                 const int32_t* seq_lens_kv_or_null, const int32_t* offsets_q,
+                                 const int32_t* offsets_kv, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Single-query decode against a paged KV cache.  The operation is that of sdpa_forward with
  * Lq = 1, no mask, not causal (equivalently the bottom-right diagonal, which leaves every
  * cached key visible), with per-batch KV lengths; only the cache's storage differs.  The

@@ -33,7 +33,7 @@ EXPORTS = (
     "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes", "sdpa_forward",
     "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
     "sdpa_status_string", "sdpa_last_error", "sdpa_version", "sdpa_decode_paged_workspace_bytes",
-    "sdpa_decode_paged",
+    "sdpa_decode_paged", "sdpa_forward_ragged", "sdpa_backward_ragged",
 )
 BACKWARD_STAGES = ("prep", "dkdv", "dq")
 
@@ -94,6 +94,10 @@ def load_library(path: Path | str | None = None):
         f = getattr(lib, name)
         f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    lib.sdpa_forward_ragged.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sdpa_forward_ragged.restype = ctypes.c_int
+    lib.sdpa_backward_ragged.argtypes = [pp] + [vp] * 15 + [sz, vp]
+    lib.sdpa_backward_ragged.restype = ctypes.c_int
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_last_error.argtypes = []
@@ -139,6 +143,57 @@ def _strides3(t: torch.Tensor, name: str):
     if t.stride(-1) != 1 and t.shape[-1] > 1:
         raise NotImplementedError(f"sdpa: {name} must have unit stride along its last dim")
     return tuple(int(s) for s in t.stride()[:3])
+
+
+class _Layout:
+    """Logical (B, H, L, D) shape and (b, h, l) element strides of one operand: a padded
+    (B, H, L, D) / (H, L, D) tensor, or with row offsets a packed (T, H, D) one whose batch
+    stride is unused."""
+
+    def __init__(self, t, name, offsets=None, max_len=None, B=None):
+        if offsets is None:
+            t4 = _as4d(t, name)
+            self.shape = tuple(int(x) for x in t4.shape)
+            self.strides = _strides3(t4, name)
+            self.tensor = t4
+            return
+        if t.dim() != 3:
+            raise ValueError(f"sdpa: packed {name} must be (T, H, D), got {tuple(t.shape)}")
+        if t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise NotImplementedError(f"sdpa: {name} must have unit stride along its last dim")
+        self.shape = (B, int(t.shape[1]), int(max_len), int(t.shape[2]))
+        self.strides = (0, int(t.stride(1)), int(t.stride(0)))
+        self.tensor = t
+
+
+def _offsets(x, device, name):
+    if x is None:
+        return None
+    if not torch.is_tensor(x):
+        x = torch.tensor(x, dtype=torch.int32)
+    x = x.reshape(-1)
+    if x.numel() < 2:
+        raise ValueError(f"sdpa: {name} needs B + 1 >= 2 entries, got {x.numel()}")
+    return x.to(device=device, dtype=torch.int32).contiguous()
+
+
+def _max_len(max_len, lens, offsets):
+    """The padded length of a ragged side: given, or the longest batch (read back from the
+    device, which synchronises)."""
+    if max_len is not None:
+        return int(max_len)
+    ls = lens if lens is not None else offsets[1:] - offsets[:-1]
+    return max(int(ls.max().item()), 0)
+
+
+def _ragged_batch(q, offsets_q, offsets_kv):
+    B = None
+    for off in (offsets_q, offsets_kv):
+        if off is not None:
+            if B is not None and off.numel() - 1 != B:
+                raise ValueError("sdpa: offsets_q and offsets_kv give different batch sizes")
+            B = off.numel() - 1
+    return B
 
 
 def _mask4d(mask, B, Hq, Lq, Lk):
@@ -194,6 +249,8 @@ def causal_code(is_causal) -> int:
 
 
 def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
+    """q, k, v are tensors (B, H, L, D) or ``_Layout``s."""
+    q, k, v = (x if isinstance(x, _Layout) else _Layout(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v")))
     B, Hq, Lq, Dqk = q.shape
     Bk, Hkv, Lk, Dk2 = k.shape
     Bv, Hv, Lv, Dv = v.shape
@@ -204,10 +261,11 @@ def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
     if Hv != Hkv or Lv != Lk:
         raise ValueError("sdpa: k and v must have the same heads and length")
     p = Problem()
-    p.dtype = _dtype_code(q)
+    p.dtype = _dtype_code(q.tensor)
     p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.Dqk, p.Dv = B, Hq, Hkv, Lq, Lk, Dqk, Dv
-    for field, t, name in (("q_stride", q, "q"), ("k_stride", k, "k"), ("v_stride", v, "v")):
-        getattr(p, field)[:] = _strides3(t, name)
+    p.q_stride[:] = q.strides
+    p.k_stride[:] = k.strides
+    p.v_stride[:] = v.strides
     p.o_stride[:] = o_strides
     p.mask_stride[:] = mask_strides
     p.scale = math.nan if scale is None else float(scale)
@@ -228,32 +286,53 @@ def _check_io(*ts):
 
 class ForwardCall:
     """Marshalled forward: outputs ``o``, ``lse`` and the workspace are allocated once;
-    ``launch()`` enqueues the kernels on the current stream with the cached arguments."""
+    ``launch()`` enqueues the kernels on the current stream with the cached arguments.
+
+    Ragged (packed) sequences: with ``offsets_q`` ((B + 1) starting rows) q is a packed
+    (T, Hq, D) tensor and o is returned packed the same way; with ``offsets_kv`` k and v are
+    packed (T, Hkv, D).  Lengths are ``seq_lens_*`` when given, else the offset differences;
+    ``max_seqlen_*`` is the padded length (computed from the lengths, with a device read,
+    when not given).  Rows of ``o`` outside every batch are left as allocated."""
 
     def __init__(self, q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
-                 seq_lens_kv=None, return_lse=True):
+                 seq_lens_kv=None, return_lse=True, offsets_q=None, offsets_kv=None,
+                 max_seqlen_q=None, max_seqlen_kv=None):
         self.lib = load_library()
-        self.squeeze = q.dim() == 3
-        q, k, v = _as4d(q, "q"), _as4d(k, "k"), _as4d(v, "v")
+        self.ragged = offsets_q is not None or offsets_kv is not None
+        self.squeeze = q.dim() == 3 and not self.ragged
         _check_io(q, k, v, *([mask] if mask is not None else []))
-        B, Hq, Lq, _ = q.shape
-        Lk, Dv = k.shape[2], v.shape[3]
-        self.o = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
-        self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+        dev = q.device
+        oq, ok = _offsets(offsets_q, dev, "offsets_q"), _offsets(offsets_kv, dev, "offsets_kv")
+        B = _ragged_batch(q, oq, ok)
+        lq = _lens(seq_lens_q, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_q")
+        lk = _lens(seq_lens_kv, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_kv")
+        qL = _Layout(q, "q", oq, _max_len(max_seqlen_q, lq, oq) if oq is not None else None, B)
+        kL = _Layout(k, "k", ok, _max_len(max_seqlen_kv, lk, ok) if ok is not None else None, B)
+        vL = _Layout(v, "v", ok, kL.shape[2], B)
+        B, Hq, Lq, _ = qL.shape
+        Lk, Dv = kL.shape[2], vL.shape[3]
+        if oq is not None:
+            self.o = torch.empty((q.shape[0], Hq, Dv), dtype=q.dtype, device=dev)
+            o_st = (0, Dv, Hq * Dv)
+        else:
+            self.o = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=dev)
+            o_st = _strides3(self.o, "o")
+        self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev) if return_lse else None
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-        self.p = make_problem(q, k, v, _strides3(self.o, "o"), mst, scale, is_causal)
-        lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
-        lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
+        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal)
         nws = self.lib.sdpa_forward_workspace_bytes(ctypes.byref(self.p))
-        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-        self._keep = (q, k, v, m, lq, lk)
-        self.device = q.device
-        self.args = [ctypes.byref(self.p), _vp(q), _vp(k), _vp(v), _vp(m), _vp(lq), _vp(lk),
-                     _vp(self.o), _vp(self.lse), _vp(self.ws), nws]
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self._keep = (qL.tensor, kL.tensor, vL.tensor, m, lq, lk, oq, ok)
+        self.device = dev
+        ptrs = [_vp(qL.tensor), _vp(kL.tensor), _vp(vL.tensor), _vp(m), _vp(lq), _vp(lk)]
+        if self.ragged:
+            ptrs += [_vp(oq), _vp(ok)]
+        self.args = [ctypes.byref(self.p), *ptrs, _vp(self.o), _vp(self.lse), _vp(self.ws), nws]
+        self.fn = self.lib.sdpa_forward_ragged if self.ragged else self.lib.sdpa_forward
 
     def launch(self):
         stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
-        st = self.lib.sdpa_forward(*self.args, stream)
+        st = self.fn(*self.args, stream)
         if st != SDPA_OK:
             raise_status(self.lib, st)
 
@@ -268,44 +347,71 @@ class ForwardCall:
 class BackwardCall:
     """Marshalled backward: dq, dk, dv and the workspace are allocated once; ``launch()``
     runs all stages, ``launch(stage)`` one of "prep", "dkdv", "dq" (prep must precede the
-    other two)."""
+    other two).  Ragged arguments as in ``ForwardCall`` (o and dO then packed like q; only
+    the whole backward is offered)."""
 
     def __init__(self, q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
-                 seq_lens_q=None, seq_lens_kv=None):
+                 seq_lens_q=None, seq_lens_kv=None, offsets_q=None, offsets_kv=None,
+                 max_seqlen_q=None, max_seqlen_kv=None):
         self.lib = load_library()
-        self.squeeze = q.dim() == 3
-        q, k, v, o, dO = (_as4d(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO")))
-        if lse.dim() == 2:
-            lse = lse.unsqueeze(0)
+        self.ragged = offsets_q is not None or offsets_kv is not None
+        self.squeeze = q.dim() == 3 and not self.ragged
         _check_io(q, k, v, o, dO, *([mask] if mask is not None else []))
-        B, Hq, Lq, _ = q.shape
-        Lk = k.shape[2]
-        if tuple(o.shape) != (B, Hq, Lq, v.shape[3]) or dO.shape != o.shape:
-            raise ValueError("sdpa: o and dO must be (B, Hq, Lq, Dv)")
+        dev = q.device
+        oq, ok = _offsets(offsets_q, dev, "offsets_q"), _offsets(offsets_kv, dev, "offsets_kv")
+        B = _ragged_batch(q, oq, ok)
+        lq = _lens(seq_lens_q, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_q")
+        lk = _lens(seq_lens_kv, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_kv")
+        qL = _Layout(q, "q", oq, _max_len(max_seqlen_q, lq, oq) if oq is not None else None, B)
+        kL = _Layout(k, "k", ok, _max_len(max_seqlen_kv, lk, ok) if ok is not None else None, B)
+        vL = _Layout(v, "v", ok, kL.shape[2], B)
+        B, Hq, Lq, _ = qL.shape
+        Lk, Dv = kL.shape[2], vL.shape[3]
+        if oq is not None:
+            want = (q.shape[0], Hq, Dv)
+        else:
+            o, dO = _as4d(o, "o"), _as4d(dO, "dO")
+            want = (B, Hq, Lq, Dv)
+        if tuple(o.shape) != want or dO.shape != o.shape:
+            raise ValueError(f"sdpa: o and dO must be {want}")
         if o.stride() != dO.stride():
             dO = dO.contiguous()
             o = o.contiguous()
+        if lse.dim() == 2:
+            lse = lse.unsqueeze(0)
         if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
             raise ValueError("sdpa: lse must be float32 (B, Hq, Lq)")
         lse = lse.contiguous()
+        if oq is not None:
+            if o.stride(-1) != 1:
+                raise NotImplementedError("sdpa: o must have unit stride along its last dim")
+            o_st = (0, int(o.stride(1)), int(o.stride(0)))
+        else:
+            o_st = _strides3(o, "o")
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-        self.p = make_problem(q, k, v, _strides3(o, "o"), mst, scale, is_causal)
-        lq = _lens(seq_lens_q, B, q.device, "seq_lens_q")
-        lk = _lens(seq_lens_kv, B, q.device, "seq_lens_kv")
-        self.dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        self.dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
-        self.dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal)
+        qt, kt, vt = qL.tensor, kL.tensor, vL.tensor
+        self.dq = torch.empty_strided(qt.shape, qt.stride(), dtype=qt.dtype, device=dev)
+        self.dk = torch.empty_strided(kt.shape, kt.stride(), dtype=kt.dtype, device=dev)
+        self.dv = torch.empty_strided(vt.shape, vt.stride(), dtype=vt.dtype, device=dev)
         nws = self.lib.sdpa_backward_workspace_bytes(ctypes.byref(self.p))
-        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-        self._keep = (q, k, v, o, dO, lse, m, lq, lk)
-        self.device = q.device
-        self.args = [ctypes.byref(self.p), _vp(q), _vp(k), _vp(v), _vp(o), _vp(dO), _vp(lse),
-                     _vp(m), _vp(lq), _vp(lk), _vp(self.dq), _vp(self.dk), _vp(self.dv),
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self._keep = (qt, kt, vt, o, dO, lse, m, lq, lk, oq, ok)
+        self.device = dev
+        ptrs = [_vp(qt), _vp(kt), _vp(vt), _vp(o), _vp(dO), _vp(lse), _vp(m), _vp(lq), _vp(lk)]
+        if self.ragged:
+            ptrs += [_vp(oq), _vp(ok)]
+        self.args = [ctypes.byref(self.p), *ptrs, _vp(self.dq), _vp(self.dk), _vp(self.dv),
                      _vp(self.ws), nws]
-        self.fns = {"all": self.lib.sdpa_backward, "prep": self.lib.sdpa_backward_prep,
-                    "dkdv": self.lib.sdpa_backward_dkdv, "dq": self.lib.sdpa_backward_dq}
+        if self.ragged:
+            self.fns = {"all": self.lib.sdpa_backward_ragged}
+        else:
+            self.fns = {"all": self.lib.sdpa_backward, "prep": self.lib.sdpa_backward_prep,
+                        "dkdv": self.lib.sdpa_backward_dkdv, "dq": self.lib.sdpa_backward_dq}
 
     def launch(self, stage: str = "all"):
+        if stage not in self.fns:
+            raise ValueError(f"sdpa: backward stage {stage!r} is not offered here ({sorted(self.fns)})")
         stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
         st = self.fns[stage](*self.args, stream)
         if st != SDPA_OK:
@@ -319,18 +425,23 @@ class BackwardCall:
 
 
 def sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
-                 seq_lens_kv=None, return_lse=True):
-    """O (and LSE) of scaled dot-product attention.  q (B,Hq,Lq,D), k/v (B,Hkv,Lk,D)."""
-    call = ForwardCall(q, k, v, mask, scale, is_causal, seq_lens_q, seq_lens_kv, return_lse)
+                 seq_lens_kv=None, return_lse=True, offsets_q=None, offsets_kv=None,
+                 max_seqlen_q=None, max_seqlen_kv=None):
+    """O (and LSE) of scaled dot-product attention.  q (B,Hq,Lq,D), k/v (B,Hkv,Lk,D), or
+    packed (T, H, D) with ``offsets_q`` / ``offsets_kv`` (see ``ForwardCall``)."""
+    call = ForwardCall(q, k, v, mask, scale, is_causal, seq_lens_q, seq_lens_kv, return_lse,
+                       offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv)
     call.launch()
     o, lse = call.result()
     return (o, lse) if return_lse else o
 
 
 def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, seq_lens_q=None,
-                  seq_lens_kv=None):
+                  seq_lens_kv=None, offsets_q=None, offsets_kv=None, max_seqlen_q=None,
+                  max_seqlen_kv=None):
     """(dQ, dK, dV) from the forward's o and lse and the output gradient dO."""
-    call = BackwardCall(q, k, v, o, dO, lse, mask, scale, is_causal, seq_lens_q, seq_lens_kv)
+    call = BackwardCall(q, k, v, o, dO, lse, mask, scale, is_causal, seq_lens_q, seq_lens_kv,
+                        offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv)
     call.launch()
     return call.result()
 

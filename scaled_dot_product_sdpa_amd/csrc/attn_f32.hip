@@ -31,8 +31,8 @@ __device__ __forceinline__ RowCtx row_ctx(const Problem& p, int64_t row) {
   r.h = (int)((row / p.Lq) % p.Hq);
   r.b = (int)(row / ((int64_t)p.Lq * p.Hq));
   r.g = r.h / p.G;
-  r.q_end = p.len_q ? min(p.len_q[r.b], p.Lq) : p.Lq;
-  r.kv_end = p.len_kv ? min(p.len_kv[r.b], p.Lk) : p.Lk;
+  r.q_end = seq_len_q(p, r.b);
+  r.kv_end = seq_len_kv(p, r.b);
   r.coff = causal_offset(p.causal, r.q_end, r.kv_end);
   r.stop = (r.i < r.q_end) ? (p.causal ? max(0, min(r.kv_end, r.i + 1 + r.coff)) : r.kv_end) : 0;
   return r;
@@ -62,10 +62,10 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
   if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
   const RowCtx r = row_ctx(p, row);
-  const float* qrow = reinterpret_cast<const float*>(a.q) + r.b * p.q_sb + r.h * p.q_sh +
+  const float* qrow = reinterpret_cast<const float*>(a.q) + q_base(p, r.b) + r.h * p.q_sh +
                       (int64_t)r.i * p.q_sl;
-  const float* kbase = reinterpret_cast<const float*>(a.k) + r.b * p.k_sb + r.g * p.k_sh;
-  const float* vbase = reinterpret_cast<const float*>(a.v) + r.b * p.v_sb + r.g * p.v_sh;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, r.b) + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, r.b) + r.g * p.v_sh;
   float qv[D], acc[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) {
@@ -89,9 +89,11 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a) {
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* orow = reinterpret_cast<float*>(a.o) + r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+  if (r.i < q_rows_out(p, r.q_end)) {
+    float* orow = reinterpret_cast<float*>(a.o) + o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
 #pragma unroll
-  for (int t = 0; t < D; ++t) orow[t] = acc[t] * inv;
+    for (int t = 0; t < D; ++t) orow[t] = acc[t] * inv;
+  }
   if (a.lse) a.lse[row] = l > 0.f ? m + logf(l) : kNegInf;
 }
 
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kTpb) void bwd_prep_f32_kernel(BwdArgs a) {
   const RowCtx r = row_ctx(p, row);
   float Di = 0.f;
   if (r.i < r.q_end) {
-    const int64_t ooff = r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+    const int64_t ooff = o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
     const float* orow = reinterpret_cast<const float*>(a.o) + ooff;
     const float* drow = reinterpret_cast<const float*>(a.dO) + ooff;
 #pragma unroll
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
   if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
   const RowCtx r = row_ctx(p, row);
-  const int64_t qoff = r.b * p.q_sb + r.h * p.q_sh + (int64_t)r.i * p.q_sl;
-  const int64_t ooff = r.b * p.o_sb + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
-  const float* kbase = reinterpret_cast<const float*>(a.k) + r.b * p.k_sb + r.g * p.k_sh;
-  const float* vbase = reinterpret_cast<const float*>(a.v) + r.b * p.v_sb + r.g * p.v_sh;
+  const int64_t qoff = q_base(p, r.b) + r.h * p.q_sh + (int64_t)r.i * p.q_sl;
+  const int64_t ooff = o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, r.b) + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, r.b) + r.g * p.v_sh;
   float qv[D], dov[D], dq[D];
   const bool ok = r.i < r.q_end;
 #pragma unroll
@@ -149,9 +151,11 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
       for (int t = 0; t < D; ++t) dq[t] = fmaf(dS, kj[t], dq[t]);
     }
   }
-  float* dqrow = reinterpret_cast<float*>(a.dq) + qoff;
+  if (r.i < q_rows_out(p, r.q_end)) {
+    float* dqrow = reinterpret_cast<float*>(a.dq) + qoff;
 #pragma unroll
-  for (int t = 0; t < D; ++t) dqrow[t] = dq[t] * p.scale;
+    for (int t = 0; t < D; ++t) dqrow[t] = dq[t] * p.scale;
+  }
 }
 
 // dK_j and dV_j: one thread per key row of a KV head, summing over the query heads it
@@ -164,10 +168,10 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
   const int j = (int)(krow % p.Lk);
   const int g = (int)((krow / p.Lk) % p.Hkv);
   const int b = (int)(krow / ((int64_t)p.Lk * p.Hkv));
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
-  const int64_t koff = b * p.k_sb + g * p.k_sh + (int64_t)j * p.k_sl;
-  const int64_t voff = b * p.v_sb + g * p.v_sh + (int64_t)j * p.v_sl;
+  const int kv_end = seq_len_kv(p, b);
+  const int q_end = seq_len_q(p, b);
+  const int64_t koff = k_base(p, b) + g * p.k_sh + (int64_t)j * p.k_sl;
+  const int64_t voff = v_base(p, b) + g * p.v_sh + (int64_t)j * p.v_sl;
   float kv[D], vv[D], dk[D], dv[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) {
@@ -186,8 +190,8 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
         const int64_t row = ((int64_t)b * p.Hq + h) * p.Lq + i;
         const float lse = a.lse[row];
         if (lse == kNegInf) continue;
-        const float* qi = reinterpret_cast<const float*>(a.q) + b * p.q_sb + h * p.q_sh + (int64_t)i * p.q_sl;
-        const float* doi = reinterpret_cast<const float*>(a.dO) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sl;
+        const float* qi = reinterpret_cast<const float*>(a.q) + q_base(p, b) + h * p.q_sh + (int64_t)i * p.q_sl;
+        const float* doi = reinterpret_cast<const float*>(a.dO) + o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
         float dot = 0.f;
 #pragma unroll
         for (int t = 0; t < D; ++t) dot = fmaf(qi[t], kv[t], dot);
@@ -210,12 +214,14 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
       }
     }
   }
-  float* dkrow = reinterpret_cast<float*>(a.dk) + koff;
-  float* dvrow = reinterpret_cast<float*>(a.dv) + voff;
+  if (j < kv_rows_out(p, kv_end)) {
+    float* dkrow = reinterpret_cast<float*>(a.dk) + koff;
+    float* dvrow = reinterpret_cast<float*>(a.dv) + voff;
 #pragma unroll
-  for (int t = 0; t < D; ++t) {
-    dkrow[t] = dk[t] * p.scale;
-    dvrow[t] = dv[t];
+    for (int t = 0; t < D; ++t) {
+      dkrow[t] = dk[t] * p.scale;
+      dvrow[t] = dv[t];
+    }
   }
 }
 

@@ -55,10 +55,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     const int i = (int)(row % p.Lq);
     const int h = (int)((row / p.Lq) % p.Hq);
     const int b = (int)(row / ((int64_t)p.Lq * p.Hq));
-    const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
+    const int q_end = seq_len_q(p, b);
     if (i < q_end) {
       valid = true;
-      const int64_t off = b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sl + c * 8;
+      const int64_t off = o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl + c * 8;
       bf16x8 o8 = __builtin_bit_cast(bf16x8, ld16(reinterpret_cast<const bf16*>(a.o) + off));
       bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(reinterpret_cast<const bf16*>(a.dO) + off));
 #pragma unroll
@@ -116,14 +116,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), 1, !CAUSAL, bg, kt);
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
-  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
   const int j0 = kt * KT;
   const int jw = j0 + wave * 32;  // this wave's first key
   const int myk = jw + l32;       // this lane's key (N index of S, dP)
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
-  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + k_base(p, b) + g * p.k_sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + v_base(p, b) + g * p.v_sh;
 
   // Query tiles that can see any key of this workgroup; the G heads of the group in turn.
   const int kstop = min(kv_end, j0 + KT);
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto load_tile = [&](int it, bf16* Qd, bf16* Gd, float* Rd, bf16* Md) {
     int h, i0;
     tile_rows(it, h, i0);
-    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-    const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + b * p.o_sb + h * p.o_sh;
+    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+    const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + o_base(p, b) + h * p.o_sh;
     qcopy.copy(rows_rsrc<D, kQT>(qb, p.q_sl, i0, q_end), Qd, wave);
     gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
     const int uw = __builtin_amdgcn_readfirstlane(wave);
@@ -378,9 +378,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // Epilogue: lane holds key myk, d = mb*32 + (v/4)*8 + 4*hi + v%4.
-  if (myk < p.Lk) {
-    bf16* dkrow = reinterpret_cast<bf16*>(a.dk) + b * p.k_sb + g * p.k_sh + (int64_t)myk * p.k_sl;
-    bf16* dvrow = reinterpret_cast<bf16*>(a.dv) + b * p.v_sb + g * p.v_sh + (int64_t)myk * p.v_sl;
+  if (myk < kv_rows_out(p, kv_end)) {
+    bf16* dkrow = reinterpret_cast<bf16*>(a.dk) + k_base(p, b) + g * p.k_sh + (int64_t)myk * p.k_sl;
+    bf16* dvrow = reinterpret_cast<bf16*>(a.dv) + v_base(p, b) + g * p.v_sh + (int64_t)myk * p.v_sl;
 #pragma unroll
     for (int mb = 0; mb < NT; ++mb) {
 #pragma unroll
@@ -433,18 +433,18 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;
-  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
   // Rows: query tile `rank` of BM rows, heavy tiles first on causal grids (as the forward).
   const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
   const int wq_lo = qt * BM + wave * 32;  // this wave's first row
   const int row_lo = qt * BM, row_hi = row_lo + BM;
   const int wq_hi = min(wq_lo + 32, q_end) - 1;
 
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + b * p.o_sb + h * p.o_sh;
-  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
-  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + o_base(p, b) + h * p.o_sh;
+  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + k_base(p, b) + g * p.k_sh;
+  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + v_base(p, b) + g * p.v_sh;
   const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
 
   int kv_stop = kv_end;
@@ -657,8 +657,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int j = 0; j < R1; ++j) dq_mfma(j, kt_op(j, Kl, 1), ds_b);
   }
 
-  if (qi < p.Lq) {
-    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + b * p.q_sb + h * p.q_sh + (int64_t)qi * p.q_sl;
+  if (qi < q_rows_out(p, q_end)) {
+    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + q_base(p, b) + h * p.q_sh + (int64_t)qi * p.q_sl;
 #pragma unroll
     for (int mb = 0; mb < NT; ++mb) {
 #pragma unroll
@@ -701,18 +701,18 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;
-  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
   // Rows: query tile `rank` of BM rows, heavy tiles first on causal grids (as the forward).
   const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
   const int wq_lo = qt * BM + wave * 32;  // this wave's first row
   const int row_lo = qt * BM, row_hi = row_lo + BM;
   const int wq_hi = min(wq_lo + 32, q_end) - 1;
 
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + b * p.o_sb + h * p.o_sh;
-  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
-  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + o_base(p, b) + h * p.o_sh;
+  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + k_base(p, b) + g * p.k_sh;
+  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + v_base(p, b) + g * p.v_sh;
   const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
 
   int kv_stop = kv_end;
@@ -830,8 +830,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
   }
 
-  if (qi < p.Lq) {
-    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + b * p.q_sb + h * p.q_sh + (int64_t)qi * p.q_sl;
+  if (qi < q_rows_out(p, q_end)) {
+    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + q_base(p, b) + h * p.q_sh + (int64_t)qi * p.q_sl;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll

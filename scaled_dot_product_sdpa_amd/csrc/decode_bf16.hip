@@ -80,19 +80,19 @@ void decode_split_kernel(DecodeArgs a) {
   const int bg = blockIdx.x % (p.B * p.Hkv); // precedes the (mostly empty) higher splits
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int kv_end = seq_len_kv(p, b);
   const int k0 = c * a.split_keys;
   // the combine reads only splits that hold keys, and none of a batch whose query row is
   // past its length (an empty row)
-  if (k0 >= kv_end || (p.len_q && p.len_q[b] < 1)) return;
+  if (k0 >= kv_end || seq_len_q(p, b) < 1) return;
   const int k1 = min(k0 + a.split_keys, kv_end);
   const int n_tiles = (k1 - k0 + kDT - 1) / kDT;
 
   const bool qvalid = i16 < p.G;
   const int h = g * p.G + (qvalid ? i16 : 0);
-  const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + (PAGED ? 0 : b * p.k_sb) + g * p.k_sh;
-  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + (PAGED ? 0 : b * p.v_sb) + g * p.v_sh;
+  const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + (PAGED ? 0 : k_base(p, b)) + g * p.k_sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(a.v) + (PAGED ? 0 : v_base(p, b)) + g * p.v_sh;
   // page index of tile `lane` of the split (the table column and the page are clamped into
   // the table row and the containers, so a length or entry out of range reads no memory
   // outside them); a split has at most 512 / 32 = 16 tiles
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
   if (bh >= p.B * p.Hq) return;
   const int b = bh / p.Hq;
   const int h = bh % p.Hq;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
-  const bool row_live = !p.len_q || p.len_q[b] >= 1;  // else the row is empty: O = 0, LSE = -inf
+  const int kv_end = seq_len_kv(p, b);
+  const bool row_live = seq_len_q(p, b) >= 1;  // else the row is empty: O = 0, LSE = -inf
   const int n_live = row_live ? (kv_end + a.split_keys - 1) / a.split_keys : 0;
   const float* pl = a.part_lse + (int64_t)bh * a.n_split;
   const float* po = a.part_o + (int64_t)bh * a.n_split * D + E * lane;
@@ -314,9 +314,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
     for (int w = 32; w >= 1; w >>= 1) L += __shfl_xor(L, w);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  bf16* orow = reinterpret_cast<bf16*>(a.o) + b * p.o_sb + h * p.o_sh + E * lane;
+  if (row_live || !p.off_q) {  // a packed batch with no query row owns no output row
+    bf16* orow = reinterpret_cast<bf16*>(a.o) + o_base(p, b) + h * p.o_sh + E * lane;
 #pragma unroll
-  for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
+    for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
+  }
   if (a.lse && lane == 0) a.lse[bh] = (L > 0.f) ? M + logf(L) : kNegInf;
 }
 

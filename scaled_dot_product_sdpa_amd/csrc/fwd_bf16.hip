@@ -77,8 +77,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;
 
-  const int q_end = p.len_q ? min(p.len_q[b], p.Lq) : p.Lq;
-  const int kv_end = p.len_kv ? min(p.len_kv[b], p.Lk) : p.Lk;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
   // Rows of this workgroup: query tile `rank` of BM rows; causal grids run the tiles
   // heavy first (tile n_qt - 1 - rank) and the scheduler evens the load.
   const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
@@ -86,10 +86,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const int row_lo = qt * BM, row_hi = row_lo + BM;  // the workgroup's row span
   const int wq_hi = min(wq_lo + 32, q_end) - 1;  // this wave's last live row
 
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + b * p.q_sb + h * p.q_sh;
-  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + b * p.k_sb + g * p.k_sh;
-  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + b * p.v_sb + g * p.v_sh;
-  bf16* ob = reinterpret_cast<bf16*>(a.o) + b * p.o_sb + h * p.o_sh;
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+  const bf16* kb_ = reinterpret_cast<const bf16*>(a.k) + k_base(p, b) + g * p.k_sh;
+  const bf16* vb_ = reinterpret_cast<const bf16*>(a.v) + v_base(p, b) + g * p.v_sh;
+  bf16* ob = reinterpret_cast<bf16*>(a.o) + o_base(p, b) + h * p.o_sh;
   const bf16* mb_ = MASK ? reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh : nullptr;
   float* lseb = a.lse ? a.lse + ((int64_t)b * p.Hq + h) * p.Lq : nullptr;
 
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const float ft = xhalf_sum(frow + frow2);
   const bool rowlive = qrow < q_end && ft > 0.f;
   const float inv = rowlive ? 1.f / ft : 0.f;
-  if (qrow < p.Lq) {
+  if (qrow < q_rows_out(p, q_end)) {
     bf16* orow = ob + (int64_t)qrow * p.o_sl;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
@@ -364,8 +364,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(orow + mb * 32 + v4 * 8 + hi * 4) = w;
       }
     }
-    if (lseb && hi == 0) lseb[qrow] = rowlive ? (mref * kLn2 + logf(ft)) : kNegInf;
   }
+  if (qrow < p.Lq && lseb && hi == 0) lseb[qrow] = rowlive ? (mref * kLn2 + logf(ft)) : kNegInf;
 }
 
 template <int D, int NW, int WPE, bool CAUSAL, bool MASK>

@@ -20,9 +20,46 @@ struct Problem {
   int causal;  // 0 none, 1 top-left, 2 bottom-right diagonal
   const int32_t* len_q;   // may be null
   const int32_t* len_kv;  // may be null
+  // ragged (packed) sequences, may be null: batch b's query rows start at row off_q[b] of
+  // q, o, dO and dq (off_kv[b] of k, v, dk, dv), and the batch stride is unused.  Without a
+  // length array a batch's length is off[b+1] - off[b] (at most Lq, Lk).
+  const int32_t* off_q;
+  const int32_t* off_kv;
   const void* mask;       // may be null (additive, io dtype)
   int mask_vec;           // mask rows may be read with 16-byte vector loads
 };
+
+// Per-batch geometry shared by every kernel: valid lengths and the element offset of a
+// batch's first row (a fixed batch stride, or the packed row of its first token).
+__device__ __forceinline__ int seq_len_q(const Problem& p, int b) {
+  if (p.len_q) return min(p.len_q[b], p.Lq);
+  if (p.off_q) return min(max(p.off_q[b + 1] - p.off_q[b], 0), p.Lq);
+  return p.Lq;
+}
+__device__ __forceinline__ int seq_len_kv(const Problem& p, int b) {
+  if (p.len_kv) return min(p.len_kv[b], p.Lk);
+  if (p.off_kv) return min(max(p.off_kv[b + 1] - p.off_kv[b], 0), p.Lk);
+  return p.Lk;
+}
+// q, o, dO, dq (query side) and k, v, dk, dv (key side)
+__device__ __forceinline__ int64_t q_base(const Problem& p, int b) {
+  return p.off_q ? (int64_t)p.off_q[b] * p.q_sl : (int64_t)b * p.q_sb;
+}
+__device__ __forceinline__ int64_t o_base(const Problem& p, int b) {
+  return p.off_q ? (int64_t)p.off_q[b] * p.o_sl : (int64_t)b * p.o_sb;
+}
+__device__ __forceinline__ int64_t k_base(const Problem& p, int b) {
+  return p.off_kv ? (int64_t)p.off_kv[b] * p.k_sl : (int64_t)b * p.k_sb;
+}
+__device__ __forceinline__ int64_t v_base(const Problem& p, int b) {
+  return p.off_kv ? (int64_t)p.off_kv[b] * p.v_sl : (int64_t)b * p.v_sb;
+}
+
+// Output rows (o, dq; dk, dv) a batch writes: every row up to the padded length (zeros past
+// the valid length), but only the valid rows of a ragged batch: the rows after them belong
+// to the next batch or to a gap the caller owns.
+__device__ __forceinline__ int q_rows_out(const Problem& p, int q_end) { return p.off_q ? q_end : p.Lq; }
+__device__ __forceinline__ int kv_rows_out(const Problem& p, int kv_end) { return p.off_kv ? kv_end : p.Lk; }
 
 struct FwdArgs {
   Problem p;

@@ -106,7 +106,8 @@ bool use_decode(const sdpa_problem* p, bool has_mask) {
 }
 
 sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_t* lq,
-                           const int32_t* lk) {
+                           const int32_t* lk, const int32_t* off_q = nullptr,
+                           const int32_t* off_kv = nullptr) {
   sdpa::Problem k{};
   k.B = p->B; k.Hq = p->Hq; k.Hkv = p->Hkv; k.G = p->Hq / p->Hkv;
   k.Lq = p->Lq; k.Lk = p->Lk; k.D = p->Dqk;
@@ -120,6 +121,8 @@ sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_
   k.causal = p->is_causal;
   k.len_q = lq;
   k.len_kv = lk;
+  k.off_q = off_q;
+  k.off_kv = off_kv;
   k.mask = mask;
   // 16-byte mask vectors need every (b, h, i) row start 16-byte aligned and whole 8-key
   // chunks per row
@@ -188,9 +191,11 @@ size_t sdpa_backward_workspace_bytes(const sdpa_problem* p) {
   return 2 * round_up((size_t)p->B * p->Hq * p->Lq * sizeof(float));
 }
 
-sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, const void* v,
-                         const void* mask, const int32_t* lq, const int32_t* lk, void* o,
-                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+sdpa_status forward_impl(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* mask, const int32_t* lq, const int32_t* lk,
+                         const int32_t* off_q, const int32_t* off_kv, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   sdpa_status st = check_problem(p);
   if (st != SDPA_OK) return st;
   const bool hq = p->Lq > 0, hk = p->Lk > 0;
@@ -199,7 +204,7 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
   if (st != SDPA_OK) return st;
   (void)elem_bytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  sdpa::Problem kp = make_problem(p, mask, lq, lk);
+  sdpa::Problem kp = make_problem(p, mask, lq, lk, off_q, off_kv);
   if (p->Lq == 0) {
     g_last_error.clear();
     return SDPA_OK;
@@ -228,12 +233,48 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
   return hip_result(sdpa::launch_fwd_bf16(a, s), "bf16 forward launch");
 }
 
+// Ragged entry points: the offsets replace the batch strides of their side, so a copy of
+// the problem with those strides zeroed goes through the common checks.
+sdpa_status ragged_problem(const sdpa_problem* p, const int32_t* off_q, const int32_t* off_kv,
+                           sdpa_problem* out) {
+  if (!p) return fail(SDPA_ERR_INVALID_ARGUMENT, "problem pointer is null");
+  if (!off_q && !off_kv)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "ragged call with neither query nor key offsets");
+  sdpa_status st = check_ptr(off_q, "offsets_q", false, 4);
+  if (st == SDPA_OK) st = check_ptr(off_kv, "offsets_kv", false, 4);
+  if (st != SDPA_OK) return st;
+  *out = *p;
+  if (off_q) out->q_stride[0] = out->o_stride[0] = 0;
+  if (off_kv) out->k_stride[0] = out->v_stride[0] = 0;
+  return SDPA_OK;
+}
+}  // namespace
+
+sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                         const void* mask, const int32_t* lq, const int32_t* lk, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(p, q, k, v, mask, lq, lk, nullptr, nullptr, o, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+sdpa_status sdpa_forward_ragged(const sdpa_problem* p, const void* q, const void* k,
+                                const void* v, const void* mask, const int32_t* lq,
+                                const int32_t* lk, const int32_t* off_q, const int32_t* off_kv,
+                                void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  sdpa_problem r;
+  sdpa_status st = ragged_problem(p, off_q, off_kv, &r);
+  if (st != SDPA_OK) return st;
+  return forward_impl(&r, q, k, v, mask, lq, lk, off_q, off_kv, o, lse, workspace,
+                      workspace_bytes, stream);
+}
+
 namespace {
 sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, const void* k,
                             const void* v, const void* o, const void* dO, const float* lse,
-                            const void* mask, const int32_t* lq, const int32_t* lk, void* dq,
-                            void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            const void* mask, const int32_t* lq, const int32_t* lk,
+                            const int32_t* off_q, const int32_t* off_kv, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   sdpa_status st = check_problem(p);
   if (st != SDPA_OK) return st;
   const bool hq = p->Lq > 0, hk = p->Lk > 0;
@@ -249,7 +290,7 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
     return fail(SDPA_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   sdpa::BwdArgs a{};
-  a.p = make_problem(p, mask, lq, lk);
+  a.p = make_problem(p, mask, lq, lk, off_q, off_kv);
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = reinterpret_cast<float*>(workspace);
@@ -265,12 +306,25 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
       const void *dO, const float *lse, const void *mask, const int32_t *lq,               \
       const int32_t *lk, void *dq, void *dk, void *dv, void *workspace,                    \
       size_t workspace_bytes, void *stream
-#define SDPA_BWD_PASS p, q, k, v, o, dO, lse, mask, lq, lk, dq, dk, dv, workspace, workspace_bytes, stream
+#define SDPA_BWD_PASS \
+  p, q, k, v, o, dO, lse, mask, lq, lk, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes, stream
 
 sdpa_status sdpa_backward(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdAll, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_prep(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdPrep, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dkdv(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDkdv, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dq(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDq, SDPA_BWD_PASS); }
+
+sdpa_status sdpa_backward_ragged(const sdpa_problem* p, const void* q, const void* k,
+                                 const void* v, const void* o, const void* dO, const float* lse,
+                                 const void* mask, const int32_t* lq, const int32_t* lk,
+                                 const int32_t* off_q, const int32_t* off_kv, void* dq, void* dk,
+                                 void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa_problem r;
+  sdpa_status st = ragged_problem(p, off_q, off_kv, &r);
+  if (st != SDPA_OK) return st;
+  return backward_stages(sdpa::kBwdAll, &r, q, k, v, o, dO, lse, mask, lq, lk, off_q, off_kv, dq,
+                         dk, dv, workspace, workspace_bytes, stream);
+}
 
 }  // extern "C"
 

@@ -189,3 +189,46 @@ def test_paged_decode_pointers_and_workspace(lib):
     assert _dec(lib, p, lens=None) == SDPA_ERR_INVALID_ARGUMENT
     assert _dec(lib, p, ws=FAKE, nws=need - 1) == SDPA_ERR_WORKSPACE_TOO_SMALL
     assert _dec(lib, p, ws=None, nws=need) == SDPA_ERR_WORKSPACE_TOO_SMALL
+
+
+def _fwd_ragged(lib, p, off_q=FAKE, off_kv=FAKE, q=FAKE, lse=FAKE):
+    return lib.sdpa_forward_ragged(ctypes.byref(p), q, FAKE, FAKE, None, None, None, off_q, off_kv,
+                                   FAKE, lse, None, 0, None)
+
+
+def _bwd_ragged(lib, p, off_q=FAKE, off_kv=FAKE, lse=FAKE, ws=FAKE, nws=1 << 20):
+    return lib.sdpa_backward_ragged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, lse, None, None,
+                                    None, off_q, off_kv, FAKE, FAKE, FAKE, ws, nws, None)
+
+
+def test_ragged_rejects(lib):
+    p = _problem()
+    # at least one side ragged; offsets 4-byte aligned
+    assert _fwd_ragged(lib, p, off_q=None, off_kv=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _bwd_ragged(lib, p, off_q=None, off_kv=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _fwd_ragged(lib, p, off_q=FAKE + 2) == SDPA_ERR_UNSUPPORTED
+    assert _bwd_ragged(lib, p, off_kv=FAKE + 1) == SDPA_ERR_UNSUPPORTED
+    # the common checks still apply
+    assert _fwd_ragged(lib, _problem(Hq=3)) == SDPA_ERR_INVALID_ARGUMENT
+    assert _bwd_ragged(lib, p, lse=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert _bwd_ragged(lib, p, nws=16) == SDPA_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd_ragged(lib, p, q=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert lib.sdpa_last_error().decode() != ""
+
+
+def test_ragged_ignores_batch_strides_of_ragged_sides(lib):
+    """A batch stride that the padded call rejects is unused (and not checked) on a ragged
+    side; the call then fails on the null q instead, before any launch."""
+    p = _problem()
+    p.q_stride[0] = 3
+    p.o_stride[0] = 5
+    assert _fwd(lib, p, q=None) == SDPA_ERR_UNSUPPORTED
+    assert _fwd_ragged(lib, p, off_kv=None, q=None) == SDPA_ERR_INVALID_ARGUMENT
+    p = _problem()
+    p.k_stride[0] = 3
+    assert _fwd(lib, p, q=None) == SDPA_ERR_UNSUPPORTED
+    assert _fwd_ragged(lib, p, off_q=None, q=None) == SDPA_ERR_INVALID_ARGUMENT
+    # the query side's batch stride is still checked when only the keys are ragged
+    p = _problem()
+    p.q_stride[0] = 3
+    assert _fwd_ragged(lib, p, off_q=None, q=None) == SDPA_ERR_UNSUPPORTED
