@@ -89,6 +89,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int R2 = 2 * NS;     // slots of region 2 (S, dP MFMAs)
   constexpr int E1 = 16 / R1;    // scores per lane per region-1 slot
   constexpr int MT = MASK ? kQT * KT : 8;
+  // LDS operand reads issued ahead of their MFMA (transposed dV/dK operands, S/dP A
+  // operands): an MFMA takes 32 cycles, a 16-byte LDS read several times that, and with
+  // one wave per SIMD nothing else covers the wait; d = 128 has no registers to spare.
+  constexpr int TPRE = D == 64 ? 3 : 2;
+  constexpr int APRE = D == 64 ? 4 : 2;
   __shared__ __attribute__((aligned(16))) bf16 Q0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 Q1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 Q2[TILE];
@@ -287,11 +292,15 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
     };
     // region 1
     bf16x8 aop[R2], top[R1];
-    top[0] = tr_op(0, Qp, Gp, kbp);
-    top[1] = tr_op(1, Qp, Gp, kbp);
+#pragma unroll
+    for (int j = 0; j < TPRE; ++j) top[j] = tr_op(j, Qp, Gp, kbp);
 #pragma unroll
     for (int j = 0; j < R1; ++j) {
-      if (j + 2 < R1) top[j + 2] = tr_op(j + 2, Qp, Gp, kbp);
+      if (j + TPRE < R1) top[j + TPRE] = tr_op(j + TPRE, Qp, Gp, kbp);
+      if (j >= R1 - APRE) {  // the first A operands of block bi+1
+        const int i = j - (R1 - APRE);
+        aop[i] = tile_row8<D>((i & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (i >> 1) + hi);
+      }
       if ((j * E1) % 4 == 0 && j * E1 / 4 + 1 < 4) {
         l4[j * E1 / 4 + 1] = lr[j * E1 / 4 + 1];
         d4[j * E1 / 4 + 1] = dr[j * E1 / 4 + 1];
@@ -305,10 +314,6 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = (j - 2) * E1; e < (j - 1) * E1; ++e)
         if (e >= 0) st_c(e);
-      if (j >= R1 - 2) {  // the first A operands of block bi+1
-        const int i = j - (R1 - 2);
-        aop[i] = tile_row8<D>((i & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (i >> 1) + hi);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // region 2
@@ -316,8 +321,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dp_nx = f32x16{};
 #pragma unroll
     for (int i = 0; i < R2; ++i) {
-      if (i + 2 < R2) {
-        const int n = i + 2;
+      if (i + APRE < R2) {
+        const int n = i + APRE;
         aop[n] = tile_row8<D>((n & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (n >> 1) + hi);
       }
       if (i & 1) dp_nx = mfma32(aop[i], vreg[i >> 1], dp_nx);
@@ -334,6 +339,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // this block's P and dS stay computed inside this phase (see pin)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pin(pd[i]);
   };
 
   // One tile step (two blocks); unrolled by three over the LDS buffers (see the forward).

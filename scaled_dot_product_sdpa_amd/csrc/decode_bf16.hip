@@ -23,27 +23,9 @@ namespace {
 
 constexpr int kDT = 32;  // keys per tile
 
-// Raw buffer resource over `bytes` bytes at `base` for loads into registers (reads past the
-// end return zeros).  The resource type exists only for the GPU target; the host pass of
-// this single-source file parses the device code with a placeholder.
-#if defined(__HIP_DEVICE_COMPILE__)
-typedef __amdgpu_buffer_rsrc_t reg_rsrc_t;
-__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// 16 bytes at byte offset voff + soff of the buffer; the compiler tracks the load like any
-// other (it inserts the wait before the first use of the result).  The KV cache is read
-// once, so the loads carry the non-temporal cache policy (measured: 12 % more bandwidth
-// than the default policy on the 8k-key GQA decode).
+// The KV cache is read once, so its loads carry the non-temporal cache policy (measured: 12 %
+// more bandwidth than the default policy on the 8k-key GQA decode).
 constexpr int kNonTemporal = 2;
-__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
-}
-#else
-struct reg_rsrc_t { uint32_t w[4]; };
-__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void*, int64_t) { return reg_rsrc_t{}; }
-__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t, uint32_t, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
-#endif
 
 // 16x16x32 MFMAs: the N columns are the (at most 16) query heads of the group, so a quarter
 // of the columns do useful work where a 32-wide tile would use an eighth, and each lane holds
@@ -139,9 +121,9 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) kr[set][kb][kk] = reg_ld16(kr_, koff[kb] + 64 * kk, 0);
+      for (int kk = 0; kk < NK; ++kk) kr[set][kb][kk] = reg_ld16<kNonTemporal>(kr_, koff[kb] + 64 * kk, 0);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) vrg[set][i] = reg_ld16(vr_, voff[i], 0);
+    for (int i = 0; i < VLD; ++i) vrg[set][i] = reg_ld16<kNonTemporal>(vr_, voff[i], 0);
   };
   // Q^T operand (lane (g4, i16) holds d = 32*kk + 8*g4 .. +7 of head i16), loaded before
   // the tiles so that it is never the youngest load in flight at the top of the loop.

@@ -173,6 +173,41 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
+// Keeps a register value where it is: the empty asm reads and rewrites it, so the arithmetic
+// that produces the value cannot be moved below this point.  Without it the compiler sinks a
+// block's softmax arithmetic across the branches between pipeline phases, next to the MFMAs
+// that consume it, where it runs as one stretch of vector work with the matrix unit idle
+// instead of in the MFMA slots it was written into.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Buffer resource over `bytes` bytes at `base` for loads into registers (reads past the end
+// return zeros); the compiler tracks these loads like any other and inserts the wait before
+// the first use of a result.  The resource type exists only for the GPU target; the host
+// pass of a single-source file parses the device code with a placeholder.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t reg_rsrc_t;
+__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset voff + soff (AUX: cache policy bits)
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+__device__ __forceinline__ float reg_ld4f(reg_rsrc_t r, uint32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+#else
+struct reg_rsrc_t { uint32_t w[4]; };
+__device__ __forceinline__ reg_rsrc_t reg_rsrc(const void*, int64_t) { return reg_rsrc_t{}; }
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t, uint32_t, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ float reg_ld4f(reg_rsrc_t, uint32_t) { return 0.f; }
+#endif
+
 // SIZE bytes per lane from src + voff into LDS at lds + byte_off + SIZE * lane (wave-uniform
 // destination).  Written as inline assembly on purpose: the compiler then does not treat the
 // copy as an LDS store that may alias the LDS reads after it, and does not make those reads

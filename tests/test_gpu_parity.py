@@ -37,6 +37,9 @@ CASES = {
     # padded batch with an additive mask, extra random -inf keys and a fully masked row
     "padded_mask_d128": W["padded_mask_2k"].scaled(B=3, Hq=2, Hkv=2, Lq=260, Lk=260,
                                                    len_range=(64, 260), seed=16),
+    # the mask at d = 64 (mask tiles copied with the Q/dO tiles, two tiles in flight)
+    "padded_mask_d64": W["padded_mask_2k"].scaled(B=2, Hq=2, Hkv=1, Lq=333, Lk=333, D=64,
+                                                  len_range=(100, 333), seed=23),
     # the same inputs, mask only (no length arrays)
     "padded_mask_only_d128": W["padded_mask_2k"].scaled(B=3, Hq=2, Hkv=2, Lq=260, Lk=260,
                                                         len_range=(64, 260), seed=16, lens="none_keep"),
