@@ -38,12 +38,13 @@ HEADLINE = "mha_causal_1k"
 # kernel-name fragments (as rocprofv3 reports them) of each launch stage
 KERNEL_NAMES = {
     "fwd": "fwd_bf16_kernel", "prep": "bwd_prep_kernel", "dkdv": "bwd_dkdv_kernel",
-    "dq": "bwd_dq_kernel", "decode_split": "decode_split_kernel",
+    "dq": "bwd_dq_kernel", "main": "bwd_fused_kernel", "decode_split": "decode_split_kernel",
     "decode_combine": "decode_combine_kernel",
 }
 # source file of each kernel (traffic counters are dropped once the source changes)
 KERNEL_SOURCES = {
     "fwd": "fwd_bf16.hip", "prep": "bwd_bf16.hip", "dkdv": "bwd_bf16.hip", "dq": "bwd_bf16.hip",
+    "main": "bwd_bf16.hip",
     "decode_split": "decode_bf16.hip", "decode_combine": "decode_bf16.hip",
 }
 
@@ -76,7 +77,15 @@ def flops(w, pairs):
     fwd = 2 * (w.D + w.D) * pairs
     bwd = 2 * (3 * w.D + 2 * w.D) * pairs
     # per-kernel algorithmic shares of the backward: dK/dV does S, dP, dV, dK; dQ adds dQ
-    return {"fwd": fwd, "bwd": bwd, "dkdv": 2 * (2 * w.D + 2 * w.D) * pairs, "dq": 2 * w.D * pairs}
+    # (the one-launch dK/dV + dQ kernel does all of the backward's matrix products)
+    return {"fwd": fwd, "bwd": bwd, "dkdv": 2 * (2 * w.D + 2 * w.D) * pairs, "dq": 2 * w.D * pairs,
+            "main": bwd}
+
+
+def fused_backward(w, has_mask) -> bool:
+    """Whether the library runs dK/dV and dQ in one launch for this workload (d = 64, bf16,
+    no mask), as sdpa_backward_main documents."""
+    return w.dtype == "bf16" and w.D == 64 and not has_mask
 
 
 class Timer:
@@ -169,9 +178,12 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
                           inp["scale"], inp["is_causal"], inp["len_q"], inp["len_kv"])
         bc.launch()
         torch.cuda.synchronize()
-        for st in ("prep", "dkdv", "dq"):
+        # prep and the two main passes as the library runs them ("main": one launch at
+        # d = 64 without a mask), and the two passes as separate launches for reference
+        for st in ("prep", "main", "dkdv", "dq"):
             t[st] = kernel_ms(timer, lambda st=st: bc.launch(st), reps=10, iters=iters)
-        t["bwd"] = t["prep"] + t["dkdv"] + t["dq"]
+        t["bwd"] = t["prep"] + t["main"]
+        res["fused_backward"] = fused_backward(w, inp["mask"] is not None)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     tf = {"fwd": fl["fwd"] / (t["fwd"] * 1e-3) / 1e12}
     if "bwd" in t:
@@ -341,9 +353,7 @@ def main():
 
     def step():
         fc.launch()
-        bc.launch("prep")
-        bc.launch("dkdv")
-        bc.launch("dq")
+        bc.launch()  # the whole backward: prep, then dK/dV and dQ
 
     g = timer.capture(step)
     # the replayed graph must reproduce the eager step bit for bit
@@ -374,7 +384,8 @@ def main():
     value = (gfl["fwd"] + gfl["bwd"]) * 1e9 / (ms_per_step * 1e-3) / 1e12
 
     # ---- dominant kernel of the step and its roofline
-    kt = {k: head["ms"][k] for k in ("fwd", "prep", "dkdv", "dq")}
+    stages = ("fwd", "prep", "main") if head["fused_backward"] else ("fwd", "prep", "dkdv", "dq")
+    kt = {k: head["ms"][k] for k in stages}
     dom = max(kt, key=kt.get)
     if dom == "prep":
         nbytes = w.B * w.Hq * w.Lq * (2 * w.D * 2 + 4)
@@ -395,7 +406,9 @@ def main():
         "gpu_ms_per_step": round(gpu_ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": HEADLINE, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.Lq, "D": w.D,
-                   "causal": True, "step": "fwd + bwd (prep, dkdv, dq)"},
+                   "causal": True,
+                   "step": "fwd + bwd (prep, then dK/dV and dQ"
+                           + (" in one launch)" if head["fused_backward"] else ")")},
         "peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "kernels_ms": kt,

@@ -128,12 +128,15 @@ sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, c
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages sdpa_backward runs, in this order, for callers that schedule them
- * themselves.  Same arguments, validation and workspace as sdpa_backward.
+ * The stages sdpa_backward runs, for callers that schedule them themselves.  Same
+ * arguments, validation and workspace as sdpa_backward.
  *   prep: D_i = rowsum(dO o O)_i and LSE_i * log2(e) (fp32, into the workspace; D = 0 and
  *         +inf for empty rows);
  *   dkdv: dK and dV (reads D from the workspace);
  *   dq:   dQ       (reads D from the workspace).
+ *   main: dkdv and dq in one call (after prep), which is what sdpa_backward runs after its
+ *         prep: at d = 64 without a mask the two passes share one launch, dQ work filling
+ *         the CUs that the dK/dV work leaves idle; otherwise dkdv then dq.
  * Once prep has finished, dkdv and dq are independent of each other and may run
  * concurrently on two streams.  Source: the backward of tinyllm L5.1 section 2.3, with D
  * computed from the output as that section's identity D_i = dO_i . o_i allows.
@@ -153,6 +156,11 @@ sdpa_status sdpa_backward_dq(const sdpa_problem* p, const void* q, const void* k
                              const void* mask_or_null, const int32_t* seq_lens_q_or_null,
                              const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, void* stream);
+sdpa_status sdpa_backward_main(const sdpa_problem* p, const void* q, const void* k,
+                               const void* v, const void* o, const void* dO, const float* lse,
+                               const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                               const int32_t* seq_lens_kv_or_null, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Ragged (packed) sequences.  The operation and every argument shared with sdpa_forward /

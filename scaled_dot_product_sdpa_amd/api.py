@@ -32,10 +32,11 @@ SDPA_DTYPE_BF16 = 1
 EXPORTS = (
     "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes", "sdpa_forward",
     "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
+    "sdpa_backward_main",
     "sdpa_status_string", "sdpa_last_error", "sdpa_version", "sdpa_decode_paged_workspace_bytes",
     "sdpa_decode_paged", "sdpa_forward_ragged", "sdpa_backward_ragged",
 )
-BACKWARD_STAGES = ("prep", "dkdv", "dq")
+BACKWARD_STAGES = ("prep", "dkdv", "dq", "main")
 
 
 class Problem(ctypes.Structure):
@@ -90,7 +91,8 @@ def load_library(path: Path | str | None = None):
     lib.sdpa_backward_workspace_bytes.restype = sz
     lib.sdpa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_forward.restype = ctypes.c_int
-    for name in ("sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq"):
+    for name in ("sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
+                 "sdpa_backward_main"):
         f = getattr(lib, name)
         f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = ctypes.c_int
@@ -346,8 +348,8 @@ class ForwardCall:
 
 class BackwardCall:
     """Marshalled backward: dq, dk, dv and the workspace are allocated once; ``launch()``
-    runs all stages, ``launch(stage)`` one of "prep", "dkdv", "dq" (prep must precede the
-    other two).  Ragged arguments as in ``ForwardCall`` (o and dO then packed like q; only
+    runs all stages, ``launch(stage)`` one of "prep", "dkdv", "dq", "main" (dkdv and dq in
+    one call; prep must precede the others).  Ragged arguments as in ``ForwardCall`` (o and dO then packed like q; only
     the whole backward is offered)."""
 
     def __init__(self, q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
@@ -407,7 +409,8 @@ class BackwardCall:
             self.fns = {"all": self.lib.sdpa_backward_ragged}
         else:
             self.fns = {"all": self.lib.sdpa_backward, "prep": self.lib.sdpa_backward_prep,
-                        "dkdv": self.lib.sdpa_backward_dkdv, "dq": self.lib.sdpa_backward_dq}
+                        "dkdv": self.lib.sdpa_backward_dkdv, "dq": self.lib.sdpa_backward_dq,
+                        "main": self.lib.sdpa_backward_main}
 
     def launch(self, stage: str = "all"):
         if stage not in self.fns:

@@ -79,8 +79,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kQT = 64;  // query rows per LDS tile (two 32-row blocks)
 
+// LDS bytes of the dK/dV body: three Q, dO tiles, lse2/D rows and (with a mask) mask tiles.
+template <int D, int NW, bool MASK>
+constexpr int dkdv_lds_bytes() {
+  return 3 * (2 * kQT * D * 2 + 2 * kQT * 4 + (MASK ? kQT * 32 * NW : 8) * 2);
+}
+
+// Workgroup `bid` of `nblk` (the dK/dV grid), LDS at smem.
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, char* smem) {
   constexpr int KT = 32 * NW;    // keys per workgroup
   constexpr int TILE = kQT * D;
   constexpr int NS = D / 16;     // MFMAs of one S (or dP) block
@@ -94,19 +101,20 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // one wave per SIMD nothing else covers the wait; d = 128 has no registers to spare.
   constexpr int TPRE = D == 64 ? 3 : 2;
   constexpr int APRE = D == 64 ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) bf16 Q0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Q1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Q2[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 G0[TILE];  // dO
-  __shared__ __attribute__((aligned(16))) bf16 G1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 G2[TILE];
-  __shared__ __attribute__((aligned(16))) float R0[2 * kQT];  // lse2 rows, then D rows
-  __shared__ __attribute__((aligned(16))) float R1s[2 * kQT];
-  __shared__ __attribute__((aligned(16))) float R2s[2 * kQT];
+  bf16* const Q0 = reinterpret_cast<bf16*>(smem);
+  bf16* const Q1 = Q0 + TILE;
+  bf16* const Q2 = Q1 + TILE;
+  bf16* const G0 = Q2 + TILE;  // dO
+  bf16* const G1 = G0 + TILE;
+  bf16* const G2 = G1 + TILE;
+  float* const R0 = reinterpret_cast<float*>(G2 + TILE);  // lse2 rows, then D rows
+  float* const R1s = R0 + 2 * kQT;
+  float* const R2s = R1s + 2 * kQT;
   // mask tiles (kQT rows x KT keys, unswizzled), used when mask rows allow 16-byte copies
-  __shared__ __attribute__((aligned(16))) bf16 M0[MT];
-  __shared__ __attribute__((aligned(16))) bf16 M1[MT];
-  __shared__ __attribute__((aligned(16))) bf16 M2[MT];
+  bf16* const M0 = reinterpret_cast<bf16*>(R2s + 2 * kQT);
+  bf16* const M1 = M0 + MT;
+  bf16* const M2 = M1 + MT;
+  static_assert(6 * TILE * 2 + 6 * kQT * 4 + 3 * MT * 2 == dkdv_lds_bytes<D, NW, MASK>(), "LDS layout");
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // Work item: (batch, KV head) group, then key tile kt; low key tiles see the most
   // (causal) queries and are launched first.
   int bg, kt;
-  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), 1, !CAUSAL, bg, kt);
+  xcd_item(bid, p.B * p.Hkv, nblk / (p.B * p.Hkv), 1, !CAUSAL, bg, kt);
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int q_end = seq_len_q(p, b);
@@ -406,13 +414,23 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+template <int D, int NW, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<D, NW, MASK>()];
+  dkdv_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, gridDim.x, smem);
+}
+
 // ---------------------------------------------------------------------------------------
 // 3. dQ (query-stationary)
 // ---------------------------------------------------------------------------------------
 constexpr int kBN = 64;
 
+// LDS bytes of the pipelined dQ body: three K and three V tiles.
+template <int D>
+constexpr int dq_lds_bytes() { return 6 * kBN * D * 2; }
+
 template <int D, int NW, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, char* smem) {
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
   constexpr int NS = D / 16;   // MFMAs of one S^T (or dP^T) block
@@ -420,12 +438,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int R1 = 2 * NT;   // slots of region 1 (dQ MFMAs)
   constexpr int R2 = 2 * NS;   // slots of region 2 (S^T, dP^T MFMAs)
   constexpr int E1 = 16 / R1;  // scores per lane per region-1 slot
-  __shared__ __attribute__((aligned(16))) bf16 K0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 K2[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
-  __shared__ __attribute__((aligned(16))) bf16 V2[TILE];
+  bf16* const K0 = reinterpret_cast<bf16*>(smem);
+  bf16* const K1 = K0 + TILE;
+  bf16* const K2 = K1 + TILE;
+  bf16* const V0 = K2 + TILE;
+  bf16* const V1 = V0 + TILE;
+  bf16* const V2 = V1 + TILE;
+  static_assert(6 * TILE * 2 == dq_lds_bytes<D>(), "LDS layout");
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -436,7 +455,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // Work item: (batch, KV head) group, then query tile `rank` of head h of the group.
   int gi, r;
-  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
+  xcd_item(bid, p.B * p.Hkv, nblk / (p.B * p.Hkv), p.G, !CAUSAL, gi, r);
   const int b = gi / p.Hkv;
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
@@ -686,6 +705,25 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 
 template <int D, int NW, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<D>()];
+  dq_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, gridDim.x, smem);
+}
+
+// dK/dV and dQ in one launch: workgroups [0, n_dkdv) run the dK/dV body (heavy key tiles
+// first), the rest the dQ body, so dQ work fills the CUs that the dK/dV tail leaves idle
+// and no launch boundary separates the two.  Both bodies fit two waves per SIMD (d = 64).
+// n_dkdv is a multiple of 8 whenever the XCD-aware item order is used, so the dQ items
+// keep their XCD.
+template <int D, int NW, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_fused_kernel(BwdArgs a, int n_dkdv) {
+  constexpr int kL1 = dkdv_lds_bytes<D, NW, MASK>(), kL2 = dq_lds_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char smem[kL1 > kL2 ? kL1 : kL2];
+  if ((int)blockIdx.x < n_dkdv) dkdv_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, n_dkdv, smem);
+  else dq_body<D, NW, CAUSAL, MASK>(a, blockIdx.x - n_dkdv, gridDim.x - n_dkdv, smem);
+}
+
+template <int D, int NW, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;
@@ -866,14 +904,24 @@ template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   constexpr int KNW = BwdShape<D>::KV_NW, QNW = BwdShape<D>::Q_NW;
   const int n_kt = (a.p.Lk + 32 * KNW - 1) / (32 * KNW);
+  constexpr int BM = 32 * QNW;
+  const int n_qt = (a.p.Lq + BM - 1) / BM;
+  if constexpr (BwdShape<D>::PIPE_DQ && KNW == QNW && !MASK) {
+    // both passes in one launch (see bwd_fused_kernel)
+    if ((stages & kBwdDkdv) && (stages & kBwdDq)) {
+      const int n_dkdv = n_kt * a.p.B * a.p.Hkv, n_dq = n_qt * a.p.B * a.p.Hq;
+      if (n_dkdv + n_dq > 0)
+        hipLaunchKernelGGL((bwd_fused_kernel<D, KNW, CAUSAL, MASK>), dim3(n_dkdv + n_dq), dim3(64 * KNW), 0, s,
+                           a, n_dkdv);
+      return hipGetLastError();
+    }
+  }
   if ((stages & kBwdDkdv) && n_kt > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CAUSAL, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
                        dim3(64 * KNW), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int BM = 32 * QNW;
-  const int n_qt = (a.p.Lq + BM - 1) / BM;
   if ((stages & kBwdDq) && n_qt > 0) {
     if constexpr (BwdShape<D>::PIPE_DQ)
       hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq),

@@ -313,6 +313,9 @@ sdpa_status sdpa_backward(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdAll,
 sdpa_status sdpa_backward_prep(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdPrep, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dkdv(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDkdv, SDPA_BWD_PASS); }
 sdpa_status sdpa_backward_dq(SDPA_BWD_ARGS) { return backward_stages(sdpa::kBwdDq, SDPA_BWD_PASS); }
+sdpa_status sdpa_backward_main(SDPA_BWD_ARGS) {
+  return backward_stages(sdpa::kBwdDkdv | sdpa::kBwdDq, SDPA_BWD_PASS);
+}
 
 sdpa_status sdpa_backward_ragged(const sdpa_problem* p, const void* q, const void* k,
                                  const void* v, const void* o, const void* dO, const float* lse,

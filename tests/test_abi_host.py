@@ -124,7 +124,7 @@ def test_prefill_and_backward_workspace(lib):
 
 
 @pytest.mark.parametrize("stage", ["sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv",
-                                   "sdpa_backward_dq"])
+                                   "sdpa_backward_dq", "sdpa_backward_main"])
 def test_backward_rejects(lib, stage):
     p = _problem()
     assert _bwd(lib, p, lse=None, stage=stage) == SDPA_ERR_INVALID_ARGUMENT

@@ -167,6 +167,31 @@ def test_graph_replay_matches_eager():
             assert torch.equal(a, b), f"replay {rep} differs"
 
 
+@pytest.mark.parametrize("D,mask", [(64, False), (64, True), (128, False)])
+def test_backward_stages_equal_whole(D, mask):
+    """prep + dkdv + dq as separate calls, prep + main, and the whole backward give the same
+    gradients bit for bit (at d = 64 without a mask "main" runs both passes in one launch)."""
+    banner(f"backward stages d={D} mask={mask}")
+    base = WORKLOADS["padded_mask_2k"] if mask else WORKLOADS["gqa_causal_4k"]
+    w = base.scaled(B=2, Hq=4, Hkv=2, Lq=300, Lk=300, D=D, seed=36, len_range=(100, 300))
+    d = to_dev(make_inputs(w))
+    fc = ForwardCall(d["q"], d["k"], d["v"], d["mask"], d["scale"], w.causal, d["len_q"], d["len_kv"])
+    fc.launch()
+    bc = BackwardCall(d["q"], d["k"], d["v"], fc.o, d["dO"], fc.lse, d["mask"], d["scale"], w.causal,
+                      d["len_q"], d["len_kv"])
+    results = []
+    for stages in (["all"], ["prep", "dkdv", "dq"], ["prep", "main"]):
+        for t in (bc.dq, bc.dk, bc.dv):
+            t.fill_(7.0)
+        for st in stages:
+            bc.launch(st)
+        torch.cuda.synchronize()
+        results.append([t.clone() for t in (bc.dq, bc.dk, bc.dv)])
+    for r in results[1:]:
+        for a, b in zip(results[0], r):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_stale_lds_does_not_leak(D):
     """LDS left full of NaN by an earlier launch of the same kernels (all-NaN inputs, so
