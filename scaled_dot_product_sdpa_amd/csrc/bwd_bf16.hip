@@ -52,9 +52,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   float acc = 0.f;
   bool valid = false;
   if (row < nrows) {
-    const int i = (int)(row % p.Lq);
-    const int h = (int)((row / p.Lq) % p.Hq);
-    const int b = (int)(row / ((int64_t)p.Lq * p.Hq));
+    int i, h, b;
+    if (nrows < ((int64_t)1 << 31)) {  // 32-bit index arithmetic (64-bit division is slow)
+      const uint32_t r32 = (uint32_t)row, bh = r32 / (uint32_t)p.Lq;
+      i = (int)(r32 - bh * (uint32_t)p.Lq);
+      b = (int)(bh / (uint32_t)p.Hq);
+      h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
+    } else {
+      i = (int)(row % p.Lq);
+      h = (int)((row / p.Lq) % p.Hq);
+      b = (int)(row / ((int64_t)p.Lq * p.Hq));
+    }
     const int q_end = seq_len_q(p, b);
     if (i < q_end) {
       valid = true;
