@@ -295,7 +295,7 @@ def summarize_trace(stats_csv, out_md, command):
         if "sdpa::" not in n:
             continue
         n = n.replace("void sdpa::(anonymous namespace)::", "")
-        for t in ("(sdpa::BwdArgs)", "(sdpa::FwdArgs)", "(sdpa::DecodeArgs)"):
+        for t in ("(sdpa::BwdArgs, int)", "(sdpa::BwdArgs)", "(sdpa::FwdArgs)", "(sdpa::DecodeArgs)"):
             n = n.replace(t, "")
         lines.append(f"| `{n}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {tot:.3f} |")
     Path(out_md).write_text("\n".join(lines) + "\n")
