@@ -7,6 +7,12 @@
 // backward pass (dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = a dS K, dK = a dS^T Q,
 // D_i = dO_i . O_i).  The backward recomputes P_ij = exp(S_ij - LSE_i) from the forward's
 // LSE, as the FlashAttention-2 row of that page's "Going further" table describes.
+//
+// A workgroup is one wave of 64 rows of one (batch, head) (keys of one (batch, KV head) for
+// dK, dV).  The rows its 64 threads loop over (keys, or query rows) are the same for every
+// thread, so they are staged through LDS in chunks and read back as broadcasts; each
+// thread's arithmetic is the plain per-row definition (two passes for the forward: the row
+// max, then the weights and the weighted sum).
 #include "kern_common.h"
 #include "launch.h"
 
@@ -15,143 +21,202 @@ namespace {
 
 constexpr int kTpb = 64;
 
+// rows staged per chunk: 8 KB of fp32 per staged matrix
+template <int D>
+constexpr int chunk_rows() { return 2048 / D; }
+
 struct RowCtx {
   int b, h, g, i;
-  int q_end, kv_end, stop;  // stop: keys [0, stop) are candidates
+  int q_end, kv_end, stop;  // stop: keys [0, stop) are visible (before the mask)
   int coff;                 // causal diagonal offset: key j visible iff j <= i + coff
 };
 
-__device__ __forceinline__ bool key_visible(const Problem& p, const RowCtx& r, int j) {
-  return j < r.kv_end && r.i < r.q_end && (!p.causal || j <= r.i + r.coff);
-}
-
-__device__ __forceinline__ RowCtx row_ctx(const Problem& p, int64_t row) {
+__device__ __forceinline__ RowCtx row_ctx(const Problem& p, int b, int h, int i) {
   RowCtx r;
-  r.i = (int)(row % p.Lq);
-  r.h = (int)((row / p.Lq) % p.Hq);
-  r.b = (int)(row / ((int64_t)p.Lq * p.Hq));
-  r.g = r.h / p.G;
-  r.q_end = seq_len_q(p, r.b);
-  r.kv_end = seq_len_kv(p, r.b);
+  r.b = b;
+  r.h = h;
+  r.i = i;
+  r.g = h / p.G;
+  r.q_end = seq_len_q(p, b);
+  r.kv_end = seq_len_kv(p, b);
   r.coff = causal_offset(p.causal, r.q_end, r.kv_end);
-  r.stop = (r.i < r.q_end) ? (p.causal ? max(0, min(r.kv_end, r.i + 1 + r.coff)) : r.kv_end) : 0;
+  r.stop = (i < r.q_end) ? (p.causal ? max(0, min(r.kv_end, i + 1 + r.coff)) : r.kv_end) : 0;
   return r;
 }
 
-// Score of (row, key j) in natural-log units, -inf if the pair is blocked.
+// Keys [0, stop) some row of the workgroup's block [i0, i0 + 64) can see (uniform).
+__device__ __forceinline__ int block_stop(const Problem& p, const RowCtx& r, int i0) {
+  const int last = min(i0 + kTpb, r.q_end) - 1;
+  if (last < i0) return 0;
+  return p.causal ? max(0, min(r.kv_end, last + 1 + r.coff)) : r.kv_end;
+}
+
+// a . b over D elements as four interleaved partial sums (shorter dependency chains than
+// one running sum; the four are added pairwise at the end)
+template <int D>
+__device__ __forceinline__ float dot4(const float* a, const float* b) {
+  float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+  for (int t = 0; t < D; t += 4) {
+    d0 = fmaf(a[t], b[t], d0);
+    d1 = fmaf(a[t + 1], b[t + 1], d1);
+    d2 = fmaf(a[t + 2], b[t + 2], d2);
+    d3 = fmaf(a[t + 3], b[t + 3], d3);
+  }
+  return (d0 + d1) + (d2 + d3);
+}
+
+// Copy rows [j0, j0 + n) of a row-major fp32 matrix (row stride ld) into LDS rows of D.
+template <int D>
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, int64_t ld, int j0, int n) {
+  for (int e = threadIdx.x; e < n * D; e += kTpb) dst[e] = src[(int64_t)(j0 + e / D) * ld + e % D];
+}
+
+__device__ __forceinline__ float mask_at(const Problem& p, const RowCtx& r, int j) {
+  const float* m = reinterpret_cast<const float*>(p.mask) + r.b * p.m_sb + r.h * p.m_sh +
+                   (int64_t)r.i * p.m_si;
+  return m[j];
+}
+
+// Score of (row, staged key row kj) in natural-log units (-inf where the mask blocks it).
 template <int D>
 __device__ __forceinline__ float score(const Problem& p, const RowCtx& r, const float* qv,
-                                       const float* kbase, int j) {
-  if (!key_visible(p, r, j)) return kNegInf;
-  const float* kj = kbase + (int64_t)j * p.k_sl;
-  float dot = 0.f;
-#pragma unroll
-  for (int t = 0; t < D; ++t) dot = fmaf(qv[t], kj[t], dot);
-  float s = dot * p.scale;
-  if (p.mask) {
-    const float* m = reinterpret_cast<const float*>(p.mask) + r.b * p.m_sb + r.h * p.m_sh +
-                     (int64_t)r.i * p.m_si;
-    s += m[j];
-  }
+                                       const float* kj, int j) {
+  float s = dot4<D>(qv, kj) * p.scale;
+  if (p.mask) s += mask_at(p, r, j);
   return s;
 }
 
+// Workgroup -> (batch, head, first row) in a grid of n_rb row blocks per (batch, head).
+__device__ __forceinline__ void block_rows(int n_rb, int H, int& b, int& h, int& i0) {
+  const int bh = blockIdx.x / n_rb;
+  i0 = (blockIdx.x - bh * n_rb) * kTpb;
+  b = bh / H;
+  h = bh - b * H;
+}
+
 template <int D>
-__global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a, int n_rb) {
+  constexpr int CH = chunk_rows<D>();
+  __shared__ float Ks[CH * D], Vs[CH * D];
   const Problem& p = a.p;
-  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
-  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
-  const RowCtx r = row_ctx(p, row);
-  const float* qrow = reinterpret_cast<const float*>(a.q) + q_base(p, r.b) + r.h * p.q_sh +
-                      (int64_t)r.i * p.q_sl;
-  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, r.b) + r.g * p.k_sh;
-  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, r.b) + r.g * p.v_sh;
+  int b, h, i0;
+  block_rows(n_rb, p.Hq, b, h, i0);
+  const int i = i0 + threadIdx.x;
+  const RowCtx r = row_ctx(p, b, h, i);
+  const int stop_blk = block_stop(p, r, i0);
+  const bool live = i < r.q_end;
+  const float* qrow = reinterpret_cast<const float*>(a.q) + q_base(p, b) + h * p.q_sh +
+                      (int64_t)i * p.q_sl;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, b) + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, b) + r.g * p.v_sh;
   float qv[D], acc[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) {
-    qv[t] = (r.i < r.q_end) ? qrow[t] : 0.f;
+    qv[t] = live ? qrow[t] : 0.f;
     acc[t] = 0.f;
   }
   // pass 1: row max
   float m = kNegInf;
-  for (int j = 0; j < r.stop; ++j) m = fmaxf(m, score<D>(p, r, qv, kbase, j));
-  // pass 2: weights and weighted sum of values
+  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+    const int n = min(CH, stop_blk - c0);
+    __syncthreads();
+    stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
+    __syncthreads();
+    for (int jj = 0; jj < n; ++jj)
+      if (c0 + jj < r.stop) m = fmaxf(m, score<D>(p, r, qv, Ks + jj * D, c0 + jj));
+  }
+  // pass 2: weights and weighted sum of values (a masked pair has weight exp(-inf) = 0)
   float l = 0.f;
-  if (m != kNegInf) {
-    for (int j = 0; j < r.stop; ++j) {
-      const float s = score<D>(p, r, qv, kbase, j);
-      if (s == kNegInf) continue;
-      const float e = expf(s - m);
+  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+    const int n = min(CH, stop_blk - c0);
+    __syncthreads();
+    stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
+    stage_rows<D>(Vs, vbase, p.v_sl, c0, n);
+    __syncthreads();
+    if (m == kNegInf) continue;
+    for (int jj = 0; jj < n; ++jj) {
+      if (c0 + jj >= r.stop) continue;
+      const float e = expf(score<D>(p, r, qv, Ks + jj * D, c0 + jj) - m);
       l += e;
-      const float* vj = vbase + (int64_t)j * p.v_sl;
+      const float* vj = Vs + jj * D;
 #pragma unroll
       for (int t = 0; t < D; ++t) acc[t] = fmaf(e, vj[t], acc[t]);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (r.i < q_rows_out(p, r.q_end)) {
-    float* orow = reinterpret_cast<float*>(a.o) + o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+  if (i < q_rows_out(p, r.q_end)) {
+    float* orow = reinterpret_cast<float*>(a.o) + o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
 #pragma unroll
     for (int t = 0; t < D; ++t) orow[t] = acc[t] * inv;
   }
-  if (a.lse) a.lse[row] = l > 0.f ? m + logf(l) : kNegInf;
+  if (a.lse && i < p.Lq) a.lse[((int64_t)b * p.Hq + h) * p.Lq + i] = l > 0.f ? m + logf(l) : kNegInf;
 }
 
 // D_i = dO_i . O_i: one thread per query row (0 for empty rows).
 template <int D>
-__global__ __launch_bounds__(kTpb) void bwd_prep_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kTpb) void bwd_prep_f32_kernel(BwdArgs a, int n_rb) {
   const Problem& p = a.p;
-  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
-  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
-  const RowCtx r = row_ctx(p, row);
+  int b, h, i0;
+  block_rows(n_rb, p.Hq, b, h, i0);
+  const int i = i0 + threadIdx.x;
+  if (i >= p.Lq) return;
+  const int q_end = seq_len_q(p, b);
   float Di = 0.f;
-  if (r.i < r.q_end) {
-    const int64_t ooff = o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
+  if (i < q_end) {
+    const int64_t ooff = o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
     const float* orow = reinterpret_cast<const float*>(a.o) + ooff;
     const float* drow = reinterpret_cast<const float*>(a.dO) + ooff;
 #pragma unroll
     for (int t = 0; t < D; ++t) Di = fmaf(drow[t], orow[t], Di);
   }
-  a.dsum[row] = Di;
+  a.dsum[((int64_t)b * p.Hq + h) * p.Lq + i] = Di;
 }
 
 // dQ_i: one thread per query row.
 template <int D>
-__global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a, int n_rb) {
+  constexpr int CH = chunk_rows<D>();
+  __shared__ float Ks[CH * D], Vs[CH * D];
   const Problem& p = a.p;
-  const int64_t row = (int64_t)blockIdx.x * kTpb + threadIdx.x;
-  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
-  const RowCtx r = row_ctx(p, row);
-  const int64_t qoff = q_base(p, r.b) + r.h * p.q_sh + (int64_t)r.i * p.q_sl;
-  const int64_t ooff = o_base(p, r.b) + r.h * p.o_sh + (int64_t)r.i * p.o_sl;
-  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, r.b) + r.g * p.k_sh;
-  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, r.b) + r.g * p.v_sh;
+  int b, h, i0;
+  block_rows(n_rb, p.Hq, b, h, i0);
+  const int i = i0 + threadIdx.x;
+  const RowCtx r = row_ctx(p, b, h, i);
+  const int stop_blk = block_stop(p, r, i0);
+  const int64_t qoff = q_base(p, b) + h * p.q_sh + (int64_t)i * p.q_sl;
+  const int64_t ooff = o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
+  const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, b) + r.g * p.k_sh;
+  const float* vbase = reinterpret_cast<const float*>(a.v) + v_base(p, b) + r.g * p.v_sh;
   float qv[D], dov[D], dq[D];
-  const bool ok = r.i < r.q_end;
+  const bool ok = i < r.q_end;
 #pragma unroll
   for (int t = 0; t < D; ++t) {
     qv[t] = ok ? reinterpret_cast<const float*>(a.q)[qoff + t] : 0.f;
     dov[t] = ok ? reinterpret_cast<const float*>(a.dO)[ooff + t] : 0.f;
     dq[t] = 0.f;
   }
-  const float Di = a.dsum[row];
-  const float lse = a.lse[row];
-  if (ok && lse != kNegInf) {
-    for (int j = 0; j < r.stop; ++j) {
-      const float s = score<D>(p, r, qv, kbase, j);
-      if (s == kNegInf) continue;
-      const float P = expf(s - lse);
-      const float* vj = vbase + (int64_t)j * p.v_sl;
-      float dP = 0.f;
-#pragma unroll
-      for (int t = 0; t < D; ++t) dP = fmaf(dov[t], vj[t], dP);
-      const float dS = P * (dP - Di);
-      const float* kj = kbase + (int64_t)j * p.k_sl;
+  const int64_t row = ((int64_t)b * p.Hq + h) * p.Lq + i;
+  const float Di = ok ? a.dsum[row] : 0.f;
+  const float lse = ok ? a.lse[row] : kNegInf;
+  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+    const int n = min(CH, stop_blk - c0);
+    __syncthreads();
+    stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
+    stage_rows<D>(Vs, vbase, p.v_sl, c0, n);
+    __syncthreads();
+    if (lse == kNegInf) continue;
+    for (int jj = 0; jj < n; ++jj) {
+      if (c0 + jj >= r.stop) continue;
+      const float* kj = Ks + jj * D;
+      const float P = expf(score<D>(p, r, qv, kj, c0 + jj) - lse);  // 0 for a masked pair
+      const float* vj = Vs + jj * D;
+      const float dS = P * (dot4<D>(dov, vj) - Di);
 #pragma unroll
       for (int t = 0; t < D; ++t) dq[t] = fmaf(dS, kj[t], dq[t]);
     }
   }
-  if (r.i < q_rows_out(p, r.q_end)) {
+  if (i < q_rows_out(p, r.q_end)) {
     float* dqrow = reinterpret_cast<float*>(a.dq) + qoff;
 #pragma unroll
     for (int t = 0; t < D; ++t) dqrow[t] = dq[t] * p.scale;
@@ -161,55 +226,66 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a) {
 // dK_j and dV_j: one thread per key row of a KV head, summing over the query heads it
 // serves and over their rows.
 template <int D>
-__global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a, int n_kb) {
+  constexpr int CH = chunk_rows<D>();
+  __shared__ float Qs[CH * D], Gs[CH * D], Ls[CH], Ds[CH];
   const Problem& p = a.p;
-  const int64_t krow = (int64_t)blockIdx.x * kTpb + threadIdx.x;
-  if (krow >= (int64_t)p.B * p.Hkv * p.Lk) return;
-  const int j = (int)(krow % p.Lk);
-  const int g = (int)((krow / p.Lk) % p.Hkv);
-  const int b = (int)(krow / ((int64_t)p.Lk * p.Hkv));
+  int b, g, j0;
+  block_rows(n_kb, p.Hkv, b, g, j0);
+  const int j = j0 + threadIdx.x;
   const int kv_end = seq_len_kv(p, b);
   const int q_end = seq_len_q(p, b);
+  const int coff = causal_offset(p.causal, q_end, kv_end);
   const int64_t koff = k_base(p, b) + g * p.k_sh + (int64_t)j * p.k_sl;
   const int64_t voff = v_base(p, b) + g * p.v_sh + (int64_t)j * p.v_sl;
+  const bool ok = j < kv_end;
   float kv[D], vv[D], dk[D], dv[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) {
-    const bool ok = j < kv_end;
     kv[t] = ok ? reinterpret_cast<const float*>(a.k)[koff + t] : 0.f;
     vv[t] = ok ? reinterpret_cast<const float*>(a.v)[voff + t] : 0.f;
     dk[t] = 0.f;
     dv[t] = 0.f;
   }
-  if (j < kv_end) {
-    // first query row that sees key j (row i sees it iff i >= j - offset)
-    const int i_begin = p.causal ? max(0, j - causal_offset(p.causal, q_end, kv_end)) : 0;
+  // first query row that sees key j (row i sees it iff i >= j - offset); the block's first
+  // key bounds the staged rows
+  const int i_begin = p.causal ? max(0, j - coff) : 0;
+  const int i_blk = p.causal ? max(0, j0 - coff) : 0;
+  if (j0 < kv_end) {
     for (int hh = 0; hh < p.G; ++hh) {
       const int h = g * p.G + hh;
-      for (int i = i_begin; i < q_end; ++i) {
-        const int64_t row = ((int64_t)b * p.Hq + h) * p.Lq + i;
-        const float lse = a.lse[row];
-        if (lse == kNegInf) continue;
-        const float* qi = reinterpret_cast<const float*>(a.q) + q_base(p, b) + h * p.q_sh + (int64_t)i * p.q_sl;
-        const float* doi = reinterpret_cast<const float*>(a.dO) + o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
-        float dot = 0.f;
-#pragma unroll
-        for (int t = 0; t < D; ++t) dot = fmaf(qi[t], kv[t], dot);
-        float s = dot * p.scale;
-        if (p.mask) {
-          const float* m = reinterpret_cast<const float*>(p.mask) + b * p.m_sb + h * p.m_sh + (int64_t)i * p.m_si;
-          s += m[j];
+      const float* qb = reinterpret_cast<const float*>(a.q) + q_base(p, b) + h * p.q_sh;
+      const float* gb = reinterpret_cast<const float*>(a.dO) + o_base(p, b) + h * p.o_sh;
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq;
+      const float* mrow = p.mask ? reinterpret_cast<const float*>(p.mask) + b * p.m_sb + h * p.m_sh
+                                 : nullptr;
+      for (int c0 = i_blk; c0 < q_end; c0 += CH) {
+        const int n = min(CH, q_end - c0);
+        __syncthreads();
+        stage_rows<D>(Qs, qb, p.q_sl, c0, n);
+        stage_rows<D>(Gs, gb, p.o_sl, c0, n);
+        for (int e = threadIdx.x; e < n; e += kTpb) {
+          Ls[e] = a.lse[rb + c0 + e];
+          Ds[e] = a.dsum[rb + c0 + e];
         }
-        if (s == kNegInf) continue;
-        const float P = expf(s - lse);
-        float dP = 0.f;
+        __syncthreads();
+        if (!ok) continue;
+        for (int ii = 0; ii < n; ++ii) {
+          const int i = c0 + ii;
+          if (i < i_begin) continue;
+          const float lse = Ls[ii];
+          const float* qi = Qs + ii * D;
+          const float* doi = Gs + ii * D;
+          float s = dot4<D>(qi, kv) * p.scale;
+          if (mrow) s += mrow[(int64_t)i * p.m_si + j];
+          // a row with no visible key (LSE = -inf) or a masked pair gets P = 0
+          const float P = (lse == kNegInf || s == kNegInf) ? 0.f : expf(s - lse);
+          const float dS = P * (dot4<D>(doi, vv) - Ds[ii]);
 #pragma unroll
-        for (int t = 0; t < D; ++t) dP = fmaf(doi[t], vv[t], dP);
-        const float dS = P * (dP - a.dsum[row]);
-#pragma unroll
-        for (int t = 0; t < D; ++t) {
-          dv[t] = fmaf(P, doi[t], dv[t]);
-          dk[t] = fmaf(dS, qi[t], dk[t]);
+          for (int t = 0; t < D; ++t) {
+            dv[t] = fmaf(P, doi[t], dv[t]);
+            dk[t] = fmaf(dS, qi[t], dk[t]);
+          }
         }
       }
     }
@@ -227,29 +303,29 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t fwd_d(const FwdArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)((rows + kTpb - 1) / kTpb)), dim3(kTpb), 0, s, a);
+  const int n_rb = (a.p.Lq + kTpb - 1) / kTpb;
+  const int64_t grid = (int64_t)n_rb * a.p.B * a.p.Hq;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(kTpb), 0, s, a, n_rb);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_d(const BwdArgs& a, int stages, hipStream_t s) {
-  const int64_t qrows = (int64_t)a.p.B * a.p.Hq * a.p.Lq;
-  const int64_t krows = (int64_t)a.p.B * a.p.Hkv * a.p.Lk;
-  const dim3 qgrid((unsigned)((qrows + kTpb - 1) / kTpb)), kgrid((unsigned)((krows + kTpb - 1) / kTpb));
-  if ((stages & kBwdPrep) && qrows > 0) {
-    hipLaunchKernelGGL((bwd_prep_f32_kernel<D>), qgrid, dim3(kTpb), 0, s, a);
+  const int n_rb = (a.p.Lq + kTpb - 1) / kTpb, n_kb = (a.p.Lk + kTpb - 1) / kTpb;
+  const int64_t qgrid = (int64_t)n_rb * a.p.B * a.p.Hq, kgrid = (int64_t)n_kb * a.p.B * a.p.Hkv;
+  if ((stages & kBwdPrep) && qgrid > 0) {
+    hipLaunchKernelGGL((bwd_prep_f32_kernel<D>), dim3((unsigned)qgrid), dim3(kTpb), 0, s, a, n_rb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & kBwdDkdv) && krows > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), kgrid, dim3(kTpb), 0, s, a);
+  if ((stages & kBwdDkdv) && kgrid > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3((unsigned)kgrid), dim3(kTpb), 0, s, a, n_kb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & kBwdDq) && qrows > 0) {
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), qgrid, dim3(kTpb), 0, s, a);
+  if ((stages & kBwdDq) && qgrid > 0) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3((unsigned)qgrid), dim3(kTpb), 0, s, a, n_rb);
   }
   return hipGetLastError();
 }
