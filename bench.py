@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -295,8 +296,7 @@ def summarize_trace(stats_csv, out_md, command):
         if "sdpa::" not in n:
             continue
         n = n.replace("void sdpa::(anonymous namespace)::", "")
-        for t in ("(sdpa::BwdArgs, int)", "(sdpa::BwdArgs)", "(sdpa::FwdArgs)", "(sdpa::DecodeArgs)"):
-            n = n.replace(t, "")
+        n = re.sub(r"\(sdpa::\w+(, int)?\)$", "", n)  # the argument list
         lines.append(f"| `{n}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {tot:.3f} |")
     Path(out_md).write_text("\n".join(lines) + "\n")
     print(Path(out_md).read_text())
