@@ -43,6 +43,7 @@ class _Problem(ctypes.Structure):
         ("mask_stride", ctypes.c_int64 * 4),
         ("scale", ctypes.c_double),
         ("is_causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -88,7 +89,7 @@ class Oracle:
 
     # ---- marshalling -------------------------------------------------------------
     @staticmethod
-    def _problem(q, k, v, mask, scale, is_causal):
+    def _problem(q, k, v, mask, scale, is_causal, window=0):
         if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
             raise ValueError("oracle expects (B, H, L, D) arrays")
         B, Hq, Lq, Dk = q.shape
@@ -100,6 +101,7 @@ class Oracle:
         p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.Dk, p.Dv = B, Hq, Hkv, Lq, Lk, Dk, Dv
         p.scale = math.nan if scale is None else float(scale)
         p.is_causal = causal_mode(is_causal)
+        p.window = int(window)
         m = None
         if mask is not None:
             m = _f64(mask)
@@ -133,9 +135,12 @@ class Oracle:
             raise RuntimeError(f"oracle: status {rc}")
 
     # ---- calls ---------------------------------------------------------------------
-    def forward(self, q, k, v, mask=None, scale=None, is_causal=False, len_q=None, len_kv=None):
+    def forward(self, q, k, v, mask=None, scale=None, is_causal=False, len_q=None, len_kv=None,
+                window=0):
+        """``window`` W > 0 (with a causal diagonal): a row also sees only the last W keys
+        up to its diagonal (the sliding window)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
-        p, m = self._problem(q, k, v, mask, scale, is_causal)
+        p, m = self._problem(q, k, v, mask, scale, is_causal, window)
         lq, lk = self._lens(len_q, p.B), self._lens(len_kv, p.B)
         o = np.zeros((p.B, p.Hq, p.Lq, p.Dv))
         lse = np.zeros((p.B, p.Hq, p.Lq))
@@ -145,10 +150,10 @@ class Oracle:
         return o, lse
 
     def forward_rows(self, q, k, v, rows, mask=None, scale=None, is_causal=False, len_q=None,
-                     len_kv=None):
+                     len_kv=None, window=0):
         """Forward on an explicit list of (b, h, i) rows; returns (o_rows, lse_rows)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
-        p, m = self._problem(q, k, v, mask, scale, is_causal)
+        p, m = self._problem(q, k, v, mask, scale, is_causal, window)
         lq, lk = self._lens(len_q, p.B), self._lens(len_kv, p.B)
         r = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
         o = np.zeros((r.shape[0], p.Dv))
@@ -161,10 +166,10 @@ class Oracle:
         return o, lse
 
     def backward(self, q, k, v, dO, mask=None, scale=None, is_causal=False, len_q=None,
-                 len_kv=None):
+                 len_kv=None, window=0):
         """Returns (dq, dk, dv, D) with D_i = sum_j P_ij dP_ij."""
         q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
-        p, m = self._problem(q, k, v, mask, scale, is_causal)
+        p, m = self._problem(q, k, v, mask, scale, is_causal, window)
         if dO.shape != (p.B, p.Hq, p.Lq, p.Dv):
             raise ValueError("dO must have the output's shape")
         lq, lk = self._lens(len_q, p.B), self._lens(len_kv, p.B)

@@ -32,6 +32,10 @@
  *    BOTTOM_RIGHT alignment the diagonal ends at the bottom-right corner of the actual
  *    (per-batch) sequence lengths, and right bound 0 masks every column past it, so query
  *    i sees key j iff j <= i + (len_kv - len_q).
+ *  - cuDNN "Attention", forward Configurable Options, diagonal masking: a sliding window
+ *    of length W is the causal right bound 0 plus the left bound W, which masks every
+ *    column at or before row_idx - W (row_idx on the diagonal's alignment), so query i
+ *    sees key j iff i + off - W < j <= i + off.
  *
  * Readings where the pages are silent: a query row at or past len_q is empty (O = 0,
  * LSE = -inf, no gradient); an empty or fully blocked row has LSE = -inf (ln 0);
@@ -54,6 +58,7 @@ static int check_problem(const oracle_problem* p, const int32_t* len_q, const in
   if (p->Hq % p->Hkv != 0) return -1;
   if (isinf(p->scale)) return -1;
   if (p->is_causal < 0 || p->is_causal > 2) return -1;
+  if (p->window < 0 || (p->window > 0 && !p->is_causal)) return -1;
   for (int b = 0; b < p->B; ++b) {
     if (len_q && (len_q[b] < 0 || len_q[b] > p->Lq)) return -1;
     if (len_kv && (len_kv[b] < 0 || len_kv[b] > p->Lk)) return -1;
@@ -69,9 +74,9 @@ static double resolve_scale(const oracle_problem* p) {
 /*
  * One query row (b, h, i): fills P[0..Lk) with the attention weights and returns the
  * row's LSE through *lse.  Returns 0, or -2 for an undefined mask entry.
- *   allowed(j) = (j < len_kv[b]) and (not causal or j <= i + off), and the row itself
- *   must satisfy i < len_q[b]; off = 0 for the top-left diagonal and len_kv[b] - len_q[b]
- *   for the bottom-right one;
+ *   allowed(j) = (j < len_kv[b]) and (not causal or j <= i + off) and (no window or
+ *   j > i + off - W), and the row itself must satisfy i < len_q[b]; off = 0 for the
+ *   top-left diagonal and len_kv[b] - len_q[b] for the bottom-right one;
  *   s_j = alpha * (q_i . k_g,j) + M[b,h,i,j]   if allowed, else -inf;
  *   m = max_j s_j; a row with m = -inf (or an empty row) has P = 0 and LSE = -inf;
  *   otherwise P_j = exp(s_j - m) / sum_t exp(s_t - m) and LSE = m + ln sum_t exp(s_t - m).
@@ -89,7 +94,8 @@ static int row_weights(const oracle_problem* p, double alpha, const double* q, c
 
   double m = -INFINITY;
   for (int j = 0; j < p->Lk; ++j) {
-    int allowed = row_valid && j < kv_len && (!p->is_causal || j <= i + off);
+    int allowed = row_valid && j < kv_len && (!p->is_causal || j <= i + off) &&
+                  (!p->window || j > i + off - p->window);
     if (!allowed) {
       s[j] = -INFINITY;
       continue;

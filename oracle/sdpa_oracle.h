@@ -31,6 +31,8 @@ typedef struct {
   double scale;      /* NaN selects the default 1/sqrt(Dk) */
   int32_t is_causal; /* 0: none; 1 top-left: key j visible to query i iff j <= i;
                         2 bottom-right: iff j <= i + (len_kv - len_q) of the batch */
+  int32_t window;    /* 0: none; W > 0 (with is_causal): also j > i + off - W, i.e. a row
+                        sees the last W keys up to its diagonal (off as above) */
 } oracle_problem;
 
 int oracle_sdpa_forward(const oracle_problem* p, const double* q, const double* k,

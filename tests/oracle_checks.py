@@ -476,6 +476,55 @@ def check_bottom_right_is_shifted_tril(orc):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def check_window_is_band_mask(orc):
+    """A sliding window of W keys (with either diagonal) equals an explicit additive band
+    mask built with numpy (tril at the diagonal offset minus tril W further down), bit for
+    bit in the forward and the backward, with Lq < Lk, Lq = Lk and Lq > Lk."""
+    for Lq, Lk, W, mode in ((7, 9, 3, 1), (7, 9, 3, 2), (6, 6, 2, 1), (8, 5, 4, 2), (5, 11, 1, 2)):
+        c = _case(431 + Lq + W, Lq=Lq, Lk=Lk, mask=False)
+        off = Lk - Lq if mode == 2 else 0
+        band = np.tril(np.ones((Lq, Lk), bool), k=off) & ~np.tril(np.ones((Lq, Lk), bool), k=off - W)
+        m = np.where(band, 0.0, -np.inf).reshape(1, 1, Lq, Lk)
+        o1, l1 = _fwd(orc, c, is_causal=mode, window=W)
+        o2, l2 = _fwd(orc, c, mask=m, is_causal=False)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        g1 = _bwd(orc, c, is_causal=mode, window=W)
+        g2 = _bwd(orc, c, mask=m, is_causal=False)
+        for a, b in zip(g1, g2):
+            assert np.array_equal(a, b)
+        # every row sees at most W keys
+        assert band.sum(axis=1).max() <= W
+
+
+def check_window_limits(orc):
+    """A window at least as long as the key range is plain causal attention (bit for bit);
+    a window of one key leaves each row its diagonal key alone: O_i = v_i, LSE_i = the
+    score of that pair, and (P = 1 is constant) dQ = dK = 0 while dV_i = dO_i summed over
+    the query heads of the group."""
+    c = _case(441, Lq=9, Lk=9, mask=False, lens=True)
+    for mode in (1, 2):
+        o1, l1 = _fwd(orc, c, is_causal=mode, window=9)
+        o2, l2 = _fwd(orc, c, is_causal=mode)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        for a, b in zip(_bwd(orc, c, is_causal=mode, window=40), _bwd(orc, c, is_causal=mode)):
+            assert np.array_equal(a, b)
+    c = _case(442, Lq=6, Lk=6, mask=False)
+    q, k, v, dO = c["q"], c["k"], c["v"], c["dO"]
+    B, Hq, L, _ = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    o, lse = _fwd(orc, c, is_causal=1, window=1)
+    dq, dk, dv, _ = _bwd(orc, c, is_causal=1, window=1)
+    for h in range(Hq):
+        g = h // G
+        assert np.array_equal(o[:, h], v[:, g])
+        s = scale * np.einsum("bid,bid->bi", q[:, h], k[:, g])
+        assert np.abs(lse[:, h] - s).max() <= 1e-12
+    assert np.abs(dq).max() <= 1e-12 and np.abs(dk).max() <= 1e-12
+    want = dO.reshape(B, k.shape[1], G, L, -1).sum(axis=2)
+    assert np.abs(dv - want).max() <= 1e-12
+
+
 def check_bottom_right_torch(orc):
     """Library pin: torch's CPU fp64 scaled_dot_product_attention with its lower-right
     causal bias (torch.nn.attention.bias.causal_lower_right) and autograd, Lq < Lk, GQA."""
@@ -510,5 +559,5 @@ ALL_CHECKS = [
     check_causal_is_tril, check_gqa_is_repeat_interleave, check_score_variance,
     check_single_key, check_identical_keys, check_lengths_are_masks, check_torch_library,
     check_bottom_right_chunked_prefill, check_bottom_right_is_shifted_tril,
-    check_bottom_right_torch,
+    check_bottom_right_torch, check_window_is_band_mask, check_window_limits,
 ]

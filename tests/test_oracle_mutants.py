@@ -47,6 +47,10 @@ MUTANTS = {
     "dv_uses_dS": [("for (int t = 0; t < p->Dv; ++t) dvj[t] += P[j] * dOi[t];",
                     "for (int t = 0; t < p->Dv; ++t) dvj[t] += dS * dOi[t];")],
     "len_kv_inclusive": [("j < kv_len &&", "j <= kv_len &&")],
+    # the window's left edge off by one (a row would see W + 1 keys), or ignoring the
+    # bottom-right offset
+    "window_inclusive_edge": [("j > i + off - p->window", "j >= i + off - p->window")],
+    "window_top_left_only": [("j > i + off - p->window", "j > i - p->window")],
     "dq_missing_row_max": [("P[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);",
                             "P[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j]);")],
 }
