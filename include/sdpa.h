@@ -24,6 +24,11 @@
  *    with right bound 0 -- a prefill chunk against its KV cache; rows that end up with no
  *    key are empty);
  *    ("Understanding PyTorch Scaled Dot-Product Attention" section 3, tril);
+ *  - sliding_window = W > 0 (with is_causal 1 or 2): key j is also visible only if
+ *    j > i + offset - W, offset being the diagonal's (0, or len_kv - len_q): each row sees
+ *    the last W keys up to its diagonal (cuDNN "Attention", forward Configurable Options,
+ *    diagonal masking: sliding window = right bound 0 with left bound W, which masks the
+ *    columns at or before row_idx - W);
  *  - per-batch lengths: keys j >= seq_lens_kv[b] are blocked and query rows
  *    i >= seq_lens_q[b] are empty (cuDNN "Attention", Support Matrix glossary note on
  *    padded layouts; Configurable Options, Padding mask).  Rows and keys past a length
@@ -85,6 +90,7 @@ typedef struct {
   int64_t mask_stride[3];           /* (b, h, i) of the mask; keys have unit stride */
   float scale;                      /* NaN selects 1/sqrt(Dqk); else finite and > 0 */
   int32_t is_causal;                /* 0 none, 1 top-left, 2 bottom-right (see above) */
+  int32_t sliding_window;           /* 0 none; W > 0 needs is_causal 1 or 2 (see above) */
 } sdpa_problem;
 
 /*

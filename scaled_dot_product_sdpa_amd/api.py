@@ -52,6 +52,7 @@ class Problem(ctypes.Structure):
         ("mask_stride", ctypes.c_int64 * 3),
         ("scale", ctypes.c_float),
         ("is_causal", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
     ]
 
 
@@ -250,7 +251,7 @@ def causal_code(is_causal) -> int:
     return code
 
 
-def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
+def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal, sliding_window=0) -> Problem:
     """q, k, v are tensors (B, H, L, D) or ``_Layout``s."""
     q, k, v = (x if isinstance(x, _Layout) else _Layout(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v")))
     B, Hq, Lq, Dqk = q.shape
@@ -272,6 +273,7 @@ def make_problem(q, k, v, o_strides, mask_strides, scale, is_causal) -> Problem:
     p.mask_stride[:] = mask_strides
     p.scale = math.nan if scale is None else float(scale)
     p.is_causal = causal_code(is_causal)
+    p.sliding_window = int(sliding_window)
     return p
 
 
@@ -298,7 +300,7 @@ class ForwardCall:
 
     def __init__(self, q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                  seq_lens_kv=None, return_lse=True, offsets_q=None, offsets_kv=None,
-                 max_seqlen_q=None, max_seqlen_kv=None):
+                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0):
         self.lib = load_library()
         self.ragged = offsets_q is not None or offsets_kv is not None
         self.squeeze = q.dim() == 3 and not self.ragged
@@ -321,7 +323,7 @@ class ForwardCall:
             o_st = _strides3(self.o, "o")
         self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev) if return_lse else None
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal)
+        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal, sliding_window)
         nws = self.lib.sdpa_forward_workspace_bytes(ctypes.byref(self.p))
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self._keep = (qL.tensor, kL.tensor, vL.tensor, m, lq, lk, oq, ok)
@@ -354,7 +356,7 @@ class BackwardCall:
 
     def __init__(self, q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
                  seq_lens_q=None, seq_lens_kv=None, offsets_q=None, offsets_kv=None,
-                 max_seqlen_q=None, max_seqlen_kv=None):
+                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0):
         self.lib = load_library()
         self.ragged = offsets_q is not None or offsets_kv is not None
         self.squeeze = q.dim() == 3 and not self.ragged
@@ -391,7 +393,7 @@ class BackwardCall:
         else:
             o_st = _strides3(o, "o")
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
-        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal)
+        self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal, sliding_window)
         qt, kt, vt = qL.tensor, kL.tensor, vL.tensor
         self.dq = torch.empty_strided(qt.shape, qt.stride(), dtype=qt.dtype, device=dev)
         self.dk = torch.empty_strided(kt.shape, kt.stride(), dtype=kt.dtype, device=dev)
@@ -429,11 +431,13 @@ class BackwardCall:
 
 def sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                  seq_lens_kv=None, return_lse=True, offsets_q=None, offsets_kv=None,
-                 max_seqlen_q=None, max_seqlen_kv=None):
+                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0):
     """O (and LSE) of scaled dot-product attention.  q (B,Hq,Lq,D), k/v (B,Hkv,Lk,D), or
-    packed (T, H, D) with ``offsets_q`` / ``offsets_kv`` (see ``ForwardCall``)."""
+    packed (T, H, D) with ``offsets_q`` / ``offsets_kv`` (see ``ForwardCall``).
+    ``sliding_window`` W > 0 (with a causal diagonal): each row sees the last W keys up to
+    its diagonal."""
     call = ForwardCall(q, k, v, mask, scale, is_causal, seq_lens_q, seq_lens_kv, return_lse,
-                       offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv)
+                       offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv, sliding_window)
     call.launch()
     o, lse = call.result()
     return (o, lse) if return_lse else o
@@ -441,10 +445,11 @@ def sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=Non
 
 def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                   seq_lens_kv=None, offsets_q=None, offsets_kv=None, max_seqlen_q=None,
-                  max_seqlen_kv=None):
-    """(dQ, dK, dV) from the forward's o and lse and the output gradient dO."""
+                  max_seqlen_kv=None, sliding_window=0):
+    """(dQ, dK, dV) from the forward's o and lse and the output gradient dO (same
+    problem, mask, causal flag, window and lengths as the forward)."""
     call = BackwardCall(q, k, v, o, dO, lse, mask, scale, is_causal, seq_lens_q, seq_lens_kv,
-                        offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv)
+                        offsets_q, offsets_kv, max_seqlen_q, max_seqlen_kv, sliding_window)
     call.launch()
     return call.result()
 

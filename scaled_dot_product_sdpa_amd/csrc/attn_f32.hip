@@ -27,9 +27,15 @@ constexpr int chunk_rows() { return 2048 / D; }
 
 struct RowCtx {
   int b, h, g, i;
-  int q_end, kv_end, stop;  // stop: keys [0, stop) are visible (before the mask)
-  int coff;                 // causal diagonal offset: key j visible iff j <= i + coff
+  int q_end, kv_end;
+  int start, stop;  // keys [start, stop) are visible (before the mask)
+  int coff;         // causal diagonal offset: key j visible iff j <= i + coff
 };
+
+// First key row i sees under a sliding window of W keys (0 without one).
+__device__ __forceinline__ int window_start(const Problem& p, int i, int coff) {
+  return (p.causal && p.window > 0) ? max(0, i + coff - p.window + 1) : 0;
+}
 
 __device__ __forceinline__ RowCtx row_ctx(const Problem& p, int b, int h, int i) {
   RowCtx r;
@@ -41,10 +47,15 @@ __device__ __forceinline__ RowCtx row_ctx(const Problem& p, int b, int h, int i)
   r.kv_end = seq_len_kv(p, b);
   r.coff = causal_offset(p.causal, r.q_end, r.kv_end);
   r.stop = (i < r.q_end) ? (p.causal ? max(0, min(r.kv_end, i + 1 + r.coff)) : r.kv_end) : 0;
+  r.start = window_start(p, i, r.coff);
   return r;
 }
 
-// Keys [0, stop) some row of the workgroup's block [i0, i0 + 64) can see (uniform).
+// Keys [block_start, block_stop) cover every key some row of the workgroup's block
+// [i0, i0 + 64) can see (uniform).
+__device__ __forceinline__ int block_start(const Problem& p, const RowCtx& r, int i0) {
+  return window_start(p, i0, r.coff);
+}
 __device__ __forceinline__ int block_stop(const Problem& p, const RowCtx& r, int i0) {
   const int last = min(i0 + kTpb, r.q_end) - 1;
   if (last < i0) return 0;
@@ -104,7 +115,7 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a, int n_rb) {
   block_rows(n_rb, p.Hq, b, h, i0);
   const int i = i0 + threadIdx.x;
   const RowCtx r = row_ctx(p, b, h, i);
-  const int stop_blk = block_stop(p, r, i0);
+  const int start_blk = block_start(p, r, i0), stop_blk = block_stop(p, r, i0);
   const bool live = i < r.q_end;
   const float* qrow = reinterpret_cast<const float*>(a.q) + q_base(p, b) + h * p.q_sh +
                       (int64_t)i * p.q_sl;
@@ -118,17 +129,17 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a, int n_rb) {
   }
   // pass 1: row max
   float m = kNegInf;
-  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+  for (int c0 = start_blk; c0 < stop_blk; c0 += CH) {
     const int n = min(CH, stop_blk - c0);
     __syncthreads();
     stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
     __syncthreads();
     for (int jj = 0; jj < n; ++jj)
-      if (c0 + jj < r.stop) m = fmaxf(m, score<D>(p, r, qv, Ks + jj * D, c0 + jj));
+      if (c0 + jj >= r.start && c0 + jj < r.stop) m = fmaxf(m, score<D>(p, r, qv, Ks + jj * D, c0 + jj));
   }
   // pass 2: weights and weighted sum of values (a masked pair has weight exp(-inf) = 0)
   float l = 0.f;
-  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+  for (int c0 = start_blk; c0 < stop_blk; c0 += CH) {
     const int n = min(CH, stop_blk - c0);
     __syncthreads();
     stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(kTpb) void fwd_f32_kernel(FwdArgs a, int n_rb) {
     __syncthreads();
     if (m == kNegInf) continue;
     for (int jj = 0; jj < n; ++jj) {
-      if (c0 + jj >= r.stop) continue;
+      if (c0 + jj < r.start || c0 + jj >= r.stop) continue;
       const float e = expf(score<D>(p, r, qv, Ks + jj * D, c0 + jj) - m);
       l += e;
       const float* vj = Vs + jj * D;
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a, int n_rb) {
   block_rows(n_rb, p.Hq, b, h, i0);
   const int i = i0 + threadIdx.x;
   const RowCtx r = row_ctx(p, b, h, i);
-  const int stop_blk = block_stop(p, r, i0);
+  const int start_blk = block_start(p, r, i0), stop_blk = block_stop(p, r, i0);
   const int64_t qoff = q_base(p, b) + h * p.q_sh + (int64_t)i * p.q_sl;
   const int64_t ooff = o_base(p, b) + h * p.o_sh + (int64_t)i * p.o_sl;
   const float* kbase = reinterpret_cast<const float*>(a.k) + k_base(p, b) + r.g * p.k_sh;
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a, int n_rb) {
   const int64_t row = ((int64_t)b * p.Hq + h) * p.Lq + i;
   const float Di = ok ? a.dsum[row] : 0.f;
   const float lse = ok ? a.lse[row] : kNegInf;
-  for (int c0 = 0; c0 < stop_blk; c0 += CH) {
+  for (int c0 = start_blk; c0 < stop_blk; c0 += CH) {
     const int n = min(CH, stop_blk - c0);
     __syncthreads();
     stage_rows<D>(Ks, kbase, p.k_sl, c0, n);
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kTpb) void bwd_dq_f32_kernel(BwdArgs a, int n_rb) {
     __syncthreads();
     if (lse == kNegInf) continue;
     for (int jj = 0; jj < n; ++jj) {
-      if (c0 + jj >= r.stop) continue;
+      if (c0 + jj < r.start || c0 + jj >= r.stop) continue;
       const float* kj = Ks + jj * D;
       const float P = expf(score<D>(p, r, qv, kj, c0 + jj) - lse);  // 0 for a masked pair
       const float* vj = Vs + jj * D;
@@ -251,6 +262,10 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a, int n_kb)
   // key bounds the staged rows
   const int i_begin = p.causal ? max(0, j - coff) : 0;
   const int i_blk = p.causal ? max(0, j0 - coff) : 0;
+  // under a sliding window of W keys row i sees key j only if i <= j - coff + W - 1
+  const bool win = p.causal && p.window > 0;
+  const int i_stop = win ? min(q_end, max(j - coff + p.window, 0)) : q_end;
+  const int i_stop_blk = win ? min(q_end, max(min(j0 + kTpb, kv_end) - 1 - coff + p.window, 0)) : q_end;
   if (j0 < kv_end) {
     for (int hh = 0; hh < p.G; ++hh) {
       const int h = g * p.G + hh;
@@ -259,8 +274,8 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a, int n_kb)
       const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq;
       const float* mrow = p.mask ? reinterpret_cast<const float*>(p.mask) + b * p.m_sb + h * p.m_sh
                                  : nullptr;
-      for (int c0 = i_blk; c0 < q_end; c0 += CH) {
-        const int n = min(CH, q_end - c0);
+      for (int c0 = i_blk; c0 < i_stop_blk; c0 += CH) {
+        const int n = min(CH, i_stop_blk - c0);
         __syncthreads();
         stage_rows<D>(Qs, qb, p.q_sl, c0, n);
         stage_rows<D>(Gs, gb, p.o_sl, c0, n);
@@ -272,7 +287,7 @@ __global__ __launch_bounds__(kTpb) void bwd_dkdv_f32_kernel(BwdArgs a, int n_kb)
         if (!ok) continue;
         for (int ii = 0; ii < n; ++ii) {
           const int i = c0 + ii;
-          if (i < i_begin) continue;
+          if (i < i_begin || i >= i_stop) continue;
           const float lse = Ls[ii];
           const float* qi = Qs + ii * D;
           const float* doi = Gs + ii * D;

@@ -94,8 +94,9 @@ constexpr int dkdv_lds_bytes() {
 }
 
 // Workgroup `bid` of `nblk` (the dK/dV grid), LDS at smem.
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, char* smem) {
+  constexpr bool CAUSAL = CM != 0;  // CM: 0 no diagonal, 1 causal, 2 causal + sliding window
   constexpr int KT = 32 * NW;    // keys per workgroup
   constexpr int TILE = kQT * D;
   constexpr int NS = D / 16;     // MFMAs of one S (or dP) block
@@ -151,7 +152,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   // first query tile with a row that sees key j0 (row i sees it iff i >= j0 - coff)
   const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;
   const int qt_begin = CAUSAL ? max(j0 - coff, 0) / kQT : 0;
-  const int qt_end = (j0 < kstop) ? (q_end + kQT - 1) / kQT : 0;
+  // sliding window of W keys: row i sees key j only if i <= j - coff + W - 1, so rows past
+  // kstop - coff + W - 2 see none of this workgroup's keys
+  const int W = CM == 2 ? p.window : 0;
+  const int q_last = W > 0 ? min(q_end, max(kstop - coff + W - 1, 0)) : q_end;
+  const int qt_end = (j0 < kstop) ? (q_last + kQT - 1) / kQT : 0;
   const int n_q_tiles = qt_end > qt_begin ? qt_end - qt_begin : 0;
   const int total = n_q_tiles * p.G;
   auto tile_rows = [&](int it, int& h, int& i0) {
@@ -276,12 +281,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
         }
       }
     }
-    const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 + coff < jw + 31);
+    const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 + coff < jw + 31) ||
+                         (W > 0 && jw <= r0 + 31 + coff - W);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int qi = r0 + 16 * hi + v;
-        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff);
+        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff) &&
+                        (W == 0 || myk > qi + coff - W);
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -422,10 +429,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<D, NW, MASK>()];
-  dkdv_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, gridDim.x, smem);
+  dkdv_body<D, NW, CM, MASK>(a, blockIdx.x, gridDim.x, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -437,8 +444,9 @@ constexpr int kBN = 64;
 template <int D>
 constexpr int dq_lds_bytes() { return 6 * kBN * D * 2; }
 
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, char* smem) {
+  constexpr bool CAUSAL = CM != 0;  // CM: 0 no diagonal, 1 causal, 2 causal + sliding window
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
   constexpr int NS = D / 16;   // MFMAs of one S^T (or dP^T) block
@@ -487,6 +495,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
+  // sliding window: tiles before the first row's window are skipped (as the forward)
+  const int W = CM == 2 ? p.window : 0;
+  const int t0 = W > 0 ? min(max(row_lo + coff - W + 1, 0) / kBN, n_tiles) : 0;
   int vis_stop = wq_lo < q_end ? kv_stop : 0;
   if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1 + coff);
   const int nvis = vis_stop > 0 ? (vis_stop + 31) / 32 : 0;  // 32-key blocks this wave works on (a prefix)
@@ -499,7 +510,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
   };
   // tile 0 and this lane's row operands land first; tile 1 streams in behind
-  if (n_tiles > 0) load_tile(0, K0, V0);
+  if (n_tiles > t0) load_tile(t0 * kBN, K0, V0);
   const int qi = wq_lo + l32;  // this lane's query (N index)
   const bool qok = qi < q_end;
   bf16x8 qreg[NS], doreg[NS];
@@ -512,7 +523,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   const float nl2 = qok ? -a.lse2[rowid] : kNegInf;  // exp2 offset of this lane's row
   const float dsum = qok ? a.dsum[rowid] : 0.f;
   wait_vmem();
-  if (n_tiles > 1) load_tile(kBN, K1, V1);
+  if (n_tiles > t0 + 1) load_tile((t0 + 1) * kBN, K1, V1);
 
   f32x16 dq_acc[NT];
 #pragma unroll
@@ -553,7 +564,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   };
 
   u32x4 mk[2];
-  load_mask(0, mk);
+  load_mask(2 * t0, mk);
   // ---- one pipeline phase for block bi (keys kb*32.. of Kc/Vc; the previous block's keys
   // kbp*32.. of Kp; the next block's keys kbn*32.. of Kn/Vn).  Region 1: dQ MFMAs of block
   // bi-1 with the P, dS arithmetic of block bi.  Region 2: S^T, dP^T MFMAs of block bi+1
@@ -563,7 +574,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
                    bf16x8 (&ds)[2]) __attribute__((always_inline)) {
     if (bi >= nvis) {
       // the wave's last block: its dQ, while its K tile is still resident
-      if (bi == nvis && bi > 0) {
+      if (bi == nvis && bi > 2 * t0) {
 #pragma unroll
         for (int j = 0; j < R1; ++j) dq_mfma(j, kt_op(j, Kp, kbp), ds_prev);
       }
@@ -584,12 +595,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
           mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
       }
     }
-    const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo + coff) || (wq_lo + 32 > q_end);
+    const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo + coff) ||
+                         (wq_lo + 32 > q_end) || (W > 0 && 32 * bi <= wq_hi + coff - W);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff);
+        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff) &&
+                        (W == 0 || key > qi + coff - W);
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -664,12 +677,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     phase(2 * t + 1, Kc, 0, Kn, Vn, 0, s_b, dp_b, s_a, dp_a, ds_a, ds_b);
   };
 
-  if (n_tiles > 0) {
+  if (n_tiles > t0) {
     // the first phase runs the dQ MFMAs of "block -1" (rows 32..63 of buffer 2) with zero
     // weights: those rows are zeroed so the products are exactly zero
     lds_zero<32 * D * 2, 64 * NW>(K2 + 32 * D, tid);
-    __syncthreads();  // every wave's share of tile 0 has landed; the zeros are visible
-    if (nvis > 0) {
+    __syncthreads();  // every wave's share of the first tile has landed; the zeros are visible
+    if (nvis > 2 * t0) {
 #pragma unroll
       for (int i = 0; i < R2; ++i) {
         const bf16x8 op = tile_row8<D>((i & 1) ? V0 : K0, krow_l, 2 * (i >> 1) + hi);
@@ -678,15 +691,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
       }
     }
   }
-  for (int t = 0; t < n_tiles; t += 3) {
+  for (int t = t0; t < n_tiles; t += 3) {
     step(t, K2, K0, V0, K1, V1, K2, V2);
     if (t + 1 < n_tiles) step(t + 1, K0, K1, V1, K2, V2, K0, V0);
     if (t + 2 < n_tiles) step(t + 2, K1, K2, V2, K0, V0, K1, V1);
   }
   // a wave whose last block is the workgroup's last: that block's dQ (second block of
-  // tile n_tiles-1, buffer (n_tiles-1) % 3, never overwritten)
-  if (nvis > 0 && nvis == 2 * n_tiles) {
-    const int lt = (n_tiles - 1) % 3;
+  // tile n_tiles-1, buffer (n_tiles-1-t0) % 3, never overwritten)
+  if (nvis > 2 * t0 && nvis == 2 * n_tiles) {
+    const int lt = (n_tiles - 1 - t0) % 3;
     const bf16* Kl = lt == 0 ? K0 : (lt == 1 ? K1 : K2);
 #pragma unroll
     for (int j = 0; j < R1; ++j) dq_mfma(j, kt_op(j, Kl, 1), ds_b);
@@ -712,10 +725,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
 //     not fit two waves per SIMD): each 32-key block's S^T, dP^T, dS^T and dQ^T in turn.
 // ---------------------------------------------------------------------------------------
 
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<D>()];
-  dq_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, gridDim.x, smem);
+  dq_body<D, NW, CM, MASK>(a, blockIdx.x, gridDim.x, smem);
 }
 
 // dK/dV and dQ in one launch: workgroups [0, n_dkdv) run the dK/dV body (heavy key tiles
@@ -723,16 +736,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 // and no launch boundary separates the two.  Both bodies fit two waves per SIMD (d = 64).
 // n_dkdv is a multiple of 8 whenever the XCD-aware item order is used, so the dQ items
 // keep their XCD.
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_fused_kernel(BwdArgs a, int n_dkdv) {
   constexpr int kL1 = dkdv_lds_bytes<D, NW, MASK>(), kL2 = dq_lds_bytes<D>();
   __shared__ __attribute__((aligned(16))) char smem[kL1 > kL2 ? kL1 : kL2];
-  if ((int)blockIdx.x < n_dkdv) dkdv_body<D, NW, CAUSAL, MASK>(a, blockIdx.x, n_dkdv, smem);
-  else dq_body<D, NW, CAUSAL, MASK>(a, blockIdx.x - n_dkdv, gridDim.x - n_dkdv, smem);
+  if ((int)blockIdx.x < n_dkdv) dkdv_body<D, NW, CM, MASK>(a, blockIdx.x, n_dkdv, smem);
+  else dq_body<D, NW, CM, MASK>(a, blockIdx.x - n_dkdv, gridDim.x - n_dkdv, smem);
 }
 
-template <int D, int NW, bool CAUSAL, bool MASK>
+template <int D, int NW, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = CM != 0;  // CM: 0 no diagonal, 1 causal, 2 causal + sliding window
   constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;
   constexpr int TILE = kBN * D;
@@ -774,6 +788,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
+  // sliding window: tiles before the first row's window are skipped
+  const int W = CM == 2 ? p.window : 0;
+  const int t0 = W > 0 ? min(max(row_lo + coff - W + 1, 0) / kBN, n_tiles) : 0;
 
   const int qi = wq_lo + l32;  // this lane's query (N index)
   const bool qok = qi < q_end;
@@ -812,11 +829,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
     const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo + coff) ||
-                           (wq_lo + 32 > q_end);
+                           (wq_lo + 32 > q_end) || (W > 0 && j0 <= wq_hi + coff - W);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key_lo = j0 + kb * 32;
-      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi + coff))) continue;
+      if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi + coff) &&
+            (W == 0 || key_lo + 31 > wq_lo + coff - W)))
+        continue;
       // S^T = K Q^T and dP^T = V dO^T for keys key_lo + perm
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
@@ -858,7 +877,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
           float x = fmaf(s_acc[v], c2, MASK ? mv[v] - lse2 : -lse2);
           if (partial_t) {
             const int key = key0 + v;
-            const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff);
+            const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff) &&
+                            (W == 0 || key > qi + coff - W);
             x = ok ? x : kNegInf;
           }
           const float pv = fast_exp2(x);
@@ -878,8 +898,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     }
   };
 
-  if (n_tiles > 0) load_tile(0, K0, V0);
-  for (int t = 0; t < n_tiles; t += 2) {
+  if (n_tiles > t0) load_tile(t0 * kBN, K0, V0);
+  for (int t = t0; t < n_tiles; t += 2) {
     step(t, K0, V0, K1, V1);
     if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
   }
@@ -908,7 +928,7 @@ template <int D> struct BwdShape;
 template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = true; };
 template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = false; };
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, int CM, bool MASK>
 hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   constexpr int KNW = BwdShape<D>::KV_NW, QNW = BwdShape<D>::Q_NW;
   const int n_kt = (a.p.Lk + 32 * KNW - 1) / (32 * KNW);
@@ -919,23 +939,23 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
     if ((stages & kBwdDkdv) && (stages & kBwdDq)) {
       const int n_dkdv = n_kt * a.p.B * a.p.Hkv, n_dq = n_qt * a.p.B * a.p.Hq;
       if (n_dkdv + n_dq > 0)
-        hipLaunchKernelGGL((bwd_fused_kernel<D, KNW, CAUSAL, MASK>), dim3(n_dkdv + n_dq), dim3(64 * KNW), 0, s,
+        hipLaunchKernelGGL((bwd_fused_kernel<D, KNW, CM, MASK>), dim3(n_dkdv + n_dq), dim3(64 * KNW), 0, s,
                            a, n_dkdv);
       return hipGetLastError();
     }
   }
   if ((stages & kBwdDkdv) && n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CAUSAL, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
                        dim3(64 * KNW), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((stages & kBwdDq) && n_qt > 0) {
     if constexpr (BwdShape<D>::PIPE_DQ)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
+      hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CM, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
                          dim3(64 * QNW), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_seq_kernel<D, QNW, CAUSAL, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
+      hipLaunchKernelGGL((bwd_dq_seq_kernel<D, QNW, CM, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
                          dim3(64 * QNW), 0, s, a);
   }
   return hipGetLastError();
@@ -951,9 +971,12 @@ hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (!(stages & (kBwdDkdv | kBwdDq))) return hipSuccess;
-  const bool causal = a.p.causal != 0, mask = a.p.mask != nullptr;
-  if (causal) return mask ? launch_main<D, true, true>(a, stages, s) : launch_main<D, true, false>(a, stages, s);
-  return mask ? launch_main<D, false, true>(a, stages, s) : launch_main<D, false, false>(a, stages, s);
+  const bool mask = a.p.mask != nullptr;
+  // the window's checks are compiled only into the windowed kernels
+  if (a.p.causal && a.p.window > 0)
+    return mask ? launch_main<D, 2, true>(a, stages, s) : launch_main<D, 2, false>(a, stages, s);
+  if (a.p.causal) return mask ? launch_main<D, 1, true>(a, stages, s) : launch_main<D, 1, false>(a, stages, s);
+  return mask ? launch_main<D, 0, true>(a, stages, s) : launch_main<D, 0, false>(a, stages, s);
 }
 
 }  // namespace

@@ -43,6 +43,12 @@ constexpr int kNonTemporal = 2;
 // PAGED: the cache lives in pages (a 32-key tile never straddles two, since the page size
 // is a multiple of 32); each lane first reads the page index of one tile of the split,
 // and a tile's rows are then addressed from its page like the rows of a contiguous cache.
+// First key the query row sees: 0, or kv_end - W under a sliding window of W keys (the
+// bottom-right diagonal of one query row ends at the last key).
+__device__ __forceinline__ int decode_key_start(const Problem& p, int kv_end) {
+  return (p.causal && p.window > 0) ? max(0, kv_end - p.window) : 0;
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeArgs a) {
@@ -63,11 +69,13 @@ void decode_split_kernel(DecodeArgs a) {
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int kv_end = seq_len_kv(p, b);
-  const int k0 = c * a.split_keys;
+  // a sliding window of W keys leaves the single query row the keys [kv_end - W, kv_end)
+  const int klo = decode_key_start(p, kv_end);
+  const int k0 = max(c * a.split_keys, klo);
+  const int k1 = min(c * a.split_keys + a.split_keys, kv_end);
   // the combine reads only splits that hold keys, and none of a batch whose query row is
   // past its length (an empty row)
-  if (k0 >= kv_end || seq_len_q(p, b) < 1) return;
-  const int k1 = min(k0 + a.split_keys, kv_end);
+  if (k0 >= k1 || seq_len_q(p, b) < 1) return;
   const int n_tiles = (k1 - k0 + kDT - 1) / kDT;
 
   const bool qvalid = i16 < p.G;
@@ -261,9 +269,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
   const int h = bh % p.Hq;
   const int kv_end = seq_len_kv(p, b);
   const bool row_live = seq_len_q(p, b) >= 1;  // else the row is empty: O = 0, LSE = -inf
-  const int n_live = row_live ? (kv_end + a.split_keys - 1) / a.split_keys : 0;
-  const float* pl = a.part_lse + (int64_t)bh * a.n_split;
-  const float* po = a.part_o + (int64_t)bh * a.n_split * D + E * lane;
+  // live splits c_lo .. c_lo + n_live - 1 (those holding a key of the row's range)
+  const int klo = decode_key_start(p, kv_end);
+  const int c_lo = klo / a.split_keys;
+  const int n_live = row_live && kv_end > klo ? (kv_end + a.split_keys - 1) / a.split_keys - c_lo : 0;
+  const float* pl = a.part_lse + (int64_t)bh * a.n_split + c_lo;
+  const float* po = a.part_o + ((int64_t)bh * a.n_split + c_lo) * D + E * lane;
   // M = max_c lse_c, L = sum_c exp(lse_c - M) over the live splits
   float M = kNegInf;
   for (int c = lane; c < n_live; c += 64) M = fmaxf(M, pl[c]);

@@ -51,8 +51,9 @@ namespace {
 constexpr int kBN = 64;             // keys per K/V tile (two 32-key MFMA blocks)
 constexpr float kRescaleLog2 = 8.f; // move the reference max only past this growth
 
-template <int D, int NW, int WPE, bool CAUSAL, bool MASK>
+template <int D, int NW, int WPE, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = CM != 0;  // CM: 0 no diagonal, 1 causal, 2 causal + sliding window
   constexpr int BM = NW * 32;
   constexpr int TILE = kBN * D;
   // Tile t's K is read by the phases of blocks 2t-1 (the next block's scores) and 2t; its V
@@ -99,7 +100,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   if (CAUSAL) kv_stop = min(kv_stop, min(row_hi, q_end) + coff);
   if (row_lo >= q_end) kv_stop = 0;
   const int n_tiles = kv_stop > 0 ? (kv_stop + kBN - 1) / kBN : 0;
-  // 32-key blocks this wave works on: a prefix of the keys.
+  // Sliding window of W keys: the workgroup's first row sees no key before
+  // row_lo + coff - W + 1, so the tiles before that one are skipped.
+  const int W = CM == 2 ? p.window : 0;
+  const int t0 = W > 0 ? min(max(row_lo + coff - W + 1, 0) / kBN, n_tiles) : 0;
+  // 32-key blocks this wave works on: a prefix of the keys (from block 2 * t0).
   int vis_stop = wq_lo < q_end ? kv_stop : 0;
   if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1 + coff);
   const int nvis = vis_stop > 0 ? (vis_stop + 31) / 32 : 0;
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   };
   // ---- tile 0 and the Q operand (B of S^T = K Q^T: lane holds query row, 8 consecutive d
   // per k-step) land first; tile 1 streams in behind the first block.
-  if (n_tiles > 0) load_tile(0, Kb[0], Vb[0]);
+  if (n_tiles > t0) load_tile(t0 * kBN, Kb[0], Vb[0]);
   const int qrow = wq_lo + l32;
   bf16x8 qreg[D / 16];
 #pragma unroll
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
     qreg[kk] = __builtin_bit_cast(bf16x8, x);
   }
   wait_vmem();
-  if (n_tiles > 1) load_tile(kBN, Kb[1], Vb[1]);
+  if (n_tiles > t0 + 1) load_tile((t0 + 1) * kBN, Kb[1], Vb[1]);
 
   // reference max (log2 units) and the sum of the fp32 weights relative to it (normalises
   // O and gives LSE), kept as two partial sums (even / odd scores) so the adds form two
@@ -193,12 +198,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], c2, mv[v] * kLog2e);
     }
     const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo + coff) ||
-                         (wq_lo + 32 > q_end);
+                         (wq_lo + 32 > q_end) || (W > 0 && key_lo <= wq_hi + coff - W);
     if (partial) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow + coff);
+        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow + coff) &&
+                        (W == 0 || key > qrow + coff - W);
         x[v] = ok ? x[v] : kNegInf;
       }
     }
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // S of the current block and of the next one; the two phases of a tile step swap them.
   f32x16 sacc_a = f32x16{}, sacc_b = f32x16{};
   u32x4 mk[2];
-  load_mask(0, mk);
+  load_mask(2 * t0, mk);
 
   // ---- one pipeline phase for block bi (V rows kb*32.. of Vt; the next block's K rows
   // kbn*32.. of Kn).  Region 1: PV MFMAs of block bi-1 with the row max of block bi.
@@ -331,18 +337,18 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
     phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a);
   };
 
-  if (n_tiles > 0) {
-    __syncthreads();  // every wave's share of tile 0 has landed
-    if (nvis > 0) {
+  if (n_tiles > t0) {
+    __syncthreads();  // every wave's share of the first tile has landed
+    if (nvis > 2 * t0) {
 #pragma unroll
       for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(Kb[0], 0, kk), qreg[kk], sacc_a);
     }
   }
-  for (int t = 0; t < n_tiles; t += 6) {
+  for (int tl = 0; tl < n_tiles - t0; tl += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u)
-      if (t + u < n_tiles)
-        step(t + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3]);
+      if (tl + u < n_tiles - t0)
+        step(t0 + tl + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3]);
   }
   // the last block's PV
 #pragma unroll
@@ -368,30 +374,32 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   if (qrow < p.Lq && lseb && hi == 0) lseb[qrow] = rowlive ? (mref * kLn2 + logf(ft)) : kNegInf;
 }
 
-template <int D, int NW, int WPE, bool CAUSAL, bool MASK>
+template <int D, int NW, int WPE, int CM, bool MASK>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   constexpr int BM = NW * 32;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
   const int grid = n_qt * a.p.B * a.p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, WPE, CAUSAL, MASK>), dim3(grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, WPE, CM, MASK>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, int CM, bool MASK>
 hipError_t launch_shape(const FwdArgs& a, hipStream_t s) {
   // Two independent workgroups of 4 waves (128 query rows) per CU: two waves per SIMD hide
   // each other's LDS and MFMA latencies, and the two workgroups' barriers do not wait for
   // each other (measured faster than one 8-wave workgroup per CU on every workload here:
   // causal MHA 1k 26.3 -> 23.1 us, causal GQA 4k 318 -> 309 us, padded 2k 217 -> 205 us).
-  return launch_t<D, 4, 2, CAUSAL, MASK>(a, s);
+  return launch_t<D, 4, 2, CM, MASK>(a, s);
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-  const bool causal = a.p.causal != 0;
   const bool mask = a.p.mask != nullptr;
-  if (causal) return mask ? launch_shape<D, true, true>(a, s) : launch_shape<D, true, false>(a, s);
-  return mask ? launch_shape<D, false, true>(a, s) : launch_shape<D, false, false>(a, s);
+  // the window's checks are compiled only into the windowed kernels
+  if (a.p.causal && a.p.window > 0)
+    return mask ? launch_shape<D, 2, true>(a, s) : launch_shape<D, 2, false>(a, s);
+  if (a.p.causal) return mask ? launch_shape<D, 1, true>(a, s) : launch_shape<D, 1, false>(a, s);
+  return mask ? launch_shape<D, 0, true>(a, s) : launch_shape<D, 0, false>(a, s);
 }
 
 }  // namespace

@@ -18,6 +18,7 @@ struct Problem {
   float scale;       // resolved scale
   float scale_log2;  // scale * log2(e)
   int causal;  // 0 none, 1 top-left, 2 bottom-right diagonal
+  int window;  // 0 none; W > 0 (causal only): key j visible only if j > i + offset - W
   const int32_t* len_q;   // may be null
   const int32_t* len_kv;  // may be null
   // ragged (packed) sequences, may be null: batch b's query rows start at row off_q[b] of

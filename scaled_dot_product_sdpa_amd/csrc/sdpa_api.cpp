@@ -59,6 +59,10 @@ sdpa_status check_problem(const sdpa_problem* p) {
       p->is_causal != SDPA_CAUSAL_BOTTOM_RIGHT)
     return fail(SDPA_ERR_INVALID_ARGUMENT, "is_causal must be 0, 1 (top-left) or 2 (bottom-right), got %d",
                 p->is_causal);
+  if (p->sliding_window < 0 || (p->sliding_window > 0 && p->is_causal == SDPA_CAUSAL_NONE))
+    return fail(SDPA_ERR_INVALID_ARGUMENT,
+                "sliding_window must be 0, or > 0 together with a causal diagonal (got %d, is_causal %d)",
+                p->sliding_window, p->is_causal);
   if (!std::isnan(p->scale) && !(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be NaN (default) or finite and > 0");
   if (p->Dqk != p->Dv)
@@ -119,6 +123,7 @@ sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_
   k.scale = std::isnan(p->scale) ? 1.0f / std::sqrt((float)p->Dqk) : p->scale;
   k.scale_log2 = k.scale * 1.4426950408889634f;
   k.causal = p->is_causal;
+  k.window = p->sliding_window;
   k.len_q = lq;
   k.len_kv = lk;
   k.off_q = off_q;
@@ -441,6 +446,6 @@ const char* sdpa_status_string(sdpa_status s) {
 
 const char* sdpa_last_error(void) { return g_last_error.c_str(); }
 
-int sdpa_version(void) { return 100; }
+int sdpa_version(void) { return 200; }  // 0.2.0: sdpa_problem gained sliding_window
 
 }  // extern "C"

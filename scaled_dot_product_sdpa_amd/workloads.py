@@ -37,6 +37,7 @@ class Workload:
     mask: str = "none"         # "none" | "padded_random" (B,1,Lq,Lk) additive mask
     mask_drop: float = 0.0     # Bernoulli rate of extra -inf entries inside the lengths
     poison: bool = False       # fill K/V rows at or past len_kv with NaN
+    window: int = 0            # sliding window of this many keys up to the diagonal (0: none)
     backward: bool = True
     note: str = field(default="", compare=False)
 
@@ -117,7 +118,7 @@ def make_inputs(w: Workload, device="cpu") -> dict:
             v[b, :, n:, :] = float("nan")
 
     return dict(q=q, k=k, v=v, dO=dO, mask=mask, len_q=len_q, len_kv=len_kv,
-                scale=w.scale, is_causal=w.causal)
+                scale=w.scale, is_causal=w.causal, window=w.window)
 
 
 def fully_masked_rows(inputs: dict) -> list:

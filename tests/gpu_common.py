@@ -45,7 +45,7 @@ def gpu_forward(inp):
     from scaled_dot_product_sdpa_amd import sdpa_forward
     o, lse = sdpa_forward(inp["q"], inp["k"], inp["v"], mask=inp.get("mask"), scale=inp["scale"],
                           is_causal=inp["is_causal"], seq_lens_q=inp.get("len_q"),
-                          seq_lens_kv=inp.get("len_kv"))
+                          seq_lens_kv=inp.get("len_kv"), sliding_window=inp.get("window", 0))
     torch.cuda.synchronize()
     return o, lse
 
@@ -54,14 +54,14 @@ def gpu_backward(inp, o, lse):
     from scaled_dot_product_sdpa_amd import sdpa_backward
     g = sdpa_backward(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, mask=inp.get("mask"),
                       scale=inp["scale"], is_causal=inp["is_causal"], seq_lens_q=inp.get("len_q"),
-                      seq_lens_kv=inp.get("len_kv"))
+                      seq_lens_kv=inp.get("len_kv"), sliding_window=inp.get("window", 0))
     torch.cuda.synchronize()
     return g
 
 
 def oracle_args(inp):
     return dict(mask=f64(inp.get("mask")), scale=inp["scale"], is_causal=inp["is_causal"],
-                len_q=i32(inp.get("len_q")), len_kv=i32(inp.get("len_kv")))
+                len_q=i32(inp.get("len_q")), len_kv=i32(inp.get("len_kv")), window=inp.get("window", 0))
 
 
 def oracle_forward(orc, inp):

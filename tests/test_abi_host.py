@@ -83,6 +83,9 @@ def _bwd(lib, p, lse=FAKE, dq=FAKE, ws=FAKE, nws=1 << 20, stage="sdpa_backward")
     (lambda p: p.mask_stride.__setitem__(2, 1 << 24), SDPA_ERR_UNSUPPORTED),
     (lambda p: setattr(p, "is_causal", 3), SDPA_ERR_INVALID_ARGUMENT),    # 0, 1 or 2 only
     (lambda p: setattr(p, "is_causal", -1), SDPA_ERR_INVALID_ARGUMENT),
+    # a sliding window is a count of keys and needs a causal diagonal to end at
+    (lambda p: (setattr(p, "is_causal", 1), setattr(p, "sliding_window", -1)), SDPA_ERR_INVALID_ARGUMENT),
+    (lambda p: (setattr(p, "is_causal", 0), setattr(p, "sliding_window", 16)), SDPA_ERR_INVALID_ARGUMENT),
 ])
 def test_forward_rejects(lib, mutate, status):
     p = _problem()
@@ -132,6 +135,9 @@ def test_backward_rejects(lib, stage):
     assert _bwd(lib, p, nws=16, stage=stage) == SDPA_ERR_WORKSPACE_TOO_SMALL
     bad = _problem(Hq=3)
     assert _bwd(lib, bad, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+    nowin = _problem()
+    nowin.is_causal, nowin.sliding_window = 0, 16
+    assert _bwd(lib, nowin, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings_and_version(lib):

@@ -61,6 +61,27 @@ CASES = {
     "decode_g16_d64": W["gqa_decode_8k"].scaled(B=2, Hq=16, Hkv=1, Lk=600, D=64, len_range=(1, 600), seed=19),
     "decode_g6_d128": W["gqa_decode_8k"].scaled(B=2, Hq=12, Hkv=2, Lk=2100, len_range=(500, 2100), seed=20),
     "decode_g32_d128": W["gqa_decode_8k"].scaled(B=2, Hq=32, Hkv=1, Lk=300, len_range=(1, 300), seed=21),
+    # sliding window of W keys up to the diagonal: whole key tiles before the window are
+    # skipped and the window's first tile is cut per element; d = 64 without a mask runs the
+    # one-launch backward, W = 1 leaves only the diagonal key, the decode skips leading splits
+    "window_d64": W["mha_causal_1k"].scaled(B=2, Hq=3, Hkv=3, Lq=700, Lk=700, window=100, seed=50),
+    "window_br_gqa_lens_d128": W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=2, Lq=300, Lk=700, causal=2,
+                                                         lens="chunk", len_range=(100, 700),
+                                                         window=150, seed=51),
+    "window_1_d128": W["gqa_causal_4k"].scaled(B=1, Hq=2, Hkv=1, Lq=200, Lk=200, window=1, seed=52),
+    "window_mask_d128": W["padded_mask_2k"].scaled(B=2, Hq=2, Hkv=2, Lq=400, Lk=400, causal=True,
+                                                   len_range=(64, 400), window=130, seed=53),
+    "window_mask_br_d64": W["padded_mask_2k"].scaled(B=2, Hq=2, Hkv=1, Lq=300, Lk=450, D=64, causal=2,
+                                                     lens="chunk", len_range=(100, 450), window=77,
+                                                     seed=54),
+    "window_fp32": W["tiny_fp32"].scaled(B=2, Hq=4, Hkv=2, Lq=150, Lk=150, D=64, causal=True,
+                                         window=70, seed=55),
+    "window_fp32_br_lens": W["tiny_fp32"].scaled(B=2, Hq=2, Hkv=1, Lq=100, Lk=200, causal=2,
+                                                 lens="chunk", len_range=(50, 200), window=45, seed=56),
+    "decode_window_d128": W["gqa_decode_8k"].scaled(B=4, Hq=8, Hkv=2, Lk=3000, causal=2,
+                                                    len_range=(1, 3000), window=1000, seed=57),
+    "decode_window_d64": W["gqa_decode_8k"].scaled(B=3, Hq=4, Hkv=4, Lk=900, D=64, causal=2,
+                                                   len_range=(30, 900), window=50, seed=58),
 }
 
 
@@ -77,7 +98,8 @@ def _inputs(name):
 def test_parity(name, orc):
     w, inp = _inputs(name)
     banner(f"parity {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Lq={w.Lq} Lk={w.Lk} D={w.D} {w.dtype} "
-           f"causal={w.causal} mask={inp['mask'] is not None} lens={inp['len_kv'] is not None}")
+           f"causal={w.causal} window={w.window} mask={inp['mask'] is not None} "
+           f"lens={inp['len_kv'] is not None}")
     d = to_dev(inp)
     o, lse = gpu_forward(d)
     o_ref, lse_ref = oracle_forward(orc, inp)

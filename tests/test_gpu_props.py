@@ -260,3 +260,42 @@ def test_decode_with_query_lengths(orc, causal):
     assert torch.all(torch.isneginf(lse[1])) and torch.all(torch.isneginf(lse[3]))
     o_ref, lse_ref = oracle_forward(orc, inp)
     compare_forward(inp, o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("D,dtype,causal,Lq", [(64, "bf16", 1, 500), (128, "bf16", 2, 300),
+                                               (64, "f32", 1, 130), (128, "bf16", 2, 1)])
+def test_window_covering_every_key_changes_nothing(D, dtype, causal, Lq):
+    """A sliding window at least as wide as the key sequence skips no tile and cuts no key,
+    so every output is bit-identical to the plain causal problem's (prefill, fp32, decode)."""
+    banner(f"window >= Lk is the causal problem: D={D} {dtype} causal={causal} Lq={Lq}")
+    w = MID.scaled(B=2, Hq=4, Hkv=2, Lq=Lq, Lk=500, D=D, dtype=dtype, causal=causal, seed=59,
+                   backward=Lq > 1)
+    d = to_dev(make_inputs(w))
+    o1, l1 = gpu_forward(d)
+    dw = dict(d, window=w.Lk)
+    o2, l2 = gpu_forward(dw)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if w.backward:
+        for a, b in zip(gpu_backward(d, o1, l1), gpu_backward(dw, o2, l2)):
+            assert torch.equal(a, b)
+
+
+def test_window_equals_band_mask():
+    """is_causal with a sliding window of W keys and an explicit additive band mask
+    (-inf outside i - W < j <= i) give the same result."""
+    banner("window == band mask")
+    w = MID.scaled(Hq=2, Hkv=2, D=128, Lq=400, Lk=400, seed=60)
+    W = 97
+    d = to_dev(make_inputs(w))
+    dw = dict(d, window=W)
+    o1, l1 = gpu_forward(dw)
+    i = torch.arange(w.Lq, device="cuda").view(-1, 1)
+    j = torch.arange(w.Lk, device="cuda").view(1, -1)
+    band = (j <= i) & (j > i - W)
+    m = torch.zeros(w.Lq, w.Lk, device="cuda").masked_fill(~band, float("-inf")).to(torch.bfloat16)
+    d2 = dict(d, is_causal=False, mask=m.view(1, 1, w.Lq, w.Lk))
+    o2, l2 = gpu_forward(d2)
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-4
+    for a, b in zip(gpu_backward(dw, o1, l1), gpu_backward(d2, o2, l2)):
+        assert rel_fro(f64(a), f64(b)) <= 1e-2

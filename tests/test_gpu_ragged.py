@@ -45,6 +45,10 @@ CASES = {
     "kv_ragged_only_d128": (W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=1, Lq=100, Lk=280, causal=False,
                                                       lens="kv", len_range=(1, 280), seed=64),
                             False, True, 3),
+    # sliding window over packed sequences (bottom-right diagonal, GQA, d = 128)
+    "thd_window_br_d128": (W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=2, Lq=200, Lk=400, causal=2,
+                                                     lens="chunk", len_range=(50, 400), window=90,
+                                                     seed=68), True, True, 0),
     # fp32 path
     "thd_fp32_gqa": (W["tiny_fp32"].scaled(B=3, Hq=4, Hkv=2, Lq=70, Lk=70, D=64, lens="qkv",
                                            len_range=(1, 70), seed=65), True, True, 2),
@@ -112,6 +116,7 @@ def test_ragged(name, orc):
     # padded reference run on the GPU
     o_p, lse_p = gpu_forward(d)
 
+    ragged_kw["sliding_window"] = w.window
     fc = ForwardCall(q.cuda(), k.cuda(), v.cuda(), d["mask"], w.scale, w.causal, **ragged_kw)
     fc.o.fill_(SENTINEL)
     fc.launch()
