@@ -302,6 +302,73 @@ def summarize_trace(stats_csv, out_md, command):
     print(Path(out_md).read_text())
 
 
+# Derived per-kernel figures from SQ/GRBM counters, with rocprofv3's own definitions
+# (256 CUs, 1024 SIMDs on the MI355X): MFMA busy = MFMA busy cycles over all SIMDs'
+# active cycles; VALU busy = VALU-active cycles per CU over active cycles; LDS bank
+# conflict = conflict-stall cycles per CU over active cycles; mean waves per CU from the
+# wave-cycle count (sampled every 4 cycles).  The csv gives GRBM_GUI_ACTIVE summed over
+# the 8 XCDs (8x the dispatch's cycles); the definitions take one XCD's, hence the / 8.
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+COUNTER_COLUMNS = [
+    ("clock GHz", lambda c: c["GRBM_GUI_ACTIVE"] / XCD_NUM / c["ns"]),
+    ("MFMA busy %", lambda c: 100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / XCD_NUM * SIMD_NUM)),
+    ("VALU busy %", lambda c: 100 * c["SQ_ACTIVE_INST_VALU"] / CU_NUM / (c["GRBM_GUI_ACTIVE"] / XCD_NUM)),
+    ("LDS bank-conflict %", lambda c: 100 * c["SQ_LDS_BANK_CONFLICT"] / CU_NUM / (c["GRBM_GUI_ACTIVE"] / XCD_NUM)),
+    ("waves / CU", lambda c: 4 * c["SQ_WAVE_CYCLES"] / CU_NUM / (c["GRBM_GUI_ACTIVE"] / XCD_NUM)),
+    ("MFMA instr (M)", lambda c: c["SQ_INSTS_MFMA"] / 1e6),
+    ("VALU instr / MFMA instr", lambda c: c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None),
+    ("LDS instr / MFMA instr", lambda c: c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"] if c["SQ_INSTS_MFMA"] else None),
+]
+COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
+            "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_counters(pmc_dir, out_md, command):
+    """Markdown table of per-kernel averages of the COUNTERS pass and the figures derived
+    from them (COUNTER_COLUMNS)."""
+    import csv
+    import glob
+    per = {}  # kernel -> dispatch -> counter -> value
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                n = r["Kernel_Name"]
+                if "sdpa::" not in n:
+                    continue
+                d = per.setdefault(n, {}).setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    lines = ["# rocprofv3 counters per kernel", "",
+             "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "Per-kernel means over its dispatches. " + "; ".join(
+                 ["A = GRBM_GUI_ACTIVE / 8 (the csv sums it over the 8 XCDs)",
+                  "clock = A / dispatch duration",
+                  "MFMA busy = 100·SQ_VALU_MFMA_BUSY_CYCLES / (A·1024 SIMDs)",
+                  "VALU busy = 100·SQ_ACTIVE_INST_VALU / 256 CUs / A",
+                  "LDS bank-conflict = 100·SQ_LDS_BANK_CONFLICT / 256 / A",
+                  "waves / CU = 4·SQ_WAVE_CYCLES / 256 / A",
+                  "MFMA instr = SQ_INSTS_MFMA per dispatch (millions)"]) + ". For dispatches "
+             "of a few tens of microseconds GRBM_GUI_ACTIVE also counts cycles around the kernel "
+             "(the clock column then reads above the real ~2 GHz), so their busy and wave figures "
+             "are low by that factor.", "",
+             "| kernel | dispatches | " + " | ".join(c for c, _ in COUNTER_COLUMNS) + " |",
+             "|---|---:|" + "---:|" * len(COUNTER_COLUMNS)]
+    table = []
+    for n, disp in per.items():
+        full = [d for d in disp.values() if all(k in d for k in COUNTERS)]
+        if not full:
+            continue
+        mean = {k: sum(d[k] for d in full) / len(full) for k in COUNTERS + ["ns"]}
+        name = n.replace("void sdpa::(anonymous namespace)::", "")
+        name = re.sub(r"\(sdpa::\w+(, int)?\)$", "", name)
+        table.append((mean["GRBM_GUI_ACTIVE"] * len(full), f"| `{name}` | {len(full)} | " +
+                      " | ".join("–" if fn(mean) is None else f"{fn(mean):.2f}"
+                                 for _, fn in COUNTER_COLUMNS) + " |"))
+    lines += [t for _, t in sorted(table, key=lambda t: -t[0])]
+    Path(out_md).write_text("\n".join(lines) + "\n")
+    print(Path(out_md).read_text())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,7 +383,12 @@ def main():
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs (no GPU)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv (no GPU)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "OUT_MD", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 --pmc run of COUNTERS (no GPU)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return

@@ -2,11 +2,15 @@
 
 Usage: ``python -m scaled_dot_product_sdpa_amd.build`` (or ``build()`` from Python).
 Each source is compiled to an object file in ``_build/`` in parallel, then linked.
+``python -m scaled_dot_product_sdpa_amd.build --resource-usage`` instead prints, as a
+markdown table, the registers, LDS and register-limited occupancy the compiler gives each
+kernel (its ``kernel-resource-usage`` remarks on a device-only compile).
 """
 
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -68,5 +72,43 @@ def build(verbose: bool = False, extra=()) -> Path:
     return LIB
 
 
+def resource_usage() -> str:
+    """Markdown table of every kernel's VGPRs, AGPRs, SGPRs, LDS bytes per workgroup,
+    waves per SIMD the registers allow, and spills, from hipcc's resource remarks."""
+    rows = []
+    for name in SOURCES:
+        if not name.endswith(".hip"):
+            continue
+        cmd = [HIPCC, *FLAGS, "--offload-device-only", "-Rpass-analysis=kernel-resource-usage",
+               "-c", str(CSRC / name), "-o", os.devnull]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stderr)
+            raise RuntimeError(f"hipcc failed on {name}")
+        cur = None
+        for ln in r.stderr.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", ln)
+            if m:
+                cur = {"sym": m.group(1)}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass", ln)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = m.group(2)
+    dem = subprocess.run(["c++filt"], input="\n".join(r["sym"] for r in rows), capture_output=True,
+                         text=True).stdout.splitlines()
+    out = ["| kernel | VGPRs | AGPRs | SGPRs | LDS bytes / workgroup | waves / SIMD (registers) | spills V/S |",
+           "|---|---:|---:|---:|---:|---:|---|"]
+    for r, d in zip(rows, dem):
+        d = re.sub(r"\(.*\)$", "", d.replace("sdpa::(anonymous namespace)::", "").replace("sdpa::", ""))
+        out.append(f"| `{d}` | {r['VGPRs']} | {r['AGPRs']} | {r['TotalSGPRs']} | "
+                   f"{r['LDS Size [bytes/block]']} | {r['Occupancy [waves/SIMD]']} | "
+                   f"{r['VGPRs Spill']}/{r['SGPRs Spill']} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--resource-usage" in sys.argv[1:]:
+        print(resource_usage())
+    else:
+        build(verbose=True)
