@@ -195,22 +195,34 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
     return res, inp, fc, bc
 
 
+CPU_SECONDS = 10.0
+
+
 def cpu_baseline(w, inp):
     """The fp64 oracle (as it stands) on the host cores, on the headline workload's step."""
     from oracle import load_oracle
     orc = load_oracle()
     f = lambda t: None if t is None else t.detach().double().cpu().numpy()
     q, k, v, dO = f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["dO"])
-    t0 = time.perf_counter()
-    orc.forward(q, k, v, scale=w.scale, is_causal=w.causal)
-    t1 = time.perf_counter()
-    orc.backward(q, k, v, dO, scale=w.scale, is_causal=w.causal)
-    t2 = time.perf_counter()
+    # whole steps, repeated until at least CPU_SECONDS have passed (one step is well under
+    # a second on a many-core host, too short to time on its own)
+    t_fwd = t_bwd = 0.0
+    n = 0
+    while n == 0 or t_fwd + t_bwd < CPU_SECONDS:
+        t0 = time.perf_counter()
+        orc.forward(q, k, v, scale=w.scale, is_causal=w.causal)
+        t1 = time.perf_counter()
+        orc.backward(q, k, v, dO, scale=w.scale, is_causal=w.causal)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        n += 1
     fl = flops(w, visible_pairs(w))
-    return {"value": (fl["fwd"] + fl["bwd"]) / (t2 - t0) / 1e12, "unit": "TFLOP/s",
+    return {"value": n * (fl["fwd"] + fl["bwd"]) / (t_fwd + t_bwd) / 1e12, "unit": "TFLOP/s",
             "cores": orc.num_threads, "kind": "oracle",
-            "sample": f"the full {HEADLINE} step (fwd + bwd over all {w.B}x{w.Hq} heads), fp64",
-            "seconds": {"fwd": t1 - t0, "bwd": t2 - t1}}
+            "sample": f"the full {HEADLINE} step (fwd + bwd over all {w.B}x{w.Hq} heads), fp64, "
+                      f"{n} steps in {t_fwd + t_bwd:.1f} s",
+            "seconds": {"fwd": t_fwd / n, "bwd": t_bwd / n}}
 
 
 def traffic_for(stage, launches_per_step=1):
