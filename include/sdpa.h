@@ -216,7 +216,9 @@ sdpa_status sdpa_backward_ragged(const sdpa_problem* p, const void* q, const voi
  * calculation):
  *   K_cache[b, h, s, d] = k_pages[page_table[b, s / page_size], h, s mod page_size, d]
  *   V_cache[b, h, s, d] = v_pages[page_table[b, s / page_size], h, s mod page_size, d]
- * for s < seq_lens_kv[b].
+ * for s < seq_lens_kv[b].  sliding_window = W > 0 restricts the query to the keys
+ * s >= seq_lens_kv[b] - W (the sliding window of sdpa_problem on the bottom-right diagonal,
+ * which for one query row ends at the last key).
  *   q (B, Hq, D), o (B, Hq, D) bf16 with (b, h) strides; lse (B, Hq) fp32 or NULL;
  *   k_pages, v_pages (num_pages, Hkv, page_size, D) bf16 with (page, h, s) strides;
  *   page_table (B, max_pages) int32 device array, row-major; seq_lens_kv (B) int32 device
@@ -236,6 +238,7 @@ typedef struct {
   int64_t k_stride[3];       /* (page, h, s) element strides of k_pages */
   int64_t v_stride[3];       /* (page, h, s) element strides of v_pages */
   float scale;               /* NaN selects 1/sqrt(D); else finite and > 0 */
+  int32_t sliding_window;    /* 0 none; W > 0: only the last W keys of each sequence */
 } sdpa_paged_decode;
 
 /* Device workspace (bytes) of sdpa_decode_paged: the split-KV partial results. */

@@ -64,7 +64,7 @@ class PagedDecode(ctypes.Structure):
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_pages", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 2), ("o_stride", ctypes.c_int64 * 2),
         ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
-        ("scale", ctypes.c_float),
+        ("scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
     ]
 
 
@@ -457,9 +457,11 @@ def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, s
 class PagedDecodeCall:
     """Marshalled single-query decode against a paged KV cache (see ``sdpa_decode_paged`` in
     include/sdpa.h): q (B, Hq, D); k_pages, v_pages (num_pages, Hkv, page_size, D);
-    page_table (B, max_pages) int32; seq_lens_kv (B) int32; all on one GPU."""
+    page_table (B, max_pages) int32; seq_lens_kv (B) int32; all on one GPU.
+    ``sliding_window`` W > 0 attends to the last W keys of each sequence only."""
 
-    def __init__(self, q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True):
+    def __init__(self, q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True,
+                 sliding_window=0):
         self.lib = load_library()
         if q.dim() == 4 and q.shape[2] == 1:
             q = q[:, :, 0]
@@ -489,6 +491,7 @@ class PagedDecodeCall:
         p.k_stride[:] = (k_pages.stride(0), k_pages.stride(1), k_pages.stride(2))
         p.v_stride[:] = (v_pages.stride(0), v_pages.stride(1), v_pages.stride(2))
         p.scale = math.nan if scale is None else float(scale)
+        p.sliding_window = int(sliding_window)
         self.p = p
         nws = self.lib.sdpa_decode_paged_workspace_bytes(ctypes.byref(p))
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
@@ -507,9 +510,12 @@ class PagedDecodeCall:
         return self.o, self.lse
 
 
-def sdpa_decode_paged(q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True):
-    """O (B, Hq, D) (and LSE (B, Hq)) of single-query attention over a paged KV cache."""
-    call = PagedDecodeCall(q, k_pages, v_pages, page_table, seq_lens_kv, scale, return_lse)
+def sdpa_decode_paged(q, k_pages, v_pages, page_table, seq_lens_kv, scale=None, return_lse=True,
+                      sliding_window=0):
+    """O (B, Hq, D) (and LSE (B, Hq)) of single-query attention over a paged KV cache
+    (the last ``sliding_window`` keys of each sequence only, when it is > 0)."""
+    call = PagedDecodeCall(q, k_pages, v_pages, page_table, seq_lens_kv, scale, return_lse,
+                           sliding_window)
     call.launch()
     o, lse = call.result()
     return (o, lse) if return_lse else o

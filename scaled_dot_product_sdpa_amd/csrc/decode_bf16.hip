@@ -69,9 +69,11 @@ void decode_split_kernel(DecodeArgs a) {
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int kv_end = seq_len_kv(p, b);
-  // a sliding window of W keys leaves the single query row the keys [kv_end - W, kv_end)
+  // a sliding window of W keys leaves the single query row the keys [klo, kv_end) with
+  // klo = kv_end - W; the split's first tile starts on the 32-key boundary below klo (so a
+  // tile never straddles a page) and the keys before klo are masked
   const int klo = decode_key_start(p, kv_end);
-  const int k0 = max(c * a.split_keys, klo);
+  const int k0 = max(c * a.split_keys, klo / kDT * kDT);
   const int k1 = min(c * a.split_keys + a.split_keys, kv_end);
   // the combine reads only splits that hold keys, and none of a batch whose query row is
   // past its length (an empty row)
@@ -188,11 +190,11 @@ void decode_split_kernel(DecodeArgs a) {
     float x[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) { x[v] = s0[v]; x[4 + v] = s1[v]; }
-    if (j0 + kDT > k1) {
+    if (j0 + kDT > k1 || j0 < klo) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const int key = j0 + (v < 4 ? 0 : 16) + 4 * g4 + (v & 3);
-        x[v] = key < k1 ? x[v] : kNegInf;
+        x[v] = (key < k1 && key >= klo) ? x[v] : kNegInf;
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));

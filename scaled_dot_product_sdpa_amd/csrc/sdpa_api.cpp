@@ -349,6 +349,8 @@ sdpa_status check_paged(const sdpa_paged_decode* p) {
     return fail(SDPA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
   if (!std::isnan(p->scale) && !(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(SDPA_ERR_INVALID_ARGUMENT, "scale must be NaN (default) or finite and > 0");
+  if (p->sliding_window < 0)
+    return fail(SDPA_ERR_INVALID_ARGUMENT, "sliding_window must be >= 0 (got %d)", p->sliding_window);
   if (p->D != 64 && p->D != 128) return fail(SDPA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", p->D);
   if (p->Hq / p->Hkv > 16)
     return fail(SDPA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", p->Hq / p->Hkv);
@@ -415,7 +417,9 @@ sdpa_status sdpa_decode_paged(const sdpa_paged_decode* p, const void* q, const v
   k.v_sb = 0; k.v_sh = p->v_stride[1]; k.v_sl = p->v_stride[2];
   k.scale = std::isnan(p->scale) ? 1.0f / std::sqrt((float)p->D) : p->scale;
   k.scale_log2 = k.scale * 1.4426950408889634f;
-  k.causal = 0;
+  // a window ends at the last key: the bottom-right diagonal of the one query row
+  k.causal = p->sliding_window > 0 ? SDPA_CAUSAL_BOTTOM_RIGHT : SDPA_CAUSAL_NONE;
+  k.window = p->sliding_window;
   k.len_kv = seq_lens_kv;
   a.q = q; a.k = k_pages; a.v = v_pages; a.o = o; a.lse = lse;
   a.page_table = page_table;

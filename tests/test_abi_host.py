@@ -179,6 +179,7 @@ def _dec(lib, p, table=FAKE, lens=FAKE, ws=FAKE, nws=1 << 20):
     (lambda p: setattr(p, "scale", -1.0), SDPA_ERR_INVALID_ARGUMENT),
     (lambda p: p.k_stride.__setitem__(2, 60), SDPA_ERR_UNSUPPORTED),
     (lambda p: p.v_stride.__setitem__(2, 64), SDPA_ERR_INVALID_ARGUMENT),  # rows overlap
+    (lambda p: setattr(p, "sliding_window", -1), SDPA_ERR_INVALID_ARGUMENT),
 ])
 def test_paged_decode_rejects(lib, mutate, status):
     p = _paged()

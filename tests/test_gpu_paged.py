@@ -36,27 +36,33 @@ def _paged(inp, page_size, seed, token_major=False):
 
 
 CASES = [
-    # (B, Hq, Hkv, Lk, D, page_size, length range, token-major pages)
-    (4, 8, 2, 1100, 128, 64, (1, 1100), False),
-    (3, 16, 1, 700, 64, 32, (30, 700), True),
-    (2, 12, 2, 2100, 128, 256, (500, 2100), False),
-    (5, 32, 8, 1500, 128, 128, (0, 1500), True),
+    # (B, Hq, Hkv, Lk, D, page_size, length range, token-major pages, sliding window)
+    (4, 8, 2, 1100, 128, 64, (1, 1100), False, 0),
+    (3, 16, 1, 700, 64, 32, (30, 700), True, 0),
+    (2, 12, 2, 2100, 128, 256, (500, 2100), False, 0),
+    (5, 32, 8, 1500, 128, 128, (0, 1500), True, 0),
+    # the last W keys only: the window starts inside a page and inside a 32-key tile, and
+    # skips whole key splits
+    (4, 8, 2, 2100, 128, 64, (1, 2100), False, 700),
+    (3, 4, 4, 900, 64, 32, (30, 900), True, 45),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_G{c[1] // c[2]}_D{c[4]}_ps{c[5]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_G{c[1] // c[2]}_D{c[4]}_ps{c[5]}_W{c[8]}")
 def test_paged_decode_matches_contiguous_and_oracle(orc, case):
-    B, Hq, Hkv, Lk, D, ps, lr, token_major = case
-    w = WORKLOADS["gqa_decode_8k"].scaled(B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, D=D, len_range=lr, seed=60 + ps)
+    B, Hq, Hkv, Lk, D, ps, lr, token_major, win = case
+    w = WORKLOADS["gqa_decode_8k"].scaled(B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, D=D, len_range=lr, seed=60 + ps,
+                                          causal=2 if win else 0, window=win)
     inp = make_inputs(w)
     if lr[0] == 0:
         inp["len_kv"][1] = 0  # an empty cache: O = 0, LSE = -inf
-    banner(f"paged decode B={B} Hq={Hq} Hkv={Hkv} Lk={Lk} D={D} page={ps} token_major={token_major}")
+    banner(f"paged decode B={B} Hq={Hq} Hkv={Hkv} Lk={Lk} D={D} page={ps} token_major={token_major} "
+           f"window={win}")
     kp, vp, table = _paged(inp, ps, seed=70 + ps, token_major=token_major)
     d = to_dev(inp)
     o_c, l_c = gpu_forward(d)
     o_p, l_p = sdpa_decode_paged(d["q"][:, :, 0], kp.cuda(), vp.cuda(), table.cuda(), d["len_kv"],
-                                 scale=inp["scale"])
+                                 scale=inp["scale"], sliding_window=win)
     torch.cuda.synchronize()
     assert torch.equal(o_p, o_c[:, :, 0]) and torch.equal(l_p, l_c[:, :, 0])
     o_ref, lse_ref = oracle_forward(orc, inp)
