@@ -450,6 +450,6 @@ const char* sdpa_status_string(sdpa_status s) {
 
 const char* sdpa_last_error(void) { return g_last_error.c_str(); }
 
-int sdpa_version(void) { return 200; }  // 0.2.0: sdpa_problem gained sliding_window
+int sdpa_version(void) { return 200; }  // 0.2.0: sdpa_problem and sdpa_paged_decode gained sliding_window
 
 }  // extern "C"
