@@ -62,14 +62,21 @@ def source_hash(stage: str) -> str:
 
 
 def visible_pairs(w, len_q=None, len_kv=None) -> int:
-    """Number of (b, h, i, j) a query may attend to under causality and lengths."""
+    """Number of (b, h, i, j) a query may attend to under the causal diagonal (top-left or
+    bottom-right), the sliding window and the lengths."""
     import numpy as np
     lq = np.full(w.B, w.Lq) if len_q is None else np.asarray(len_q.cpu()).astype(np.int64)
     lk = np.full(w.B, w.Lk) if len_kv is None else np.asarray(len_kv.cpu()).astype(np.int64)
     total = 0
     for b in range(w.B):
         i = np.arange(int(lq[b]))
-        n = np.minimum(i + 1, lk[b]) if w.causal else np.full(i.shape, lk[b])
+        if w.causal:
+            off = int(lk[b] - lq[b]) if w.causal == 2 else 0
+            hi = np.clip(i + 1 + off, 0, lk[b])
+            lo = np.maximum(i + off - w.window + 1, 0) if w.window > 0 else 0
+            n = np.maximum(hi - lo, 0)
+        else:
+            n = np.full(i.shape, lk[b])
         total += int(n.sum())
     return total * w.Hq
 
@@ -137,11 +144,11 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
     from scaled_dot_product_sdpa_amd.workloads import make_inputs
     inp = make_inputs(w, device="cuda")
     fc = ForwardCall(inp["q"], inp["k"], inp["v"], inp["mask"], inp["scale"], inp["is_causal"],
-                     inp["len_q"], inp["len_kv"])
+                     inp["len_q"], inp["len_kv"], sliding_window=w.window)
     fc.launch()
     torch.cuda.synchronize()
     res = {"config": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lk": w.Lk, "D": w.D,
-                      "causal": w.causal, "mask": inp["mask"] is not None,
+                      "causal": w.causal, "window": w.window, "mask": inp["mask"] is not None,
                       "lens": inp["len_kv"] is not None, "dtype": w.dtype}}
     t = {"fwd": kernel_ms(timer, fc.launch, reps=10, iters=iters)}
     if w.Lq == 1:
@@ -176,7 +183,8 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
     if want_bwd and w.backward:
         o, lse = fc.result()
         bc = BackwardCall(inp["q"], inp["k"], inp["v"], o, inp["dO"], lse, inp["mask"],
-                          inp["scale"], inp["is_causal"], inp["len_q"], inp["len_kv"])
+                          inp["scale"], inp["is_causal"], inp["len_q"], inp["len_kv"],
+                          sliding_window=w.window)
         bc.launch()
         torch.cuda.synchronize()
         # prep and the two main passes as the library runs them ("main": one launch at
@@ -500,7 +508,8 @@ def main():
 
     # ---- other workloads
     if not args.no_extra:
-        names = ["gqa_causal_4k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32"]
+        names = ["gqa_causal_4k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32", "gqa_swa_4k",
+                 "gqa_chunk_4k"]
         if args.only:
             names = [n for n in names if n in args.only.split(",")]
         extra = {}

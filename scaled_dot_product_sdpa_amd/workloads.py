@@ -61,6 +61,13 @@ WORKLOADS = {
                                dtype="bf16", causal=False, scale=1 / math.sqrt(128), seed=4,
                                lens="qkv", len_range=(256, 2048), mask="padded_random",
                                mask_drop=0.1),
+    # measured beside the configurations above: a sliding window of 1024 keys over the GQA
+    # 4k prefill, and a 512-query prefill chunk against a 4096-key cache (bottom-right)
+    "gqa_swa_4k": Workload("gqa_swa_4k", B=2, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128,
+                           dtype="bf16", causal=True, scale=1 / math.sqrt(128), seed=6,
+                           window=1024),
+    "gqa_chunk_4k": Workload("gqa_chunk_4k", B=2, Hq=32, Hkv=8, Lq=512, Lk=4096, D=128,
+                             dtype="bf16", causal=2, scale=1 / math.sqrt(128), seed=7),
     "gqa_decode_8k": Workload("gqa_decode_8k", B=64, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128,
                               dtype="bf16", causal=False, scale=1 / math.sqrt(128), seed=5,
                               lens="kv", len_range=(1024, 8192), poison=True, backward=False),

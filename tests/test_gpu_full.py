@@ -33,13 +33,14 @@ def _rows(w, inp, n, rng):
 def _oracle_rows(orc, inp, rows):
     return orc.forward_rows(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), rows,
                             mask=f64(inp["mask"]), scale=inp["scale"], is_causal=inp["is_causal"],
-                            len_q=i32(inp["len_q"]), len_kv=i32(inp["len_kv"]))
+                            len_q=i32(inp["len_q"]), len_kv=i32(inp["len_kv"]),
+                            window=inp.get("window", 0))
 
 
 def _slice_group(w, inp, b, g):
     G = w.Hq // w.Hkv
     hs = slice(g * G, (g + 1) * G)
-    out = dict(scale=inp["scale"], is_causal=inp["is_causal"])
+    out = dict(scale=inp["scale"], is_causal=inp["is_causal"], window=inp.get("window", 0))
     out["q"] = inp["q"][b:b + 1, hs]
     out["dO"] = inp["dO"][b:b + 1, hs]
     out["k"] = inp["k"][b:b + 1, g:g + 1]
@@ -70,7 +71,7 @@ def _check_bwd_groups(orc, w, inp, grads, groups):
         s = _slice_group(w, inp, b, g)
         rq, rk, rv, _ = orc.backward(f64(s["q"]), f64(s["k"]), f64(s["v"]), f64(s["dO"]),
                                      mask=f64(s["mask"]), scale=s["scale"], is_causal=s["is_causal"],
-                                     len_q=i32(s["len_q"]), len_kv=i32(s["len_kv"]))
+                                     len_q=i32(s["len_q"]), len_kv=i32(s["len_kv"]), window=s["window"])
         hs = slice(g * G, (g + 1) * G)
         errs.append((check_grad(f64(dq[b:b + 1, hs]), rq, torch.bfloat16, f"dQ[{b},{g}]"),
                      check_grad(f64(dk[b:b + 1, g:g + 1]), rk, torch.bfloat16, f"dK[{b},{g}]"),
@@ -82,6 +83,8 @@ def _check_bwd_groups(orc, w, inp, grads, groups):
     ("mha_causal_1k", [(0, 0), (3, 15)]),
     ("gqa_causal_4k", [(1, 7)]),
     ("padded_mask_2k", [(0, 0), (5, 9)]),
+    ("gqa_swa_4k", [(0, 3)]),
+    ("gqa_chunk_4k", [(1, 5)]),
 ])
 def test_full_size_prefill(orc, name, groups):
     w = WORKLOADS[name]
