@@ -1,15 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the scaled dot-product attention hot path on one MI355X.
 
-One step = the whole hot path over one batch of the headline workload (causal MHA
-prefill, B=4, H=16, L=1024, d=64, bf16): forward (O, LSE) then backward (D prep, dK/dV,
-dQ).  The step is captured once into a HIP graph and replayed; inputs are resident in HBM
-before the timed region starts.  Prints ONE JSON line.
+One step = the whole hot path over one batch of the headline workload (causal GQA
+prefill, B=2, Hq=32, Hkv=8, L=4096, d=128, bf16, the largest workload): forward (O, LSE)
+then backward (D prep, dK/dV, dQ).  The step is captured once into a HIP graph and
+replayed; inputs are resident in HBM before the timed region starts.  Prints ONE JSON line.
 
 Also reported (same line, "workloads"): the other workloads' forward / backward TFLOP/s
-and the GQA decode's HBM GB/s, the per-kernel durations (HIP events around graph
-replays of that kernel alone), the roofline of the dominant kernel, and the fp64 CPU
-oracle timed on the host cores as a baseline.
+and the GQA decode's HBM GB/s, each with the roofline of its dominant kernel, the
+per-kernel durations (HIP events around graph replays of that kernel alone), and the fp64
+CPU oracle timed on the host cores as a baseline.
 
 FLOP convention: pairs (i, j) a query may attend to (causal and lengths applied, the
 random mask entries not subtracted); forward 2 (Dqk + Dv) flops per pair, backward
@@ -34,7 +34,8 @@ METRIC = "SDPA fwd / fwd+bwd TFLOP/s (+% bf16 MFMA peak); decode GB/s (+% HBM)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-HEADLINE = "mha_causal_1k"
+HEADLINE = "gqa_causal_4k"
+EXTRA = ["mha_causal_1k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32", "gqa_swa_4k", "gqa_chunk_4k"]
 
 # kernel-name fragments (as rocprofv3 reports them) of each launch stage
 KERNEL_NAMES = {
@@ -203,39 +204,30 @@ def run_workload(torch, timer, name, w, iters, want_bwd=True):
     return res, inp, fc, bc
 
 
-CPU_SECONDS = 10.0
-
-
 def cpu_baseline(w, inp):
-    """The fp64 oracle (as it stands) on the host cores, on the headline workload's step."""
+    """The fp64 oracle (as it stands) on the host cores, on one whole step of the headline
+    workload (forward over every row, backward over every (batch, KV head) group); the
+    backward runs one group per thread, so one step takes about 30 s on 16 threads."""
     from oracle import load_oracle
     orc = load_oracle()
     f = lambda t: None if t is None else t.detach().double().cpu().numpy()
     q, k, v, dO = f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["dO"])
-    # whole steps, repeated until at least CPU_SECONDS have passed (one step is well under
-    # a second on a many-core host, too short to time on its own)
-    t_fwd = t_bwd = 0.0
-    n = 0
-    while n == 0 or t_fwd + t_bwd < CPU_SECONDS:
-        t0 = time.perf_counter()
-        orc.forward(q, k, v, scale=w.scale, is_causal=w.causal)
-        t1 = time.perf_counter()
-        orc.backward(q, k, v, dO, scale=w.scale, is_causal=w.causal)
-        t2 = time.perf_counter()
-        t_fwd += t1 - t0
-        t_bwd += t2 - t1
-        n += 1
+    t0 = time.perf_counter()
+    orc.forward(q, k, v, scale=w.scale, is_causal=w.causal)
+    t1 = time.perf_counter()
+    orc.backward(q, k, v, dO, scale=w.scale, is_causal=w.causal)
+    t2 = time.perf_counter()
     fl = flops(w, visible_pairs(w))
-    return {"value": n * (fl["fwd"] + fl["bwd"]) / (t_fwd + t_bwd) / 1e12, "unit": "TFLOP/s",
-            "cores": orc.num_threads, "kind": "oracle",
-            "sample": f"the full {HEADLINE} step (fwd + bwd over all {w.B}x{w.Hq} heads), fp64, "
-                      f"{n} steps in {t_fwd + t_bwd:.1f} s",
-            "seconds": {"fwd": t_fwd / n, "bwd": t_bwd / n}}
+    return {"value": (fl["fwd"] + fl["bwd"]) / (t2 - t0) / 1e12, "unit": "TFLOP/s",
+            "cores": orc.num_threads, "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"one whole {HEADLINE} step (fwd over all {w.B}x{w.Hq} heads' rows, bwd over all "
+                      f"{w.B}x{w.Hkv} (batch, KV head) groups), fp64, {t2 - t0:.1f} s",
+            "seconds": {"fwd": t1 - t0, "bwd": t2 - t1}}
 
 
-def traffic_for(stage, launches_per_step=1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current source of that kernel (else None)."""
+def traffic_for(workload, stage):
+    """HBM bytes per launch of one kernel of a workload from the committed rocprofv3
+    counter summary, if it was taken on the current source of that kernel (else None)."""
     path = ROOT / "profiles" / "traffic.json"
     if not path.exists():
         return None
@@ -243,10 +235,49 @@ def traffic_for(stage, launches_per_step=1):
         data = json.loads(path.read_text())
     except ValueError:
         return None
-    ent = data.get(stage)
+    ent = data.get(workload, {}).get(stage) if isinstance(data.get(workload), dict) else None
     if not ent or ent.get("source_hash") != source_hash(stage):
         return None
     return ent.get("bytes_per_launch")
+
+
+def roofline(name, w, res):
+    """Roofline of a workload's dominant kernel: algorithmic flops (or bytes) of one launch
+    over its measured average duration, against the published peak."""
+    t = res["ms"]
+    if w.Lq == 1:
+        # decode: the split kernel streams the cache; the call's time (split + combine) is
+        # the duration, the algorithmic bytes those of the whole call
+        return {"bound": "hbm", "achieved": res["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": res["GBps"] / PEAK_HBM_GBS, "traffic": traffic_for(name, "decode_split"),
+                "kernel": "decode_split_kernel + decode_combine_kernel", "kernel_ms": t["fwd"]}
+    stages = ("fwd", "prep", "main") if res.get("fused_backward") else ("fwd", "prep", "dkdv", "dq")
+    kt = {k: t[k] for k in stages if k in t}
+    dom = max(kt, key=kt.get)
+    if dom == "prep":
+        nbytes = w.B * w.Hq * w.Lq * (2 * w.D * 2 + 4 + 2 * 4)
+        roof = {"bound": "hbm", "achieved": nbytes / (kt[dom] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                "achieved": res["gflop"][dom] * 1e9 / (kt[dom] * 1e-3) / 1e12,
+                "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(name, dom)
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel_ms"] = kt[dom]
+    return roof
+
+
+def cpu_model() -> str:
+    try:
+        for ln in Path("/proc/cpuinfo").read_text().splitlines():
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---- profile helpers (no GPU): turn rocprofv3 output into the committed summaries ----
@@ -268,12 +299,20 @@ def _pmc_rows(directory, counter):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, command):
-    """profiles/traffic.json: HBM bytes per launch of each headline kernel, from a
-    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by what the same
-    counter reads for the --calibrate copy of known size."""
-    out = {"note": "HBM bytes per launch = counter KiB * 1024 * scale, scale = known bytes of "
-                   "the calibration copy / its counter bytes", "command": command}
+def write_traffic(fetch_dir, write_dir, command, workload):
+    """profiles/traffic.json, entry `workload`: HBM bytes per launch of each of its kernels,
+    from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch) of a bench command that
+    runs that workload alone, each counter scaled by what it reads for the --calibrate copy
+    of known size."""
+    path = ROOT / "profiles" / "traffic.json"
+    data = {}
+    if path.exists():
+        try:
+            data = json.loads(path.read_text())
+        except ValueError:
+            data = {}
+    data = {k: v for k, v in data.items() if isinstance(v, dict) and k != workload}
+    out = {"command": command}
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
@@ -294,9 +333,11 @@ def write_traffic(fetch_dir, write_dir, command):
                       "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
                       "dispatches": min(fn, wn),
                       "bytes_per_launch": int(fk * 1024 * fs + wk * 1024 * ws)}
-    path = ROOT / "profiles" / "traffic.json"
-    path.write_text(json.dumps(out, indent=1) + "\n")
-    print(path.read_text())
+    data[workload] = out
+    data["note"] = {"text": "per workload: HBM bytes per launch = counter KiB * 1024 * scale, scale = "
+                            "known bytes of the calibration copy / its counter bytes"}
+    path.write_text(json.dumps(data, indent=1) + "\n")
+    print(json.dumps(out, indent=1))
 
 
 def summarize_trace(stats_csv, out_md, command):
@@ -392,15 +433,17 @@ def summarize_counters(pmc_dir, out_md, command):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline step (with --only: profile other workloads alone)")
     ap.add_argument("--only", default=None, help="comma list of extra workloads to run")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one 1 GiB device copy (the reference for HBM counters)")
-    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND", "WORKLOAD"),
+                    help="add WORKLOAD to profiles/traffic.json from two rocprofv3 --pmc runs (no GPU)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv (no GPU)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "OUT_MD", "COMMAND"),
@@ -439,90 +482,79 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    # ---- headline: the whole step, graph-replayed
-    log(f"headline {HEADLINE}: building inputs")
-    head, inp, fc, bc = run_workload(torch, timer, HEADLINE, w, iters=5)
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    inp = None
+    if not args.no_headline:
+        # ---- headline: the whole step, graph-replayed
+        log(f"headline {HEADLINE}: building inputs")
+        head, inp, fc, bc = run_workload(torch, timer, HEADLINE, w, iters=5)
 
-    def step():
-        fc.launch()
-        bc.launch()  # the whole backward: prep, then dK/dV and dQ
+        def step():
+            fc.launch()
+            bc.launch()  # the whole backward: prep, then dK/dV and dQ
 
-    g = timer.capture(step)
-    # the replayed graph must reproduce the eager step bit for bit
-    step()
-    torch.cuda.synchronize()
-    ref = [t.clone() for t in (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)]
-    g.replay()
-    torch.cuda.synchronize()
-    for a, b in zip(ref, (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)):
-        if not torch.equal(a, b):
-            raise SystemExit("bench.py: graph replay differs from the eager step")
-
-    log(f"headline: {args.warmup} warmup + {args.steps} timed steps")
-    for _ in range(args.warmup):
+        g = timer.capture(step)
+        # the replayed graph must reproduce the eager step bit for bit
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)]
         g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
-    gfl = head["gflop"]
-    value = (gfl["fwd"] + gfl["bwd"]) * 1e9 / (ms_per_step * 1e-3) / 1e12
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (fc.o, fc.lse, bc.dq, bc.dk, bc.dv)):
+            if not torch.equal(a, b):
+                raise SystemExit("bench.py: graph replay differs from the eager step")
 
-    # ---- dominant kernel of the step and its roofline
-    stages = ("fwd", "prep", "main") if head["fused_backward"] else ("fwd", "prep", "dkdv", "dq")
-    kt = {k: head["ms"][k] for k in stages}
-    dom = max(kt, key=kt.get)
-    if dom == "prep":
-        nbytes = w.B * w.Hq * w.Lq * (2 * w.D * 2 + 4)
-        roof = {"bound": "hbm", "achieved": nbytes / (kt[dom] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    else:
-        fl_dom = gfl[dom] * 1e9
-        roof = {"bound": "mfma", "achieved": fl_dom / (kt[dom] * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(dom)
-    roof["kernel"] = KERNEL_NAMES[dom]
-    roof["kernel_ms"] = kt[dom]
-
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "gpu_ms_per_step": round(gpu_ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": HEADLINE, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.Lq, "D": w.D,
-                   "causal": True,
-                   "step": "fwd + bwd (prep, then dK/dV and dQ"
-                           + (" in one launch)" if head["fused_backward"] else ")")},
-        "peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roof,
-        "kernels_ms": kt,
-    }
+        log(f"headline: {args.warmup} warmup + {args.steps} timed steps")
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
+        gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+        gfl = head["gflop"]
+        value = (gfl["fwd"] + gfl["bwd"]) * 1e9 / (ms_per_step * 1e-3) / 1e12
+        stages = ("fwd", "prep", "main") if head["fused_backward"] else ("fwd", "prep", "dkdv", "dq")
+        out.update({
+            "value": round(value, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_per_step, 5),
+            "gpu_ms_per_step": round(gpu_ms_per_step, 5),
+            "config": {"workload": HEADLINE, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.Lq, "D": w.D,
+                       "causal": True,
+                       "step": "fwd + bwd (prep, then dK/dV and dQ"
+                               + (" in one launch)" if head["fused_backward"] else ")")},
+            "peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
+            # forward and backward apart (kernel time of each, graph-replayed launches)
+            "peak_frac_fwd": round(head["peak_frac"]["fwd"], 4),
+            "peak_frac_bwd": round(head["peak_frac"]["bwd"], 4),
+            "roofline": roofline(HEADLINE, w, head),
+            "kernels_ms": {k: head["ms"][k] for k in stages},
+        })
 
     # ---- other workloads
     if not args.no_extra:
-        names = ["gqa_causal_4k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32", "gqa_swa_4k",
-                 "gqa_chunk_4k"]
+        names = list(EXTRA)
         if args.only:
-            names = [n for n in names if n in args.only.split(",")]
+            names = [n for n in names + [HEADLINE] if n in args.only.split(",")]
         extra = {}
         for name in names:
             log(f"workload {name}")
             res, _, fc2, bc2 = run_workload(torch, timer, name, WORKLOADS[name], iters=3)
+            res["roofline"] = roofline(name, WORKLOADS[name], res)
             extra[name] = res
             del fc2, bc2
             torch.cuda.empty_cache()
         out["workloads"] = extra
 
     # ---- CPU baseline (rank 0, N = 1 only)
-    if not args.no_cpu:
+    if not args.no_cpu and inp is not None:
         log("cpu baseline: fp64 oracle on the headline step")
         out["cpu_baseline"] = cpu_baseline(w, inp)
     else:

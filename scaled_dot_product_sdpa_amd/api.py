@@ -233,6 +233,19 @@ def _lens(x, B, device, name):
     return x.to(device=device, dtype=torch.int32).contiguous()
 
 
+def _unaliased(t: torch.Tensor) -> torch.Tensor:
+    """t itself, or a contiguous copy when a dimension of size > 1 has stride 0."""
+    if any(st == 0 and n > 1 for st, n in zip(t.stride(), t.shape)):
+        return t.contiguous()
+    return t
+
+
+def _grad_like(t: torch.Tensor, zero: bool) -> torch.Tensor:
+    """A gradient buffer with t's shape and strides, zero-filled when ``zero``."""
+    g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+    return g.zero_() if zero else g
+
+
 def _vp(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -316,7 +329,8 @@ class ForwardCall:
         B, Hq, Lq, _ = qL.shape
         Lk, Dv = kL.shape[2], vL.shape[3]
         if oq is not None:
-            self.o = torch.empty((q.shape[0], Hq, Dv), dtype=q.dtype, device=dev)
+            # rows outside every batch are not written by the library: zeros there
+            self.o = torch.zeros((q.shape[0], Hq, Dv), dtype=q.dtype, device=dev)
             o_st = (0, Dv, Hq * Dv)
         else:
             self.o = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=dev)
@@ -366,6 +380,10 @@ class BackwardCall:
         B = _ragged_batch(q, oq, ok)
         lq = _lens(seq_lens_q, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_q")
         lk = _lens(seq_lens_kv, B if B is not None else _as4d(q, "q").shape[0], dev, "seq_lens_kv")
+        # dq, dk, dv take the strides of q, k, v: an operand that repeats memory along a
+        # dimension (stride 0, an expanded view) is copied first, or several heads or
+        # batches would write their gradients into the same elements
+        q, k, v = _unaliased(q), _unaliased(k), _unaliased(v)
         qL = _Layout(q, "q", oq, _max_len(max_seqlen_q, lq, oq) if oq is not None else None, B)
         kL = _Layout(k, "k", ok, _max_len(max_seqlen_kv, lk, ok) if ok is not None else None, B)
         vL = _Layout(v, "v", ok, kL.shape[2], B)
@@ -395,9 +413,10 @@ class BackwardCall:
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
         self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal, sliding_window)
         qt, kt, vt = qL.tensor, kL.tensor, vL.tensor
-        self.dq = torch.empty_strided(qt.shape, qt.stride(), dtype=qt.dtype, device=dev)
-        self.dk = torch.empty_strided(kt.shape, kt.stride(), dtype=kt.dtype, device=dev)
-        self.dv = torch.empty_strided(vt.shape, vt.stride(), dtype=vt.dtype, device=dev)
+        # a packed (ragged) side leaves the rows outside every batch unwritten: zeros there
+        self.dq = _grad_like(qt, oq is not None)
+        self.dk = _grad_like(kt, ok is not None)
+        self.dv = _grad_like(vt, ok is not None)
         nws = self.lib.sdpa_backward_workspace_bytes(ctypes.byref(self.p))
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self._keep = (qt, kt, vt, o, dO, lse, m, lq, lk, oq, ok)

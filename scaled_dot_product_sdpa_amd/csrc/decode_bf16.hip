@@ -181,8 +181,15 @@ void decode_split_kernel(DecodeArgs a) {
       s1 = mfma16(__builtin_bit_cast(bf16x8, kr[set][1][kk]), qreg[kk], s1);
     }
     // V rows to LDS (the same wave reads them back below; LDS operations of one wave
-    // complete in order), then the register set takes tile t+2
+    // complete in order), then the register set takes tile t+2.  In the window's first
+    // tile the rows before its first key are zeroed: their weight is 0, but the cache
+    // there may hold anything (an evicted page), and 0 * NaN would poison O.
     bf16* vt = Vs[set];
+    if (j0 < klo) {
+#pragma unroll
+      for (int i = 0; i < VLD; ++i)
+        if (j0 + vr + RPL * i < klo) vrg[set][i] = zero16();
+    }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) *reinterpret_cast<u32x4*>(vt + vlds[i]) = vrg[set][i];
     load_tile(t + 2, set);

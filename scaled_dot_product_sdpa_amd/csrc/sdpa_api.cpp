@@ -287,6 +287,20 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
                              {dO, "dO", hq}, {dq, "dq", hq}, {dk, "dk", hk}, {dv, "dv", hk}},
                   mask, lq, lk, lse, hq);
   if (st != SDPA_OK) return st;
+  // dq, dk, dv are written with the strides of q, k, v: a zero batch or head stride along a
+  // dimension of size > 1 would have several gradients land on one element (the batch
+  // stride of a ragged side is unused)
+  {
+    const int64_t* st[3] = {p->q_stride, p->k_stride, p->v_stride};
+    const int32_t heads[3] = {p->Hq, p->Hkv, p->Hkv};
+    const bool ragged[3] = {off_q != nullptr, off_kv != nullptr, off_kv != nullptr};
+    const char* names[3] = {"q", "k", "v"};
+    for (int t = 0; t < 3; ++t)
+      if ((!ragged[t] && p->B > 1 && st[t][0] == 0) || (heads[t] > 1 && st[t][1] == 0))
+        return fail(SDPA_ERR_INVALID_ARGUMENT,
+                    "%s has a zero batch or head stride: its gradient would alias (pass a copy)",
+                    names[t]);
+  }
   const size_t need = sdpa_backward_workspace_bytes(p);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", need,

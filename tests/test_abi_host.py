@@ -138,6 +138,17 @@ def test_backward_rejects(lib, stage):
     nowin = _problem()
     nowin.is_causal, nowin.sliding_window = 0, 16
     assert _bwd(lib, nowin, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+    # gradients take the strides of q, k, v: a zero batch or head stride would alias them
+    for t, ax in (("q_stride", 1), ("k_stride", 0), ("v_stride", 1)):
+        alias = _problem()
+        getattr(alias, t)[ax] = 0
+        assert _bwd(lib, alias, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+        assert "alias" in lib.sdpa_last_error().decode()
+    # ... but a dimension of size 1 may have any stride
+    one = _problem(B=1, Hq=1, Hkv=1)
+    one.q_stride[0] = one.q_stride[1] = one.k_stride[0] = one.k_stride[1] = 0
+    assert _bwd(lib, one, lse=None, stage=stage) == SDPA_ERR_INVALID_ARGUMENT
+    assert "lse" in lib.sdpa_last_error().decode()
 
 
 def test_status_strings_and_version(lib):
@@ -221,6 +232,28 @@ def test_ragged_rejects(lib):
     assert _bwd_ragged(lib, p, nws=16) == SDPA_ERR_WORKSPACE_TOO_SMALL
     assert _fwd_ragged(lib, p, q=None) == SDPA_ERR_INVALID_ARGUMENT
     assert lib.sdpa_last_error().decode() != ""
+
+
+def test_ragged_backward_accepts_unused_batch_stride(lib):
+    """A ragged side's batch stride is zeroed (unused); that is no gradient alias."""
+    p = _problem()
+    assert _bwd_ragged(lib, p, off_kv=None, lse=None) == SDPA_ERR_INVALID_ARGUMENT
+    assert "lse" in lib.sdpa_last_error().decode()
+
+
+def test_binding_copies_aliased_operands():
+    """An expanded (stride-0) operand is copied before its gradient buffer is laid out, so
+    the buffer's strides never repeat memory; packed gradients start as zeros."""
+    import torch
+    from scaled_dot_product_sdpa_amd.api import _grad_like, _unaliased
+    k = torch.randn(1, 1, 8, 64).expand(2, 3, 8, 64)
+    assert k.stride()[:2] == (0, 0)
+    k2 = _unaliased(k)
+    assert k2.is_contiguous() and torch.equal(k2, k)
+    q = torch.randn(2, 3, 8, 64)
+    assert _unaliased(q) is q
+    g = _grad_like(torch.randn(10, 2, 64)[:, :, :], True)
+    assert torch.count_nonzero(g) == 0
 
 
 def test_ragged_ignores_batch_strides_of_ragged_sides(lib):

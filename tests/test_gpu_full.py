@@ -37,14 +37,15 @@ def _oracle_rows(orc, inp, rows):
                             window=inp.get("window", 0))
 
 
-def _slice_group(w, inp, b, g):
+def _slice_groups(w, inp, b, g0, g1):
+    """Batch b with KV heads g0 .. g1-1 and their query heads: an independent problem."""
     G = w.Hq // w.Hkv
-    hs = slice(g * G, (g + 1) * G)
+    hs = slice(g0 * G, g1 * G)
     out = dict(scale=inp["scale"], is_causal=inp["is_causal"], window=inp.get("window", 0))
     out["q"] = inp["q"][b:b + 1, hs]
     out["dO"] = inp["dO"][b:b + 1, hs]
-    out["k"] = inp["k"][b:b + 1, g:g + 1]
-    out["v"] = inp["v"][b:b + 1, g:g + 1]
+    out["k"] = inp["k"][b:b + 1, g0:g1]
+    out["v"] = inp["v"][b:b + 1, g0:g1]
     m = inp["mask"]
     out["mask"] = None if m is None else (m[b:b + 1] if m.shape[1] == 1 else m[b:b + 1, hs])
     out["len_q"] = None if inp["len_q"] is None else inp["len_q"][b:b + 1]
@@ -52,7 +53,7 @@ def _slice_group(w, inp, b, g):
     return out
 
 
-def _check_fwd_rows(orc, w, inp, o, lse, n=96, seed=0):
+def _check_fwd_rows(orc, w, inp, o, lse, n=256, seed=0):
     rows = _rows(w, inp, n, np.random.default_rng(seed))
     o_ref, lse_ref = _oracle_rows(orc, inp, rows)
     idx = tuple(np.array(rows).T)
@@ -64,24 +65,35 @@ def _check_fwd_rows(orc, w, inp, o, lse, n=96, seed=0):
 
 
 def _check_bwd_groups(orc, w, inp, grads, groups):
+    """dQ, dK, dV of the listed (batch, KV head) groups against the oracle.  The groups of
+    one batch with consecutive KV heads go to the oracle as one problem (its backward runs
+    the groups in parallel)."""
     dq, dk, dv = grads
     G = w.Hq // w.Hkv
+    runs = []
+    for b, g in sorted(groups):
+        if runs and runs[-1][0] == b and runs[-1][2] == g:
+            runs[-1][2] = g + 1
+        else:
+            runs.append([b, g, g + 1])
     errs = []
-    for b, g in groups:
-        s = _slice_group(w, inp, b, g)
+    for b, g0, g1 in runs:
+        s = _slice_groups(w, inp, b, g0, g1)
         rq, rk, rv, _ = orc.backward(f64(s["q"]), f64(s["k"]), f64(s["v"]), f64(s["dO"]),
                                      mask=f64(s["mask"]), scale=s["scale"], is_causal=s["is_causal"],
                                      len_q=i32(s["len_q"]), len_kv=i32(s["len_kv"]), window=s["window"])
-        hs = slice(g * G, (g + 1) * G)
-        errs.append((check_grad(f64(dq[b:b + 1, hs]), rq, torch.bfloat16, f"dQ[{b},{g}]"),
-                     check_grad(f64(dk[b:b + 1, g:g + 1]), rk, torch.bfloat16, f"dK[{b},{g}]"),
-                     check_grad(f64(dv[b:b + 1, g:g + 1]), rv, torch.bfloat16, f"dV[{b},{g}]")))
+        for g in range(g0, g1):
+            hs, ho = slice(g * G, (g + 1) * G), slice((g - g0) * G, (g - g0 + 1) * G)
+            go = slice(g - g0, g - g0 + 1)
+            errs.append((check_grad(f64(dq[b:b + 1, hs]), rq[:, ho], torch.bfloat16, f"dQ[{b},{g}]"),
+                         check_grad(f64(dk[b:b + 1, g:g + 1]), rk[:, go], torch.bfloat16, f"dK[{b},{g}]"),
+                         check_grad(f64(dv[b:b + 1, g:g + 1]), rv[:, go], torch.bfloat16, f"dV[{b},{g}]")))
     return errs
 
 
 @pytest.mark.parametrize("name,groups", [
     ("mha_causal_1k", [(0, 0), (3, 15)]),
-    ("gqa_causal_4k", [(1, 7)]),
+    ("gqa_causal_4k", [(0, g) for g in range(8)] + [(1, 7)]),
     ("padded_mask_2k", [(0, 0), (5, 9)]),
     ("gqa_swa_4k", [(0, 3)]),
     ("gqa_chunk_4k", [(1, 5)]),
@@ -102,6 +114,35 @@ def test_full_size_prefill(orc, name, groups):
     banner(f"full {name}: bwd groups {groups} rel-Frobenius {errs}")
     for b, i in fully_masked_rows(inp):
         assert torch.all(grads[0][b, :, i] == 0)
+
+
+def test_full_size_mask_only(orc):
+    """The padded workload with its additive mask alone (no length arrays): the mask blocks
+    the padding, so the result must agree with the oracle and with the run that also passes
+    the lengths, on the same sampled rows and groups."""
+    w = WORKLOADS["padded_mask_2k"]
+    banner("full padded_mask_2k, mask only: drawing inputs on the device")
+    inp = make_inputs(w, device="cuda")
+    o_l, lse_l = gpu_forward(inp)
+    g_l = gpu_backward(inp, o_l, lse_l)
+    mo = dict(inp, len_q=None, len_kv=None)
+    o, lse = gpu_forward(mo)
+    n, e_o, e_l = _check_fwd_rows(orc, w, mo, o, lse)
+    grads = gpu_backward(mo, o, lse)
+    errs = _check_bwd_groups(orc, w, mo, grads, [(0, 0), (5, 9)])
+    banner(f"full padded_mask_2k mask only: fwd {n} rows O {e_o:.2e} LSE {e_l:.2e}; bwd {errs}")
+    for b, i in fully_masked_rows(inp):
+        assert torch.all(o[b, :, i] == 0) and torch.all(torch.isneginf(lse[b, :, i]))
+        assert torch.all(grads[0][b, :, i] == 0)
+    # against the lengths run, over every element
+    d_o = (o.float() - o_l.float()).abs().max().item()
+    fin = torch.isfinite(lse_l)
+    assert torch.equal(fin, torch.isfinite(lse))
+    d_l = (lse[fin] - lse_l[fin]).abs().max().item()
+    assert d_o <= TOL_BF16_O and d_l <= TOL_BF16_LSE, (d_o, d_l)
+    for a, r, nm in zip(grads, g_l, ("dQ", "dK", "dV")):
+        check_grad(f64(a), f64(r), torch.bfloat16, f"{nm} mask-only vs lengths")
+    banner(f"full padded_mask_2k: mask-only vs lengths O {d_o:.2e} LSE {d_l:.2e}")
 
 
 def test_full_size_decode(orc):

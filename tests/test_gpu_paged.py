@@ -56,6 +56,13 @@ def test_paged_decode_matches_contiguous_and_oracle(orc, case):
     inp = make_inputs(w)
     if lr[0] == 0:
         inp["len_kv"][1] = 0  # an empty cache: O = 0, LSE = -inf
+    if win:
+        # keys before the window (an evicted part of the cache) hold NaN, in the contiguous
+        # cache and in the pages alike: the window's first 32-key tile starts below its first
+        # key, and none of those rows may reach O (0 * NaN)
+        for b, n in enumerate(inp["len_kv"].tolist()):
+            inp["k"][b, :, : max(n - win, 0)] = float("nan")
+            inp["v"][b, :, : max(n - win, 0)] = float("nan")
     banner(f"paged decode B={B} Hq={Hq} Hkv={Hkv} Lk={Lk} D={D} page={ps} token_major={token_major} "
            f"window={win}")
     kp, vp, table = _paged(inp, ps, seed=70 + ps, token_major=token_major)
@@ -64,6 +71,7 @@ def test_paged_decode_matches_contiguous_and_oracle(orc, case):
     o_p, l_p = sdpa_decode_paged(d["q"][:, :, 0], kp.cuda(), vp.cuda(), table.cuda(), d["len_kv"],
                                  scale=inp["scale"], sliding_window=win)
     torch.cuda.synchronize()
+    assert torch.isfinite(o_p).all() and torch.isfinite(o_c).all()
     assert torch.equal(o_p, o_c[:, :, 0]) and torch.equal(l_p, l_c[:, :, 0])
     o_ref, lse_ref = oracle_forward(orc, inp)
     compare_forward(inp, o_p.unsqueeze(2), l_p.unsqueeze(2), o_ref, lse_ref)
