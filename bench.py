@@ -265,7 +265,11 @@ def roofline(name, w, res):
                 "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(name, dom)
-    roof["kernel"] = KERNEL_NAMES[dom]
+    kname = KERNEL_NAMES[dom]
+    if w.dtype == "f32":  # the fp32 path's kernels (main: its dK/dV and dQ kernels)
+        kname = {"fwd": "fwd_f32_kernel", "prep": "bwd_prep_f32_kernel", "dkdv": "bwd_dkdv_f32_kernel",
+                 "dq": "bwd_dq_f32_kernel"}.get(dom, kname)
+    roof["kernel"] = kname
     roof["kernel_ms"] = kt[dom]
     return roof
 
