@@ -40,7 +40,7 @@ EXTRA = ["mha_causal_1k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32", "gqa_s
 # kernel-name fragments (as rocprofv3 reports them) of each launch stage
 KERNEL_NAMES = {
     "fwd": "fwd_bf16_kernel", "prep": "bwd_prep_kernel", "dkdv": "bwd_dkdv_kernel",
-    "dq": "bwd_dq_kernel", "main": "bwd_fused_kernel", "decode_split": "decode_split_kernel",
+    "dq": "bwd_dq_", "main": "bwd_fused_kernel", "decode_split": "decode_split_kernel",
     "decode_combine": "decode_combine_kernel",
 }
 # source file of each kernel (traffic counters are dropped once the source changes)
@@ -266,6 +266,8 @@ def roofline(name, w, res):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(name, dom)
     kname = KERNEL_NAMES[dom]
+    if dom == "dq":  # the pipelined dQ kernel at d = 64, the block-sequential one at d = 128
+        kname = "bwd_dq_kernel" if w.D == 64 else "bwd_dq_seq_kernel"
     if w.dtype == "f32":  # the fp32 path's kernels (main: its dK/dV and dQ kernels)
         kname = {"fwd": "fwd_f32_kernel", "prep": "bwd_prep_f32_kernel", "dkdv": "bwd_dkdv_f32_kernel",
                  "dq": "bwd_dq_f32_kernel"}.get(dom, kname)

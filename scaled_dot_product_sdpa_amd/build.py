@@ -21,6 +21,9 @@ CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libsdpa.so"
 SOURCES = ["sdpa_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "attn_f32.hip"]
+# microbenchmarks of the hardware ceilings (not part of libsdpa.so)
+CEIL_LIB = PKG / "libceilings.so"
+CEIL_SOURCE = "ceilings.hip"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -36,9 +39,14 @@ FLAGS = [
 ]
 
 
-def _compile(src: Path, obj: Path, extra=()) -> None:
+# the same without the VGPR-form MFMA flag: the compiler then keeps MFMA accumulators in
+# AGPRs wherever a kernel's registers exceed 256 or it uses AGPRs anyway
+AGPR_FLAGS = [f for f in FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=1")]
+
+
+def _compile(src: Path, obj: Path, extra=(), flags=None) -> None:
     lang = ["-x", "hip"] if src.suffix == ".cpp" else []
-    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, *(FLAGS if flags is None else flags), *extra, *lang, "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -69,6 +77,18 @@ def build(verbose: bool = False, extra=()) -> Path:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    # the ceilings library: its AGPR-form probes are a second object of the same source,
+    # compiled without the flag that forces VGPR-form MFMAs
+    _compile(CSRC / CEIL_SOURCE, BUILD / "ceilings.o", extra)
+    _compile(CSRC / CEIL_SOURCE, BUILD / "ceilings_agpr.o", ["-DCEIL_AGPR_FORM", *extra], flags=AGPR_FLAGS)
+    tmp = CEIL_LIB.with_name(CEIL_LIB.name + f".tmp{os.getpid()}")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
+                        str(BUILD / "ceilings.o"), str(BUILD / "ceilings_agpr.o")],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libceilings.so failed")
+    os.replace(tmp, CEIL_LIB)
     return LIB
 
 

@@ -1,0 +1,107 @@
+"""Ceilings of the gfx950 resources the attention kernels use, measured on the GPU.
+
+``python -m scaled_dot_product_sdpa_amd.ceilings`` runs the probes of ``csrc/ceilings.hip``
+(libceilings.so, built with the library) and prints one markdown table: the bf16 MFMA
+rate, LDS read rates in the two operand patterns of the kernels, the forward's matrix
+skeleton (S and PV products with their LDS operand reads, no softmax) at 32 and 64 query
+rows per wave, with the MFMA accumulators in VGPRs or AGPRs, and MFMA next to independent
+vector arithmetic.  Each probe fills every SIMD with 1 or 2 waves and is timed with HIP
+events around five back-to-back launches (after a warm-up launch); the shader clock under
+MFMA load is read with s_memtime against the 100 MHz constant-rate counter.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import sys
+
+from .build import CEIL_LIB
+
+PEAK_BF16_TFLOPS = 2500.0
+CUS = 256
+REPS = 5
+
+# id: (name, MFMAs per wave per iteration, LDS bytes per wave per iteration)
+PROBES = {
+    0: ("MFMA 32x32x16 bf16, one accumulation chain", 1, 0),
+    1: ("MFMA 32x32x16 bf16, four independent chains", 4, 0),
+    2: ("LDS 16-byte row reads (K operand pattern)", 0, 16 * 1024),
+    3: ("LDS ds_read_b64_tr_b16 pairs (V^T operand pattern)", 0, 16 * 1024),
+    6: ("forward skeleton, 32 rows per wave, operands in registers", 32, 0),
+    7: ("forward skeleton, 64 rows per wave, operands in registers", 64, 0),
+    4: ("forward skeleton, 32 rows per wave, LDS operands, VGPR accumulators", 32, 32 * 1024),
+    15: ("forward skeleton, 32 rows per wave, LDS operands, AGPR accumulators", 32, 32 * 1024),
+    5: ("forward skeleton, 64 rows per wave, LDS operands, VGPR accumulators", 64, 32 * 1024),
+    16: ("forward skeleton, 64 rows per wave, LDS operands, AGPR accumulators", 64, 32 * 1024),
+    8: ("MFMA + 4 v_fma_f32 per MFMA", 8, 0),
+    9: ("MFMA + 6 v_fma_f32 per MFMA", 8, 0),
+    10: ("MFMA + 8 v_fma_f32 per MFMA", 8, 0),
+    11: ("MFMA + 2 (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
+    12: ("MFMA + 4 (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
+    13: ("MFMA + 4 v_fma_f32 + (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
+    14: ("MFMA + 5 v_fma_f32 + (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
+}
+SKELETON = {4, 5, 6, 7, 15, 16}
+# probes whose registers do not fit two waves per SIMD
+ONE_WAVE_ONLY = {16}
+# iterations per launch, per probe kind (a few hundred microseconds each)
+ITERS = {"mfma": 4000, "lds": 4000, "skeleton": 1000, "mix": 2000}
+
+
+def _iters(pid, scale):
+    kind = "mfma" if pid in (0, 1) else "lds" if pid in (2, 3) else "skeleton" if pid in SKELETON else "mix"
+    return max(1, int(ITERS[kind] * scale))
+
+
+def run(scale: float = 1.0) -> str:
+    import torch
+    lib = ctypes.CDLL(str(CEIL_LIB))
+    lib.ceil_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_probe.restype = ctypes.c_int
+    out = torch.empty(65536 * 2, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(pid, wps, it):
+        rc = lib.ceil_probe(pid, wps, ctypes.c_void_p(out.data_ptr()), it, stream)
+        if rc != 0:
+            raise RuntimeError(f"probe {pid}: status {rc}")
+
+    # shader clock under MFMA load
+    it = _iters(0, scale)
+    launch(17, 2, it)
+    torch.cuda.synchronize()
+    cyc, ticks = out[0].item(), out[1].item()
+    ghz = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else float("nan")
+    rows = [f"Shader clock under MFMA load (s_memtime over s_memrealtime at 100 MHz): {ghz:.2f} GHz; "
+            f"the MFMA peak at that clock is {PEAK_BF16_TFLOPS * ghz / 2.4:.0f} TFLOP/s.", "",
+            "| probe | waves / SIMD | us per launch | MFMA TFLOP/s | % of bf16 peak | LDS TB/s | LDS B/clk/CU |",
+            "|---|---:|---:|---:|---:|---:|---:|"]
+    for pid, (name, mf, lds_bytes) in PROBES.items():
+        for wps in (1, 2):
+            if wps == 2 and pid in ONE_WAVE_ONLY:
+                continue
+            it = _iters(pid, scale)
+            launch(pid, wps, it)  # warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(REPS):
+                launch(pid, wps, it)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / REPS
+            waves = CUS * 4 * wps
+            # MFMAs per wave per iteration: the chains (0, 1); 2 blocks x 2 products x 8 per
+            # 32-row group (skeleton); 8 (mixes)
+            mfmas = (mf // 32) * 2 * 2 * 8 if pid in SKELETON else mf
+            tf = waves * it * mfmas * 32768 / (us * 1e-6) / 1e12 if mfmas else None
+            lds = waves * it * lds_bytes / (us * 1e-6) / 1e12 if lds_bytes else None
+            per_clk = lds * 1e12 / CUS / (ghz * 1e9) if lds else None
+            rows.append(f"| {name} | {wps} | {us:.1f} | " + ("–" if tf is None else f"{tf:.0f}") + " | " +
+                        ("–" if tf is None else f"{100 * tf / PEAK_BF16_TFLOPS:.1f}") + " | " +
+                        ("–" if lds is None else f"{lds:.1f}") + " | " +
+                        ("–" if per_clk is None else f"{per_clk:.0f}") + " |")
+    return "\n".join(rows)
+
+
+if __name__ == "__main__":
+    print(run(float(sys.argv[1]) if len(sys.argv) > 1 else 1.0))

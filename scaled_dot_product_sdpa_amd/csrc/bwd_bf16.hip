@@ -159,9 +159,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   const int qt_end = (j0 < kstop) ? (q_last + kQT - 1) / kQT : 0;
   const int n_q_tiles = qt_end > qt_begin ? qt_end - qt_begin : 0;
   const int total = n_q_tiles * p.G;
+  // The query tiles of each head are walked last to first: every key tile of the group
+  // starts at the same (last) query tile and walks the same sequence, so the workgroups of
+  // a group that run at once on one XCD read each Q / dO tile from its L2 (walking from
+  // each key tile's own diagonal instead, they would stream the rows out of step and
+  // thrash the L2).
   auto tile_rows = [&](int it, int& h, int& i0) {
     h = g * p.G + it / n_q_tiles;
-    i0 = (qt_begin + it % n_q_tiles) * kQT;
+    i0 = (qt_end - 1 - it % n_q_tiles) * kQT;
   };
 
   // ---- tiles HBM -> LDS: Q and dO rows (swizzled), lse2 and D rows, mask rows.
