@@ -123,6 +123,26 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments and results are those of sdpa_forward; where sdpa_forward needs a
+ * workspace (the single-query decode's split partial results), this call uses a scratch
+ * array built into the library instead: 16 MiB of device memory per GPU, held from the
+ * first call on that GPU until the process ends.  It allocates nothing, neither on the host
+ * nor on the device.
+ *   Limit: a problem whose sdpa_forward_workspace_bytes exceeds 16 MiB (decode partials of
+ *   more than about 32k (batch, query head, split) rows at D = 128) is rejected with
+ *   SDPA_ERR_UNSUPPORTED before anything is launched.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last call's contents:
+ *   calls that overlap on one GPU (on different streams) race and must be ordered by the
+ *   caller.  Calls on the same stream are ordered by the stream.
+ */
+sdpa_status sdpa_forward_noalloc(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                                 const void* mask_or_null, const int32_t* seq_lens_q_or_null,
+                                 const int32_t* seq_lens_kv_or_null, void* o, float* lse,
+                                 void* stream);
+
+/*
  * Backward.  Takes the forward's o and lse (same problem, mask, causal flag and lengths)
  * and dO (B,Hq,Lq,Dv); writes dq, dk, dv (shapes and strides of q, k, v).  Every element
  * of dq, dk, dv is written (zeros where no gradient flows).  Deterministic: no atomics.

@@ -13,9 +13,10 @@ has not been built (``python -m scaled_dot_product_sdpa_amd.build``).
 
 from .api import (BACKWARD_STAGES, CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, EXPORTS, LIB_PATH,
                   BackwardCall, ForwardCall, PagedDecode, PagedDecodeCall, Problem, SdpaError,
-                  load_library, sdpa_backward, sdpa_decode_paged, sdpa_forward)
+                  load_library, sdpa_backward, sdpa_decode_paged, sdpa_forward,
+                  sdpa_forward_noalloc)
 
-__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode_paged", "ForwardCall", "BackwardCall",
+__all__ = ["sdpa_forward", "sdpa_forward_noalloc", "sdpa_backward", "sdpa_decode_paged", "ForwardCall", "BackwardCall",
            "PagedDecodeCall", "PagedDecode", "BACKWARD_STAGES",
            "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "load_library", "LIB_PATH", "EXPORTS",
            "Problem", "SdpaError"]

@@ -34,7 +34,7 @@ EXPORTS = (
     "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
     "sdpa_backward_main",
     "sdpa_status_string", "sdpa_last_error", "sdpa_version", "sdpa_decode_paged_workspace_bytes",
-    "sdpa_decode_paged", "sdpa_forward_ragged", "sdpa_backward_ragged",
+    "sdpa_decode_paged", "sdpa_forward_ragged", "sdpa_backward_ragged", "sdpa_forward_noalloc",
 )
 BACKWARD_STAGES = ("prep", "dkdv", "dq", "main")
 
@@ -92,6 +92,8 @@ def load_library(path: Path | str | None = None):
     lib.sdpa_backward_workspace_bytes.restype = sz
     lib.sdpa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_forward.restype = ctypes.c_int
+    lib.sdpa_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sdpa_forward_noalloc.restype = ctypes.c_int
     for name in ("sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
                  "sdpa_backward_main"):
         f = getattr(lib, name)
@@ -313,9 +315,11 @@ class ForwardCall:
 
     def __init__(self, q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
                  seq_lens_kv=None, return_lse=True, offsets_q=None, offsets_kv=None,
-                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0):
+                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0, noalloc=False):
         self.lib = load_library()
         self.ragged = offsets_q is not None or offsets_kv is not None
+        if noalloc and self.ragged:
+            raise ValueError("sdpa: the no-allocation forward takes padded (B, H, L, D) tensors")
         self.squeeze = q.dim() == 3 and not self.ragged
         _check_io(q, k, v, *([mask] if mask is not None else []))
         dev = q.device
@@ -338,11 +342,17 @@ class ForwardCall:
         self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev) if return_lse else None
         m, mst = _mask4d(mask, B, Hq, Lq, Lk)
         self.p = make_problem(qL, kL, vL, o_st, mst, scale, is_causal, sliding_window)
-        nws = self.lib.sdpa_forward_workspace_bytes(ctypes.byref(self.p))
-        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self._keep = (qL.tensor, kL.tensor, vL.tensor, m, lq, lk, oq, ok)
         self.device = dev
         ptrs = [_vp(qL.tensor), _vp(kL.tensor), _vp(vL.tensor), _vp(m), _vp(lq), _vp(lk)]
+        if noalloc:
+            # sdpa_forward_noalloc: the library's built-in scratch replaces the workspace
+            self.ws = None
+            self.args = [ctypes.byref(self.p), *ptrs, _vp(self.o), _vp(self.lse)]
+            self.fn = self.lib.sdpa_forward_noalloc
+            return
+        nws = self.lib.sdpa_forward_workspace_bytes(ctypes.byref(self.p))
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         if self.ragged:
             ptrs += [_vp(oq), _vp(ok)]
         self.args = [ctypes.byref(self.p), *ptrs, _vp(self.o), _vp(self.lse), _vp(self.ws), nws]
@@ -460,6 +470,17 @@ def sdpa_forward(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=Non
     call.launch()
     o, lse = call.result()
     return (o, lse) if return_lse else o
+
+
+def sdpa_forward_noalloc(q, k, v, mask=None, scale=None, is_causal=False, seq_lens_q=None,
+                         seq_lens_kv=None, sliding_window=0):
+    """(O, LSE) like ``sdpa_forward``, through the C ABI's ``sdpa_forward_noalloc``: the
+    library uses its built-in per-GPU scratch where the decode needs a workspace (see
+    include/sdpa.h for its limit); only the outputs are allocated here."""
+    call = ForwardCall(q, k, v, mask, scale, is_causal, seq_lens_q, seq_lens_kv,
+                       sliding_window=sliding_window, noalloc=True)
+    call.launch()
+    return call.result()
 
 
 def sdpa_backward(q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False, seq_lens_q=None,

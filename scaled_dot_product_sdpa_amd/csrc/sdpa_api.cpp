@@ -14,9 +14,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <utility>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/sdpa.h"
 #include "launch.h"
@@ -260,6 +261,58 @@ sdpa_status sdpa_forward(const sdpa_problem* p, const void* q, const void* k, co
                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(p, q, k, v, mask, lq, lk, nullptr, nullptr, o, lse, workspace,
                       workspace_bytes, stream);
+}
+
+// ---- The forward without a workspace argument, for callers that cannot allocate device
+// memory.  The only forward path with a workspace is the split-KV decode (its partial
+// results); here they live in `scratch`, a file-scope device array of kScratchBytes that
+// each GPU holds for the life of the process.  Its address on a device is looked up once
+// per device (with that device current) and kept; host code never passes the array's name
+// itself, which on the host is only a stand-in for the device symbol.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sdpa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SDPA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(SDPA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDPA_OK;
+}
+}  // namespace
+
+sdpa_status sdpa_forward_noalloc(const sdpa_problem* p, const void* q, const void* k, const void* v,
+                                 const void* mask, const int32_t* lq, const int32_t* lk, void* o,
+                                 float* lse, void* stream) {
+  sdpa_status st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  const size_t need = use_decode(p, mask != nullptr) ? sdpa_forward_workspace_bytes(p) : 0;
+  if (need > kScratchBytes)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "this problem needs %zu bytes of workspace; the built-in scratch holds %zu (use "
+                "sdpa_forward with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != SDPA_OK) return st;
+  }
+  return forward_impl(p, q, k, v, mask, lq, lk, nullptr, nullptr, o, lse, ws, need, stream);
 }
 
 sdpa_status sdpa_forward_ragged(const sdpa_problem* p, const void* q, const void* k,

@@ -151,6 +151,20 @@ def test_backward_rejects(lib, stage):
     assert "lse" in lib.sdpa_last_error().decode()
 
 
+def test_noalloc_forward_rejects_before_launch(lib):
+    """The no-allocation forward validates like sdpa_forward and refuses a decode whose
+    partial results would not fit its built-in 16 MiB scratch, before any HIP call."""
+    p = _problem(Hq=3)
+    assert lib.sdpa_forward_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                                    None) == SDPA_ERR_INVALID_ARGUMENT
+    big = _problem(B=512, Hq=32, Hkv=8, Lq=1, Lk=8192, D=128)
+    need = lib.sdpa_forward_workspace_bytes(ctypes.byref(big))
+    assert need > (16 << 20)
+    assert lib.sdpa_forward_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE,
+                                    None) == SDPA_ERR_UNSUPPORTED
+    assert "scratch" in lib.sdpa_last_error().decode()
+
+
 def test_status_strings_and_version(lib):
     assert lib.sdpa_status_string(0) == b"ok"
     assert lib.sdpa_status_string(SDPA_ERR_WORKSPACE_TOO_SMALL) == b"workspace too small"
