@@ -527,6 +527,25 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   const int64_t rowid = ((int64_t)b * p.Hq + h) * p.Lq + qi;
   const float nl2 = qok ? -a.lse2[rowid] : kNegInf;  // exp2 offset of this lane's row
   const float dsum = qok ? a.dsum[rowid] : 0.f;
+  // Mask values of block bi for this lane (keys 32*bi + 16*hi + 0..15), read two blocks
+  // ahead into the registers of the block's parity (mk_e, mk_o): each load is issued
+  // before the wait ahead of the tile barrier that precedes its use, so it adds no wait of
+  // its own (the compiler cannot see the tile copies and would otherwise wait for all of
+  // them, the next tile's included, before the first use).
+  auto mask_vec_ok = [&](int bi) { return p.mask_vec && qok && 32 * bi + 16 * hi + 16 <= p.Lk; };
+  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
+    if (MASK && bi < nvis && mask_vec_ok(bi)) {
+      const bf16* mp = mb_ + (int64_t)qi * p.m_si + 32 * bi + 16 * hi;
+      m[0] = ld16(mp);
+      m[1] = ld16(mp + 8);
+    } else {
+      m[0] = zero16();
+      m[1] = zero16();
+    }
+  };
+  u32x4 mk_e[2], mk_o[2];
+  load_mask(2 * t0, mk_e);
+  load_mask(2 * t0 + 1, mk_o);
   wait_vmem();
   if (n_tiles > t0 + 1) load_tile((t0 + 1) * kBN, K1, V1);
 
@@ -540,19 +559,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
-
-  // mask values of block bi for this lane (keys 32*bi + 16*hi + 0..15), one block ahead
-  auto mask_vec_ok = [&](int bi) { return p.mask_vec && qok && 32 * bi + 16 * hi + 16 <= p.Lk; };
-  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
-    if (MASK && bi < nvis && mask_vec_ok(bi)) {
-      const bf16* mp = mb_ + (int64_t)qi * p.m_si + 32 * bi + 16 * hi;
-      m[0] = ld16(mp);
-      m[1] = ld16(mp + 8);
-    } else {
-      m[0] = zero16();
-      m[1] = zero16();
-    }
-  };
 
   // dQ^T of a block runs one block late: B operand bf16 dS^T (zero before the first
   // block), A operand K^T read from the block's tile just in time.
@@ -568,15 +574,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     dq_acc[mb] = mfma32(op, ds[half], dq_acc[mb]);
   };
 
-  u32x4 mk[2];
-  load_mask(2 * t0, mk);
   // ---- one pipeline phase for block bi (keys kb*32.. of Kc/Vc; the previous block's keys
   // kbp*32.. of Kp; the next block's keys kbn*32.. of Kn/Vn).  Region 1: dQ MFMAs of block
   // bi-1 with the P, dS arithmetic of block bi.  Region 2: S^T, dP^T MFMAs of block bi+1
   // with the rest of it.  The S^T, dP^T of the block after a wave's last are never used.
   auto phase = [&](int bi, const bf16* Kp, int kbp, const bf16* Kn, const bf16* Vn, int kbn,
                    f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx, const bf16x8 (&ds_prev)[2],
-                   bf16x8 (&ds)[2]) __attribute__((always_inline)) {
+                   bf16x8 (&ds)[2], u32x4 (&mk)[2]) __attribute__((always_inline)) {
     if (bi >= nvis) {
       // the wave's last block: its dQ, while its K tile is still resident
       if (bi == nvis && bi > 2 * t0) {
@@ -586,8 +590,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
       return;
     }
     const int key0 = 32 * bi + 16 * hi;  // lane holds query qi and keys key0 + v
-    u32x4 mk_next[2];
-    if (MASK) load_mask(bi + 1, mk_next);
     float mbias[16];
     if (MASK) {
       if (mask_vec_ok(bi)) {
@@ -599,6 +601,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
         for (int v = 0; v < 16; ++v)
           mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
       }
+      load_mask(bi + 2, mk);
     }
     const bool partial = (32 * bi + 32 > kv_end) || (CAUSAL && 32 * bi + 31 > wq_lo + coff) ||
                          (wq_lo + 32 > q_end) || (W > 0 && 32 * bi <= wq_hi + coff - W);
@@ -667,19 +670,19 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (MASK) { mk[0] = mk_next[0]; mk[1] = mk_next[1]; }
   };
 
   // One tile step (two blocks); unrolled by three over the LDS buffers (see the forward).
   f32x16 s_a = f32x16{}, dp_a = f32x16{}, s_b = f32x16{}, dp_b = f32x16{};
   auto step = [&](int t, const bf16* Kp, const bf16* Kc, const bf16* Vc, const bf16* Kn,
                   const bf16* Vn, bf16* Kl, bf16* Vl) __attribute__((always_inline)) {
-    phase(2 * t, Kp, 1, Kc, Vc, 1, s_a, dp_a, s_b, dp_b, ds_b, ds_a);
-    // tile t+1 has landed for every wave, and no wave still reads tile t-1
-    if (t + 1 < n_tiles) wait_vmem();
+    phase(2 * t, Kp, 1, Kc, Vc, 1, s_a, dp_a, s_b, dp_b, ds_b, ds_a, mk_e);
+    // tile t+1 has landed for every wave, and no wave still reads tile t-1 (unconditional,
+    // so that the compiler sees every earlier load complete on every path)
+    wait_vmem();
     __syncthreads();
     if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
-    phase(2 * t + 1, Kc, 0, Kn, Vn, 0, s_b, dp_b, s_a, dp_a, ds_a, ds_b);
+    phase(2 * t + 1, Kc, 0, Kn, Vn, 0, s_b, dp_b, s_a, dp_a, ds_a, ds_b, mk_o);
   };
 
   if (n_tiles > t0) {
@@ -759,6 +762,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 K1[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V0[TILE];
   __shared__ __attribute__((aligned(16))) bf16 V1[TILE];
+  // With a mask whose rows allow 16-byte copies: each wave's 32 mask rows of the tile's two
+  // 32-key blocks, one 2 KB region per (wave, block) (see load_mask)
+  constexpr int MREG = 32 * 32;
+  __shared__ __attribute__((aligned(16))) bf16 Ms[MASK ? NW * 2 * MREG : 8];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -826,11 +833,86 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
+  // This lane's LDS element offsets inside a tile, computed once and hidden from the
+  // compiler (pin): a read then adds its buffer and block row as a constant in the
+  // instruction's offset field.  Otherwise the compiler keeps a separate loop-invariant
+  // address per buffer and read, more registers than the kernel has, and spills them.
+  // A operands (tile_row8 of row krow_l at logical chunk 2kk + hi; row block kb adds 32 D):
+  int aoff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    aoff[kk] = krow_l * D + (((2 * kk + hi) ^ swz<D>(krow_l)) * 8);
+    pin(aoff[kk]);
+  }
+  // transposed operands (tile_tr8 of rows tr0 .. tr0 + 7, tr0 = 16 hi + arow, at logical
+  // chunk tchunk + 4 mb; row block kb and half add 32 D kb + 8 D half, which leave the
+  // swizzle unchanged):
+  int toff[D / 32][2];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    const int tr0 = 16 * hi + arow, c = tchunk + 4 * mb;
+    toff[mb][0] = tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf;
+    toff[mb][1] = (tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf;
+    pin(toff[mb][0]);
+    pin(toff[mb][1]);
+  }
+  auto a_op = [&](const bf16* T, int kb, int kk) {
+    return *reinterpret_cast<const bf16x8*>(T + kb * 32 * D + aoff[kk]);
+  };
+  auto t_op = [&](const bf16* T, int kb, int half, int mb) {
+    const bf16* base = T + (kb * 32 + 8 * half) * D;
+    return join_tr(lds_read_tr4(base + toff[mb][0]), lds_read_tr4(base + toff[mb][1]));
+  };
+
+  // ---- mask staging (MASK and 16-byte mask rows).  Only this wave reads its rows, so it
+  // fills its own regions without a barrier: the mask of block kb of tile t+1 is copied
+  // into region (wave, kb) as soon as the wave has read that block of tile t, and is waited
+  // for with explicit counts of the copies issued after it (the compiler cannot see them).
+  // Per wave, in issue order: tile t+1's K/V copies (NC), then the mask of tile t+1's
+  // block 0 (two copies, during block 0 of tile t), then its block 1 (two copies).
+  // A region holds rows r = 0..31 as four 16-byte chunks; logical chunk c of row r sits at
+  // chunk 4r + (c ^ ((r >> 2) & 3)), so the 16-lane phases of a read (sixteen rows at one
+  // chunk) hit sixteen distinct bank groups.
+  const bool mstage = MASK && p.mask_vec;
+  constexpr int NC = 2 * TileCopy<kBN, D, NW>::PER_WAVE;
+  uint32_t mvo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pc = 64 * i + lane, r = pc >> 2, c = (pc & 3) ^ ((r >> 2) & 3);
+    mvo[i] = (uint32_t)(((int64_t)r * p.m_si + 8 * c) * 2);
+  }
+  auto load_mask = [&](int key_lo, int kb) {
+    const int nr = min(p.Lq - wq_lo, 32);
+    const int64_t bytes = nr > 0 && key_lo < p.Lk ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - key_lo) * 2 : 0;
+    const i32x4 rs = raw_rsrc(mb_ + (int64_t)wq_lo * p.m_si + key_lo, bytes);
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buffer_to_lds<16>(rs, Ms, ((uw * 2 + kb) * 2 + i) * 1024, mvo[i]);
+  };
+  // tile t's K/V copies have landed (with staging, the four mask copies after them may not)
+  auto wait_tile = [&]() {
+    if (mstage) wait_vmem_le<4>();
+    else wait_vmem();
+  };
+  // the mask copies of the block now in use have landed: after them come the other block's
+  // two copies and, unless this is the last tile, the next tile's K/V copies
+  auto wait_mask = [&](bool next_tile) {
+    if (next_tile) wait_vmem_le<NC + 2>();
+    else wait_vmem_le<2>();
+  };
 
   auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
                   __attribute__((always_inline)) {
     const int j0 = t * kBN;
-    wait_vmem();
+    // re-pinned every step, so that no buffer's addresses are hoisted out of the loop
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) pin(aoff[kk]);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      pin(toff[mb][0]);
+      pin(toff[mb][1]);
+    }
+    wait_tile();
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
     const bool partial_t = (j0 + kBN > kv_end) || (CAUSAL && j0 + kBN - 1 > wq_lo + coff) ||
@@ -839,38 +921,47 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const int key_lo = j0 + kb * 32;
       if (!(wq_lo < q_end && key_lo < kv_stop && (!CAUSAL || key_lo <= wq_hi + coff) &&
-            (W == 0 || key_lo + 31 > wq_lo + coff - W)))
+            (W == 0 || key_lo + 31 > wq_lo + coff - W))) {
+        if (mstage) load_mask(key_lo + kBN, kb);
         continue;
+      }
       // S^T = K Q^T and dP^T = V dO^T for keys key_lo + perm
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       {
-        const int kr = kb * 32 + krow_l;
-
         bf16x8 op[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          op[kk] = tile_row8<D>(Kt, kr, 2 * kk + hi);
+        for (int kk = 0; kk < D / 16; ++kk) op[kk] = a_op(Kt, kb, kk);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) s_acc = mfma32(op[kk], qreg[kk], s_acc);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          op[kk] = tile_row8<D>(Vt, kr, 2 * kk + hi);
+        for (int kk = 0; kk < D / 16; ++kk) op[kk] = a_op(Vt, kb, kk);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) dp_acc = mfma32(op[kk], doreg[kk], dp_acc);
       }
       // lane holds query qi and keys key0 + v
       const int key0 = key_lo + 16 * hi;
-      float mv[16];
+      // with a mask, s_acc becomes the exp2 argument here (scores in log2 units less lse2)
       if (MASK) {
-        if (p.mask_vec && qok && key0 + 16 <= p.Lk) {
-          const bf16* mp = mb_ + (int64_t)qi * p.m_si + key0;
-          bf16x8 b0 = __builtin_bit_cast(bf16x8, ld16(mp)), b1 = __builtin_bit_cast(bf16x8, ld16(mp + 8));
+        if (mstage) {
+          wait_mask(t + 1 < n_tiles);
+          const bf16* mr = Ms + (wave * 2 + kb) * MREG + 4 * 8 * l32;
+          const int sw = (l32 >> 2) & 3;
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(mr + 8 * ((2 * hi) ^ sw));
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(mr + 8 * ((2 * hi + 1) ^ sw));
 #pragma unroll
-          for (int v = 0; v < 8; ++v) { mv[v] = bf2f(b0[v]) * kLog2e; mv[v + 8] = bf2f(b1[v]) * kLog2e; }
+          for (int v = 0; v < 8; ++v) {
+            s_acc[v] = fmaf(s_acc[v], c2, bf2f(b0[v]) * kLog2e - lse2);
+            s_acc[v + 8] = fmaf(s_acc[v + 8], c2, bf2f(b1[v]) * kLog2e - lse2);
+          }
+          // the region is refilled only after these reads have returned
+          wait_lds();
+          load_mask(key_lo + kBN, kb);
         } else {
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            mv[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
+          for (int v = 0; v < 16; ++v) {
+            const float mv = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) : 0.f;
+            s_acc[v] = fmaf(s_acc[v], c2, mv * kLog2e - lse2);
+          }
         }
       }
       bf16x8 dsb[2];
@@ -879,7 +970,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
           const int v = half * 8 + t8;
-          float x = fmaf(s_acc[v], c2, MASK ? mv[v] - lse2 : -lse2);
+          float x = MASK ? s_acc[v] : fmaf(s_acc[v], c2, -lse2);
           if (partial_t) {
             const int key = key0 + v;
             const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff) &&
@@ -893,21 +984,29 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
       // dQ^T += K^T dS^T  (K^T via transposing LDS reads)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
         bf16x8 kT[D / 32];
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) kT[mb] = tile_tr8<D>(Kt, tr, tchunk + 4 * mb, thalf);
+        for (int mb = 0; mb < D / 32; ++mb) kT[mb] = t_op(Kt, kb, half, mb);
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) dq_acc[mb] = mfma32(kT[mb], dsb[half], dq_acc[mb]);
       }
     }
   };
 
-  if (n_tiles > t0) load_tile(t0 * kBN, K0, V0);
+  if (n_tiles > t0) {
+    load_tile(t0 * kBN, K0, V0);
+    if (mstage) {
+      load_mask(t0 * kBN, 0);
+      load_mask(t0 * kBN + 32, 1);
+    }
+  }
   for (int t = t0; t < n_tiles; t += 2) {
     step(t, K0, V0, K1, V1);
     if (t + 1 < n_tiles) step(t + 1, K1, V1, K0, V0);
   }
+  // the last tile's mask copies (of keys past the tiles) must land before the workgroup
+  // ends and its LDS is handed to another
+  if (mstage) wait_vmem();
 
   if (qi < q_rows_out(p, q_end)) {
     bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + q_base(p, b) + h * p.q_sh + (int64_t)qi * p.q_sl;

@@ -121,6 +121,29 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // per k-step) land first; tile 1 streams in behind the first block.
   if (n_tiles > t0) load_tile(t0 * kBN, Kb[0], Vb[0]);
   const int qrow = wq_lo + l32;
+
+  // Mask values of block `bi` for this lane (keys 32*bi + 16*hi + 0..15 of row qrow),
+  // read two blocks ahead (see body).  Rows whose mask cannot be read with 16-byte loads
+  // take the element path in pre_scores.
+  auto mask_vec_ok = [&](int bi) {
+    return p.mask_vec && qrow < q_end && 32 * bi + 16 * hi + 16 <= p.Lk;
+  };
+  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
+    if (MASK && bi < nvis && mask_vec_ok(bi)) {
+      const bf16* mp = mb_ + (int64_t)qrow * p.m_si + 32 * bi + 16 * hi;
+      m[0] = ld16(mp);
+      m[1] = ld16(mp + 8);
+    } else {
+      m[0] = zero16();
+      m[1] = zero16();
+    }
+  };
+
+  // Even blocks keep their mask values in mk_e, odd blocks in mk_o; the first two land
+  // with the Q rows.
+  u32x4 mk_e[2], mk_o[2];
+  load_mask(2 * t0, mk_e);
+  load_mask(2 * t0 + 1, mk_o);
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -146,23 +169,6 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const int arow = (lane & 15) >> 2;
   const int vchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int vhalf = 4 * (lane & 1);
-
-  // Mask values of block `bi` for this lane (keys 32*bi + 16*hi + 0..15 of row qrow),
-  // read one block ahead.  Rows whose mask cannot be read with 16-byte loads take the
-  // element path in `scores`.
-  auto mask_vec_ok = [&](int bi) {
-    return p.mask_vec && qrow < q_end && 32 * bi + 16 * hi + 16 <= p.Lk;
-  };
-  auto load_mask = [&](int bi, u32x4 (&m)[2]) {
-    if (MASK && bi < nvis && mask_vec_ok(bi)) {
-      const bf16* mp = mb_ + (int64_t)qrow * p.m_si + 32 * bi + 16 * hi;
-      m[0] = ld16(mp);
-      m[1] = ld16(mp + 8);
-    } else {
-      m[0] = zero16();
-      m[1] = zero16();
-    }
-  };
 
   constexpr int NS = D / 16;  // S MFMAs per block = K operand reads = PV MFMAs = V reads
   constexpr int E = 16 / NS;  // scores per lane handled in one pipeline slot
@@ -266,8 +272,6 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 
   // S of the current block and of the next one; the two phases of a tile step swap them.
   f32x16 sacc_a = f32x16{}, sacc_b = f32x16{};
-  u32x4 mk[2];
-  load_mask(2 * t0, mk);
 
   // ---- one pipeline phase for block bi (V rows kb*32.. of Vt; the next block's K rows
   // kbn*32.. of Kn).  Region 1: PV MFMAs of block bi-1 with the row max of block bi.
@@ -276,9 +280,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // with sched_barrier so each MFMA issues next to its share of vector work.
   // The S of block bi+1 is computed even past the wave's last block (from whatever the
   // buffer holds; never used), which keeps one code path.
+  // With a mask, the block takes its mask values from `mk` and requests those of block
+  // bi+2 into the same registers.  The load is issued before the wait ahead of the next
+  // tile barrier and used only after it, so it adds no wait of its own (the compiler, which
+  // cannot see the tile copies, would otherwise wait for everything in flight, the next
+  // tile's copy included, before the first use of a mask value).
   auto body = [&](int bi, const bf16* Vt, int kb, const bf16* Kn, int kbn, f32x16& x,
-                  f32x16& snext) __attribute__((always_inline)) {
-    u32x4 mk_next[2];
+                  f32x16& snext, u32x4 (&mk)[2]) __attribute__((always_inline)) {
     bf16x8 kop[NS];
     pre_scores(bi, x, mk);
     // region 1
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       if (j < KPRE) kop[j] = read_k1(Kn, kbn, j);
-      if (MASK && j == 0) load_mask(bi + 1, mk_next);
+      if (MASK && j == 0) load_mask(bi + 2, mk);
       pv_mfma1(j);
 #pragma unroll
       for (int v = j * E; v < (j + 1) * E; ++v) mx = fmaxf(mx, x[v]);
@@ -315,11 +323,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int pr = i * P; pr < (i + 1) * P; ++pr) stage_c(pr, t, pv_p);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (MASK) { mk[0] = mk_next[0]; mk[1] = mk_next[1]; }
   };
   auto phase = [&](int bi, const bf16* Vt, int kb, const bf16* Kn, int kbn, f32x16& sacc,
-                   f32x16& snext) __attribute__((always_inline)) {
-    if (bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext);
+                   f32x16& snext, u32x4 (&mk)[2]) __attribute__((always_inline)) {
+    if (bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext, mk);
   };
 
   // One tile step; the loop below is unrolled by six (two K buffers, three V buffers) so
@@ -327,14 +334,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl)
                   __attribute__((always_inline)) {
     // block 2t: V from this tile, K of block 2t+1 from this tile
-    phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b);
+    phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b, mk_e);
     // tile t+1 has landed for every wave, and no wave still reads K of tile t or V of
-    // tile t-1
-    if (t + 1 < n_tiles) wait_vmem();
+    // tile t-1.  The wait is unconditional (after the last tile only mask loads are in
+    // flight) so that the compiler sees every earlier load complete on every path.
+    wait_vmem();
     __syncthreads();
     if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
     // block 2t+1: V from this tile, K of block 2t+2 from the next tile
-    phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a);
+    phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a, mk_o);
   };
 
   if (n_tiles > t0) {

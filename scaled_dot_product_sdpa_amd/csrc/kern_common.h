@@ -104,6 +104,12 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
+// Wait until this wave's LDS reads have returned their data (lgkmcnt 0; vmcnt and expcnt
+// fields at their maxima, i.e. no wait on those).
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
 
 // XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded).
 // gfx950 LDS has 64 four-byte banks (measured: a conflict-free pattern reads ~245 B/clk per

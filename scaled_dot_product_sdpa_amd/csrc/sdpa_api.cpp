@@ -131,11 +131,11 @@ sdpa::Problem make_problem(const sdpa_problem* p, const void* mask, const int32_
   k.off_kv = off_kv;
   k.mask = mask;
   // 16-byte mask vectors need every (b, h, i) row start 16-byte aligned and whole 8-key
-  // chunks per row
+  // chunks per row; the copies to LDS address 64 rows from one base with 32-bit offsets
   k.mask_vec = mask != nullptr && p->dtype == SDPA_DTYPE_BF16 && aligned16(mask) &&
                p->Lk % 8 == 0 &&
                (p->B == 1 || k.m_sb % 8 == 0) && (p->Hq == 1 || k.m_sh % 8 == 0) &&
-               (p->Lq == 1 || k.m_si % 8 == 0);
+               (p->Lq == 1 || k.m_si % 8 == 0) && k.m_si < (int64_t(1) << 24);
   return k;
 }
 
