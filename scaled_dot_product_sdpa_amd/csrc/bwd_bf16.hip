@@ -239,10 +239,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
 #pragma unroll
   for (int i = 0; i < 4; ++i) { pd_a[i] = bf16x8{}; pd_b[i] = bf16x8{}; }
   // MFMA j of a block's dV, dK: dV half 0, dK half 0, dV half 1, dK half 1, NT d-blocks each
+  OpOffsets<D> ofs;  // operand reads (A operands of row qr, transposed dO and Q)
+  ofs.init(qr, hi, arow, tchunk, thalf);
   auto tr_op = [&](int j, const bf16* Qt, const bf16* Gt, int kb) {
     const int half = j / (2 * NT), which = (j / NT) % 2, mb = j % NT;
-    const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
-    return tile_tr8<D>(which ? Qt : Gt, tr, tchunk + 4 * mb, thalf);
+    return ofs.tr8(which ? Qt : Gt, kb * 32 + 8 * half, mb);  // rows kb*32 + 16hi + 8half + arow ..
   };
   auto dvdk_mfma = [&](int j, bf16x8 op, const bf16x8 (&pd)[4]) {
     const int half = j / (2 * NT), which = (j / NT) % 2, mb = j % NT;
@@ -327,7 +328,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
       if (j + TPRE < R1) top[j + TPRE] = tr_op(j + TPRE, Qp, Gp, kbp);
       if (j >= R1 - APRE) {  // the first A operands of block bi+1
         const int i = j - (R1 - APRE);
-        aop[i] = tile_row8<D>((i & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (i >> 1) + hi);
+        aop[i] = ofs.row8((i & 1) ? Gn : Qn, kbn * 32, i >> 1);
       }
       if ((j * E1) % 4 == 0 && j * E1 / 4 + 1 < 4) {
         l4[j * E1 / 4 + 1] = lr[j * E1 / 4 + 1];
@@ -351,7 +352,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
     for (int i = 0; i < R2; ++i) {
       if (i + APRE < R2) {
         const int n = i + APRE;
-        aop[n] = tile_row8<D>((n & 1) ? Gn : Qn, kbn * 32 + qr, 2 * (n >> 1) + hi);
+        aop[n] = ofs.row8((n & 1) ? Gn : Qn, kbn * 32, n >> 1);
       }
       if (i & 1) dp_nx = mfma32(aop[i], vreg[i >> 1], dp_nx);
       else s_nx = mfma32(aop[i], kreg[i >> 1], s_nx);
@@ -379,6 +380,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   auto step = [&](int t, const bf16* Qp, const bf16* Gp, const bf16* Qc, const bf16* Gc,
                   const float* Rc, const bf16* Mc, const bf16* Qn, const bf16* Gn, bf16* Ql,
                   bf16* Gl, float* Rl, bf16* Ml) __attribute__((always_inline)) {
+    ofs.repin();
     phase(2 * t, Qp, Gp, 1, Qc, Gc, Rc, Mc, 0, Qc, Gc, 1, s_a, dp_a, s_b, dp_b, pd_b, pd_a);
     if (t + 1 < total) wait_vmem();
     __syncthreads();
@@ -394,7 +396,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
     __syncthreads();  // every wave's share of tile 0 has landed; the zeros are visible
 #pragma unroll
     for (int i = 0; i < R2; ++i) {
-      const bf16x8 op = tile_row8<D>((i & 1) ? G0 : Q0, qr, 2 * (i >> 1) + hi);
+      const bf16x8 op = ofs.row8((i & 1) ? G0 : Q0, 0, i >> 1);
       if (i & 1) dp_a = mfma32(op, vreg[i >> 1], dp_a);
       else s_a = mfma32(op, kreg[i >> 1], s_a);
     }
@@ -564,10 +566,11 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   // block), A operand K^T read from the block's tile just in time.
   bf16x8 ds_a[2], ds_b[2];
   ds_a[0] = ds_a[1] = ds_b[0] = ds_b[1] = bf16x8{};
+  OpOffsets<D> ofs;  // operand reads (A operands of row krow_l, transposed K)
+  ofs.init(krow_l, hi, arow, tchunk, thalf);
   auto kt_op = [&](int j, const bf16* Kt, int kb) {
     const int half = j / NT, mb = j % NT;
-    const int tr = kb * 32 + 16 * hi + 8 * half + arow;  // rows tr .. tr + 7
-    return tile_tr8<D>(Kt, tr, tchunk + 4 * mb, thalf);
+    return ofs.tr8(Kt, kb * 32 + 8 * half, mb);  // rows kb*32 + 16hi + 8half + arow ..
   };
   auto dq_mfma = [&](int j, bf16x8 op, const bf16x8 (&ds)[2]) {
     const int half = j / NT, mb = j % NT;
@@ -644,7 +647,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
 #pragma unroll
       for (int e = (j - 2) * E1; e < (j - 1) * E1; ++e)
         if (e >= 0) st_c(e);
-      if (j == R1 - 1) aop[0] = tile_row8<D>(Kn, kbn * 32 + krow_l, hi);  // first A operand of bi+1
+      if (j == R1 - 1) aop[0] = ofs.row8(Kn, kbn * 32, 0);  // first A operand of bi+1
       __builtin_amdgcn_sched_barrier(0);
     }
     // region 2
@@ -654,7 +657,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     for (int i = 0; i < R2; ++i) {
       if (i + 1 < R2) {
         const int n = i + 1;
-        aop[n] = tile_row8<D>((n & 1) ? Vn : Kn, kbn * 32 + krow_l, 2 * (n >> 1) + hi);
+        aop[n] = ofs.row8((n & 1) ? Vn : Kn, kbn * 32, n >> 1);
       }
       if (i & 1) dp_nx = mfma32(aop[i], doreg[i >> 1], dp_nx);
       else s_nx = mfma32(aop[i], qreg[i >> 1], s_nx);
@@ -676,6 +679,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   f32x16 s_a = f32x16{}, dp_a = f32x16{}, s_b = f32x16{}, dp_b = f32x16{};
   auto step = [&](int t, const bf16* Kp, const bf16* Kc, const bf16* Vc, const bf16* Kn,
                   const bf16* Vn, bf16* Kl, bf16* Vl) __attribute__((always_inline)) {
+    ofs.repin();
     phase(2 * t, Kp, 1, Kc, Vc, 1, s_a, dp_a, s_b, dp_b, ds_b, ds_a, mk_e);
     // tile t+1 has landed for every wave, and no wave still reads tile t-1 (unconditional,
     // so that the compiler sees every earlier load complete on every path)
@@ -693,7 +697,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     if (nvis > 2 * t0) {
 #pragma unroll
       for (int i = 0; i < R2; ++i) {
-        const bf16x8 op = tile_row8<D>((i & 1) ? V0 : K0, krow_l, 2 * (i >> 1) + hi);
+        const bf16x8 op = ofs.row8((i & 1) ? V0 : K0, 0, i >> 1);
         if (i & 1) dp_a = mfma32(op, doreg[i >> 1], dp_a);
         else s_a = mfma32(op, qreg[i >> 1], s_a);
       }
@@ -833,36 +837,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
-  // This lane's LDS element offsets inside a tile, computed once and hidden from the
-  // compiler (pin): a read then adds its buffer and block row as a constant in the
-  // instruction's offset field.  Otherwise the compiler keeps a separate loop-invariant
-  // address per buffer and read, more registers than the kernel has, and spills them.
-  // A operands (tile_row8 of row krow_l at logical chunk 2kk + hi; row block kb adds 32 D):
-  int aoff[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    aoff[kk] = krow_l * D + (((2 * kk + hi) ^ swz<D>(krow_l)) * 8);
-    pin(aoff[kk]);
-  }
-  // transposed operands (tile_tr8 of rows tr0 .. tr0 + 7, tr0 = 16 hi + arow, at logical
-  // chunk tchunk + 4 mb; row block kb and half add 32 D kb + 8 D half, which leave the
-  // swizzle unchanged):
-  int toff[D / 32][2];
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
-    const int tr0 = 16 * hi + arow, c = tchunk + 4 * mb;
-    toff[mb][0] = tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf;
-    toff[mb][1] = (tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf;
-    pin(toff[mb][0]);
-    pin(toff[mb][1]);
-  }
-  auto a_op = [&](const bf16* T, int kb, int kk) {
-    return *reinterpret_cast<const bf16x8*>(T + kb * 32 * D + aoff[kk]);
-  };
-  auto t_op = [&](const bf16* T, int kb, int half, int mb) {
-    const bf16* base = T + (kb * 32 + 8 * half) * D;
-    return join_tr(lds_read_tr4(base + toff[mb][0]), lds_read_tr4(base + toff[mb][1]));
-  };
+  OpOffsets<D> ofs;  // operand reads (A operands of row krow_l, transposed K)
+  ofs.init(krow_l, hi, arow, tchunk, thalf);
 
   // ---- mask staging (MASK and 16-byte mask rows).  Only this wave reads its rows, so it
   // fills its own regions without a barrier: the mask of block kb of tile t+1 is copied
@@ -904,14 +880,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   auto step = [&](int t, const bf16* Kt, const bf16* Vt, bf16* Kn, bf16* Vn)
                   __attribute__((always_inline)) {
     const int j0 = t * kBN;
-    // re-pinned every step, so that no buffer's addresses are hoisted out of the loop
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) pin(aoff[kk]);
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-      pin(toff[mb][0]);
-      pin(toff[mb][1]);
-    }
+    ofs.repin();
     wait_tile();
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(j0 + kBN, Kn, Vn);
@@ -930,11 +899,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
       {
         bf16x8 op[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) op[kk] = a_op(Kt, kb, kk);
+        for (int kk = 0; kk < D / 16; ++kk) op[kk] = ofs.row8(Kt, kb * 32, kk);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) s_acc = mfma32(op[kk], qreg[kk], s_acc);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) op[kk] = a_op(Vt, kb, kk);
+        for (int kk = 0; kk < D / 16; ++kk) op[kk] = ofs.row8(Vt, kb * 32, kk);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) dp_acc = mfma32(op[kk], doreg[kk], dp_acc);
       }
@@ -986,7 +955,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
       for (int half = 0; half < 2; ++half) {
         bf16x8 kT[D / 32];
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) kT[mb] = t_op(Kt, kb, half, mb);
+        for (int mb = 0; mb < D / 32; ++mb) kT[mb] = ofs.tr8(Kt, kb * 32 + 8 * half, mb);
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) dq_acc[mb] = mfma32(kT[mb], dsb[half], dq_acc[mb]);
       }

@@ -111,6 +111,17 @@ __device__ __forceinline__ void wait_lds() {
   asm volatile("" ::: "memory");
 }
 
+// Keeps a register value where it is: the empty asm reads and rewrites it, so the arithmetic
+// that produces the value cannot be moved below this point.  Without it the compiler sinks a
+// block's softmax arithmetic across the branches between pipeline phases, next to the MFMAs
+// that consume it, where it runs as one stretch of vector work with the matrix unit idle
+// instead of in the MFMA slots it was written into.  The value is also opaque to the
+// optimizer from here on (see OpOffsets).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // XOR swizzle of the 16-byte chunks inside an LDS tile row (tiles are stored unpadded).
 // gfx950 LDS has 64 four-byte banks (measured: a conflict-free pattern reads ~245 B/clk per
 // CU), i.e. sixteen 16-byte bank groups per 256 bytes.  Tiles are read two ways:
@@ -156,6 +167,50 @@ __device__ __forceinline__ bf16x8 tile_tr8(const bf16* tile, int tr, int c, int 
   return join_tr(lds_read_tr4(tile + o0), lds_read_tr4(tile + o1));
 }
 
+// A wave's operand reads of swizzled D-wide tiles by per-lane element offsets that are
+// computed once and hidden from the compiler (pin): every read then adds its buffer and
+// row block as a constant in the LDS instruction's offset field.  Without this the compiler
+// keeps one loop-invariant address per buffer and read (tens of registers in the kernels
+// with three tile buffers) and spills them.  Call repin() once per loop step, so that no
+// buffer's addresses are hoisted out of the loop.  The row offsets the reads add (multiples
+// of 8 rows) leave the swizzle unchanged, as it depends only on row bits 0..2 and 4.
+template <int D>
+struct OpOffsets {
+  int a[D / 16];     // tile_row8 of row `row` at logical chunk 2 kk + hi
+  int t[D / 32][2];  // tile_tr8 of rows tr0 = 16 hi + arow and tr0 + 4 at chunk tchunk + 4 mb
+  __device__ __forceinline__ void init(int row, int hi, int arow, int tchunk, int thalf) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) a[kk] = row * D + (((2 * kk + hi) ^ swz<D>(row)) * 8);
+    const int tr0 = 16 * hi + arow;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      const int c = tchunk + 4 * mb;
+      t[mb][0] = tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf;
+      t[mb][1] = (tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf;
+    }
+    repin();
+  }
+  __device__ __forceinline__ void repin() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) pin(a[kk]);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      pin(t[mb][0]);
+      pin(t[mb][1]);
+    }
+  }
+  // row `row` + r0 (r0 a multiple of 32), logical chunk 2 kk + hi
+  __device__ __forceinline__ bf16x8 row8(const bf16* tile, int r0, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + r0 * D + a[kk]);
+  }
+  // transposed operand of rows r0 + tr0 .. r0 + tr0 + 7 (r0 a multiple of 8, bit 3 or 5
+  // only), chunk tchunk + 4 mb
+  __device__ __forceinline__ bf16x8 tr8(const bf16* tile, int r0, int mb) const {
+    const bf16* base = tile + r0 * D;
+    return join_tr(lds_read_tr4(base + t[mb][0]), lds_read_tr4(base + t[mb][1]));
+  }
+};
+
 // One transposing read (four bf16) of row r, logical chunk c, 4-element half h of a tile.
 template <int D, int SW>
 __device__ __forceinline__ i16x4 tile_tr4(const bf16* tile, int r, int c, int h) {
@@ -179,15 +234,6 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
-// Keeps a register value where it is: the empty asm reads and rewrites it, so the arithmetic
-// that produces the value cannot be moved below this point.  Without it the compiler sinks a
-// block's softmax arithmetic across the branches between pipeline phases, next to the MFMAs
-// that consume it, where it runs as one stretch of vector work with the matrix unit idle
-// instead of in the MFMA slots it was written into.
-template <typename T>
-__device__ __forceinline__ void pin(T& x) {
-  asm volatile("" : "+v"(x));
-}
 
 // Buffer resource over `bytes` bytes at `base` for loads into registers (reads past the end
 // return zeros); the compiler tracks these loads like any other and inserts the wait before
