@@ -100,8 +100,49 @@ def run(scale: float = 1.0) -> str:
                         ("–" if tf is None else f"{100 * tf / PEAK_BF16_TFLOPS:.1f}") + " | " +
                         ("–" if lds is None else f"{lds:.1f}") + " | " +
                         ("–" if per_clk is None else f"{per_clk:.0f}") + " |")
+    rows += ["", atomics(scale)]
+    return "\n".join(rows)
+
+
+def atomics(scale: float = 1.0) -> str:
+    """fp32 accumulation into global memory (csrc/ceilings.hip, probe 6): atomic adds
+    without return against plain stores of the same addresses, over a buffer that fits the
+    L2 of one XCD (4 MiB) and one that does not (128 MiB)."""
+    import torch
+    lib = ctypes.CDLL(str(CEIL_LIB))
+    lib.ceil_atomic_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_atomic_probe.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows = ["| fp32 accumulation | buffer | workgroups | us per launch | G updates/s | GB/s |",
+            "|---|---:|---:|---:|---:|---:|"]
+    for n in (1 << 20, 1 << 25):
+        buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+        for mode, what in ((0, "atomic add (no return)"), (1, "plain store")):
+            for blocks in (512, 2048):
+                it = max(1, int(200 * scale))
+
+                def launch():
+                    rc = lib.ceil_atomic_probe(mode, ctypes.c_void_p(buf.data_ptr()), n, it, blocks, stream)
+                    if rc != 0:
+                        raise RuntimeError(f"atomic probe: status {rc}")
+
+                launch()  # warm-up
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(REPS):
+                    launch()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / REPS
+                ups = blocks * 256 * it / (us * 1e-6)
+                rows.append(f"| {what} | {n * 4 >> 20} MiB | {blocks} | {us:.1f} | {ups / 1e9:.0f} | {ups * 4 / 1e9:.0f} |")
+        del buf
     return "\n".join(rows)
 
 
 if __name__ == "__main__":
-    print(run(float(sys.argv[1]) if len(sys.argv) > 1 else 1.0))
+    if len(sys.argv) > 1 and sys.argv[1] == "atomics":
+        print(atomics(float(sys.argv[2]) if len(sys.argv) > 2 else 1.0))
+    else:
+        print(run(float(sys.argv[1]) if len(sys.argv) > 1 else 1.0))

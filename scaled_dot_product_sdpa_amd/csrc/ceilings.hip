@@ -222,6 +222,23 @@ __global__ __launch_bounds__(256, WPS) void ceil_clock(float* out, int iters) {
   }
 }
 
+// 6. fp32 accumulation into global memory, as a key-stationary backward would add its dQ
+// partials: thread t of the grid updates element (i * threads + t) & mask in iteration i
+// (mask + 1 = buffer length, a power of two), so each wave instruction covers 256
+// contiguous bytes and the grid sweeps the whole buffer every (mask + 1) / threads
+// iterations.  MODE 0: atomic add without return (global_atomic_add_f32); MODE 1: plain
+// store of the same addresses, for comparison.
+template <int MODE>
+__global__ __launch_bounds__(256) void ceil_atomic(float* buf, int64_t mask, int iters) {
+  const int64_t threads = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int i = 0; i < iters; ++i) {
+    float* p = buf + (((int64_t)i * threads + t) & mask);
+    if constexpr (MODE == 0) unsafeAtomicAdd(p, 1.0f);
+    else *p = (float)i;
+  }
+}
+
 template <typename K>
 hipError_t launch(K kern, int wps, float* out, int iters, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(256 * wps), dim3(256), 0, s, out, iters);
@@ -245,6 +262,17 @@ extern "C" int ceil_probe_agpr(int id, int wps, float* out, int iters, void* str
   }
 }
 #else
+// Runs the accumulation probe (ceil_atomic) with `blocks` workgroups of 256 threads over
+// buf[0 .. n), n a power of two.
+extern "C" int ceil_atomic_probe(int mode, float* buf, int64_t n, int iters, int blocks, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (n <= 0 || (n & (n - 1)) != 0 || blocks <= 0 || iters < 0) return -1;
+  if (mode == 0) hipLaunchKernelGGL(ceil_atomic<0>, dim3(blocks), dim3(256), 0, s, buf, n - 1, iters);
+  else if (mode == 1) hipLaunchKernelGGL(ceil_atomic<1>, dim3(blocks), dim3(256), 0, s, buf, n - 1, iters);
+  else return -2;
+  return (int)hipGetLastError();
+}
+
 // Runs probe `id` (see the table in ceilings.py) on a grid of 256 * wps workgroups of 256
 // threads (one per CU and wps resident per CU); out holds 65536 * wps floats.
 extern "C" int ceil_probe_agpr(int id, int wps, float* out, int iters, void* stream);

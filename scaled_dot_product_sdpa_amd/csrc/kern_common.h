@@ -176,17 +176,18 @@ __device__ __forceinline__ bf16x8 tile_tr8(const bf16* tile, int tr, int c, int 
 // of 8 rows) leave the swizzle unchanged, as it depends only on row bits 0..2 and 4.
 template <int D>
 struct OpOffsets {
+  // byte offsets (the reads add them to byte addresses, so no shift is needed per read)
   int a[D / 16];     // tile_row8 of row `row` at logical chunk 2 kk + hi
   int t[D / 32][2];  // tile_tr8 of rows tr0 = 16 hi + arow and tr0 + 4 at chunk tchunk + 4 mb
   __device__ __forceinline__ void init(int row, int hi, int arow, int tchunk, int thalf) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) a[kk] = row * D + (((2 * kk + hi) ^ swz<D>(row)) * 8);
+    for (int kk = 0; kk < D / 16; ++kk) a[kk] = 2 * (row * D + (((2 * kk + hi) ^ swz<D>(row)) * 8));
     const int tr0 = 16 * hi + arow;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       const int c = tchunk + 4 * mb;
-      t[mb][0] = tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf;
-      t[mb][1] = (tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf;
+      t[mb][0] = 2 * (tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf);
+      t[mb][1] = 2 * ((tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf);
     }
     repin();
   }
@@ -201,13 +202,14 @@ struct OpOffsets {
   }
   // row `row` + r0 (r0 a multiple of 32), logical chunk 2 kk + hi
   __device__ __forceinline__ bf16x8 row8(const bf16* tile, int r0, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(tile + r0 * D + a[kk]);
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + r0 * D) + a[kk]);
   }
   // transposed operand of rows r0 + tr0 .. r0 + tr0 + 7 (r0 a multiple of 8, bit 3 or 5
   // only), chunk tchunk + 4 mb
   __device__ __forceinline__ bf16x8 tr8(const bf16* tile, int r0, int mb) const {
-    const bf16* base = tile + r0 * D;
-    return join_tr(lds_read_tr4(base + t[mb][0]), lds_read_tr4(base + t[mb][1]));
+    const char* base = reinterpret_cast<const char*>(tile + r0 * D);
+    return join_tr(lds_read_tr4(reinterpret_cast<const bf16*>(base + t[mb][0])),
+                   lds_read_tr4(reinterpret_cast<const bf16*>(base + t[mb][1])));
   }
 };
 
