@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   if (row < nrows && c == 0) {
     a.dsum[row] = acc;
     const float l = valid ? a.lse[row] : kNegInf;
-    a.lse2[row] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+    // with a mask the kernels subtract LSE in natural units (see dkdv_body)
+    a.lse2[row] = (l == kNegInf) ? __builtin_inff() : (a.p.mask ? l : l * kLog2e);
   }
 }
 
@@ -227,6 +228,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   for (int mb = 0; mb < NT; ++mb) { dk_acc[mb] = f32x16{}; dv_acc[mb] = f32x16{}; }
 
   const float c2 = p.scale_log2;
+  const float sc = p.scale;
   const int qr = perm_row(l32);  // Q / dO row read by this lane (A operands of S, dP)
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
@@ -276,14 +278,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
     if (MASK) {
       if (p.mask_vec) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mbias[v] = bf2f(Mc[(kb * 32 + 16 * hi + v) * KT + wave * 32 + l32]) * kLog2e;
+        for (int v = 0; v < 16; ++v) mbias[v] = bf2f(Mc[(kb * 32 + 16 * hi + v) * KT + wave * 32 + l32]);
       } else {
         const bf16* mrow = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int qi = r0 + 16 * hi + v;
           const bool in = qi < q_end && myk < kv_end;
-          mbias[v] = in ? bf2f(mrow[(int64_t)qi * p.m_si + myk]) * kLog2e : 0.f;
+          mbias[v] = in ? bf2f(mrow[(int64_t)qi * p.m_si + myk]) : 0.f;
         }
       }
     }
@@ -301,9 +303,12 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
     // P and dS in three stages one slot apart: A (exp2 argument, dP - D), B (exp2),
     // C (dS and the bf16 operands)
     float xv[16], dd[16];
+    // The exp2 argument.  With a mask, scale * s + m - LSE is formed in natural units (the
+    // prep kernel then stores LSE itself) and only the difference goes to log2 units: m
+    // near the bottom of the fp32 range times log2(e) would overflow.
     auto st_a = [&](int e) {
       const float l2 = l4[e / 4][e % 4];
-      xv[e] = fmaf(s[e], c2, MASK ? mbias[e] - l2 : -l2);
+      xv[e] = MASK ? (fmaf(s[e], sc, mbias[e]) - l2) * kLog2e : fmaf(s[e], c2, -l2);
       dd[e] = dp[e] - d4[e / 4][e % 4];
     };
     auto st_b = [&](int e) { xv[e] = fast_exp2(xv[e]); };
@@ -556,6 +561,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   for (int mb = 0; mb < NT; ++mb) dq_acc[mb] = f32x16{};
 
   const float c2 = p.scale_log2;
+  const float sc = p.scale;
   const int krow_l = perm_row(l32);
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
@@ -598,11 +604,11 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
       if (mask_vec_ok(bi)) {
         const bf16x8 b0 = __builtin_bit_cast(bf16x8, mk[0]), b1 = __builtin_bit_cast(bf16x8, mk[1]);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) { mbias[v] = bf2f(b0[v]) * kLog2e; mbias[v + 8] = bf2f(b1[v]) * kLog2e; }
+        for (int v = 0; v < 8; ++v) { mbias[v] = bf2f(b0[v]); mbias[v + 8] = bf2f(b1[v]); }
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) * kLog2e : 0.f;
+          mbias[v] = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) : 0.f;
       }
       load_mask(bi + 2, mk);
     }
@@ -619,7 +625,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
     }
     float xv[16], dd[16];
     auto st_a = [&](int e) {
-      xv[e] = fmaf(s[e], c2, MASK ? mbias[e] + nl2 : nl2);
+      // with a mask in natural units (nl2 then holds -LSE; see dkdv_body)
+      xv[e] = MASK ? (fmaf(s[e], sc, mbias[e]) + nl2) * kLog2e : fmaf(s[e], c2, nl2);
       dd[e] = dp[e] - dsum;
     };
     auto st_b = [&](int e) { xv[e] = fast_exp2(xv[e]); };
@@ -832,6 +839,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
     vcopy.copy(rows_rsrc<D, kBN>(vb_, p.v_sl, j0, kv_stop), Vd, wave);
   };
   const float c2 = p.scale_log2;
+  const float sc = p.scale;
   const int krow_l = perm_row(l32);
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
@@ -909,7 +917,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
       }
       // lane holds query qi and keys key0 + v
       const int key0 = key_lo + 16 * hi;
-      // with a mask, s_acc becomes the exp2 argument here (scores in log2 units less lse2)
+      // with a mask, s_acc becomes the exp2 argument here: scale * s + m - LSE in natural
+      // units (lse2 then holds LSE; see dkdv_body), converted to log2 units
       if (MASK) {
         if (mstage) {
           wait_mask(t + 1 < n_tiles);
@@ -919,8 +928,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
           const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(mr + 8 * ((2 * hi + 1) ^ sw));
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            s_acc[v] = fmaf(s_acc[v], c2, bf2f(b0[v]) * kLog2e - lse2);
-            s_acc[v + 8] = fmaf(s_acc[v + 8], c2, bf2f(b1[v]) * kLog2e - lse2);
+            s_acc[v] = (fmaf(s_acc[v], sc, bf2f(b0[v])) - lse2) * kLog2e;
+            s_acc[v + 8] = (fmaf(s_acc[v + 8], sc, bf2f(b1[v])) - lse2) * kLog2e;
           }
           // the region is refilled only after these reads have returned
           wait_lds();
@@ -929,7 +938,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float mv = (qok && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qi * p.m_si + key0 + v]) : 0.f;
-            s_acc[v] = fmaf(s_acc[v], c2, mv * kLog2e - lse2);
+            s_acc[v] = (fmaf(s_acc[v], sc, mv) - lse2) * kLog2e;
           }
         }
       }

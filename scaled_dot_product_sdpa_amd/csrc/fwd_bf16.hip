@@ -162,6 +162,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
 
   const float c2 = p.scale_log2;
+  const float sc = p.scale;
   // K operand read: row kb*32 + perm_row(l32), logical chunk 2*kk + hi
   const int krow_l = perm_row(l32);
   // V^T operand (transposing read): row key_base + arow, logical chunk vchunk, half vhalf
@@ -185,7 +186,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Scores of block bi before the max, in place in its S accumulator: raw dot products,
-  // or log2-unit scores with a mask; -inf where a block touching a boundary hides a key.
+  // or with a mask scale * s + m in natural units; -inf where a block touching a boundary
+  // hides a key.  Masked scores stay in natural units until the row max is subtracted: a
+  // mask value near the bottom of the fp32 range (say the most negative bf16) times
+  // log2(e) would overflow to -inf and turn a row masked that way into an empty one,
+  // where the definition gives equal weights.
   auto pre_scores = [&](int bi, f32x16& x, const u32x4 (&mk)[2]) {
     const int key_lo = 32 * bi;
     const int key0 = key_lo + 16 * hi;
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
           mv[v] = (qrow < q_end && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qrow * p.m_si + key0 + v]) : 0.f;
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], c2, mv[v] * kLog2e);
+      for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], sc, mv[v]);
     }
     const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo + coff) ||
                          (wq_lo + 32 > q_end) || (W > 0 && key_lo <= wq_hi + coff - W);
@@ -217,14 +222,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Row max of the block (partial maxima `mx` over the lane's scores) -> moves the
-  // reference max if some row grew past the threshold; returns the exp2 offset.
+  // reference max if some row grew past the threshold; returns the offset stage A takes
+  // off the scores.  mref is in log2 units, or in natural units with a mask.
   auto post_max = [&](float mx) {
     mx = xhalf_max(mx);
-    const float mt = MASK ? mx : mx * c2;  // block max in log2 units (c2 > 0)
-    const bool need = mt > mref + kRescaleLog2;
+    const float mt = MASK ? mx : mx * c2;  // block max (c2 > 0)
+    const bool need = mt > mref + (MASK ? kRescaleLog2 * kLn2 : kRescaleLog2);
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float mnew = need ? mt : mref;
-      const float corr = need ? fast_exp2(mref - mnew) : 1.f;
+      const float corr = need ? fast_exp2(MASK ? (mref - mnew) * kLog2e : mref - mnew) : 1.f;
       mref = mnew;
       frow *= corr;
       frow2 *= corr;
@@ -239,8 +245,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   //   A: exp2 argument;  B: exp2;  C: bf16 B operand of O^T += V^T P^T, both sums.
   auto stage_a = [&](const f32x16& x, float m_use, int pr, f32x2 (&t)[8]) {
     if (MASK) {
-      t[pr][0] = x[2 * pr] - m_use;
-      t[pr][1] = x[2 * pr + 1] - m_use;
+      t[pr][0] = (x[2 * pr] - m_use) * kLog2e;
+      t[pr][1] = (x[2 * pr + 1] - m_use) * kLog2e;
     } else {
       t[pr][0] = fmaf(x[2 * pr], c2, -m_use);
       t[pr][1] = fmaf(x[2 * pr + 1], c2, -m_use);
@@ -362,7 +368,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) pv_mfma1(j);
 
-  // ---- epilogue: O = O^T / f (0 for empty rows), LSE = ln2 * (mref + log2 f).
+  // ---- epilogue: O = O^T / f (0 for empty rows), LSE = ln2 * mref + ln f (mref + ln f with
+  // a mask).
   const float ft = xhalf_sum(frow + frow2);
   const bool rowlive = qrow < q_end && ft > 0.f;
   const float inv = rowlive ? 1.f / ft : 0.f;
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       }
     }
   }
-  if (qrow < p.Lq && lseb && hi == 0) lseb[qrow] = rowlive ? (mref * kLn2 + logf(ft)) : kNegInf;
+  if (qrow < p.Lq && lseb && hi == 0) lseb[qrow] = rowlive ? ((MASK ? mref : mref * kLn2) + logf(ft)) : kNegInf;
 }
 
 template <int D, int NW, int WPE, int CM, bool MASK>

@@ -83,7 +83,8 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;  // workspace: D = rowsum(dO o O), contiguous (B, Hq, Lq)
-  float* lse2;  // workspace: LSE * log2(e), +inf for empty rows, contiguous (B, Hq, Lq)
+  float* lse2;  // workspace: LSE * log2(e) (LSE itself with a mask), +inf for empty rows,
+                // contiguous (B, Hq, Lq)
 };
 
 struct DecodeArgs {

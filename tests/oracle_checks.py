@@ -348,6 +348,29 @@ def check_identical_keys(orc):
     assert np.abs(o - mean).max() <= 1e-12
 
 
+def check_mask_at_bf16_min(orc):
+    """A mask value at the most negative finite bf16 (what masks built from a dtype's
+    minimum carry) is a finite number, not a block: a row holding it for every key has
+    equal weights, O = mean of the values, and LSE equal to that value (ln n is below
+    its spacing); a row holding it for some keys gives those keys weight 0 and matches the
+    same row with -inf there."""
+    lo = -3.3895313892515355e38  # -(2 - 2**-7) * 2**127, the most negative finite bf16
+    c = _case(157, mask=False, Lq=4, Lk=6)
+    B, H, Lq, Lk = c["q"].shape[0], c["q"].shape[1], c["q"].shape[2], c["k"].shape[2]
+    m = np.zeros((B, 1, Lq, Lk))
+    m[:, :, 0, :] = lo
+    m[:, :, 1, ::2] = lo
+    o, lse = orc.forward(c["q"], c["k"], c["v"], mask=m)
+    mean = np.repeat(c["v"].mean(axis=2), 2, axis=1)  # (B, Hq, Dv), Hq = 2 Hkv
+    assert np.abs(o[:, :, 0] - mean).max() <= 1e-12
+    assert np.all(lse[:, :, 0] == lo)
+    m_inf = m.copy()
+    m_inf[:, :, 1, ::2] = -np.inf
+    o2, lse2 = orc.forward(c["q"], c["k"], c["v"], mask=m_inf)
+    assert np.abs(o[:, :, 1] - o2[:, :, 1]).max() <= 1e-12
+    assert np.abs(lse[:, :, 1] - lse2[:, :, 1]).max() <= 1e-12
+
+
 def check_lengths_are_masks(orc):
     """Per-batch lengths equal an additive mask with -inf at padded keys, with padded query
     rows empty (O = 0, LSE = -inf, no gradient); padded K/V contents are never read
@@ -557,7 +580,7 @@ ALL_CHECKS = [
     check_key_permutation_equivariance, check_query_independence, check_batched_equals_per_item,
     check_masked_keys, check_fully_masked_row, check_large_scores, check_default_scale,
     check_causal_is_tril, check_gqa_is_repeat_interleave, check_score_variance,
-    check_single_key, check_identical_keys, check_lengths_are_masks, check_torch_library,
+    check_single_key, check_identical_keys, check_mask_at_bf16_min, check_lengths_are_masks, check_torch_library,
     check_bottom_right_chunked_prefill, check_bottom_right_is_shifted_tril,
     check_bottom_right_torch, check_window_is_band_mask, check_window_limits,
 ]

@@ -145,3 +145,51 @@ def test_blocked_keys_get_exactly_zero_gradient(orc, D, lens):
         assert np.all(dk_r[b, :, j] == 0.0) and np.all(dv_r[b, :, j] == 0.0)
         n += 1
     assert n >= 3 * 30  # every batch has at least 30 keys past its length
+
+
+BF16_MIN = float(torch.finfo(torch.bfloat16).min)
+
+
+@pytest.mark.parametrize("D,causal", [(64, False), (128, False), (128, True)])
+def test_rows_masked_at_bf16_min_keep_equal_weights(orc, D, causal):
+    """Additive masks built from a dtype's minimum carry the most negative finite bf16, a
+    finite number: a row holding it for every key has equal weights (O = mean of the
+    visible values, LSE = that number), a row holding it for some keys gives them weight
+    0, and -inf still empties a row.  The kernels keep masked scores in natural units, where
+    the value times log2(e) would overflow to -inf.
+
+    The backward recovers P from LSE, and at that magnitude LSE absorbs ln(n): a row held
+    at the minimum for every key gets P = 1 per key there.  Its dO is zero here, as for the
+    padding rows such masks mark, which makes its gradient terms zero on both sides."""
+    B, Hq, Hkv, L = 2, 4, 2, 150
+    g = torch.Generator().manual_seed(120 + D + causal)
+    bf = lambda t: t.to(torch.bfloat16)
+    q = bf(torch.randn(B, Hq, L, D, generator=g))
+    k = bf(torch.randn(B, Hkv, L, D, generator=g))
+    v = bf(torch.randn(B, Hkv, L, D, generator=g))
+    dO = torch.randn(B, Hq, L, D, generator=g)
+    m = torch.zeros(B, 1, L, L)
+    m[torch.rand(B, 1, L, L, generator=g) < 0.05] = BF16_MIN
+    full_row, half_row, empty_row = 5, 40, 77
+    m[:, :, full_row, :] = BF16_MIN
+    m[:, :, half_row, ::2] = BF16_MIN
+    m[:, :, empty_row, :] = float("-inf")
+    dO[:, :, full_row, :] = 0.0
+    inp = dict(q=q, k=k, v=v, dO=bf(dO), mask=bf(m), len_q=None, len_kv=None,
+               scale=1.0 / np.sqrt(D), is_causal=causal, window=0)
+    banner(f"bf16-min mask rows D={D} causal={causal}")
+    d = to_dev(inp)
+    o, lse = gpu_forward(d)
+    o_ref, lse_ref = oracle_forward(orc, inp)
+    G = Hq // Hkv
+    nvis = full_row + 1 if causal else L
+    vmean = f64(v)[:, :, :nvis].mean(axis=2)  # (B, Hkv, D)
+    for h in range(Hq):
+        assert np.abs(o_ref[:, h, full_row] - vmean[:, h // G]).max() < 1e-9
+    assert np.all(f64(lse)[:, :, full_row] == BF16_MIN)
+    assert np.all(lse_ref[:, :, full_row] == BF16_MIN)
+    assert np.all(np.isneginf(lse_ref[:, :, empty_row]))
+    compare_forward(inp, o, lse, o_ref, lse_ref)
+    grads = gpu_backward(d, o, lse)
+    refs = oracle_backward(orc, inp)[:3]
+    compare_backward(inp, grads, refs, lse_ref)
