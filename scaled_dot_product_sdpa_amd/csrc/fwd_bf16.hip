@@ -59,8 +59,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // Tile t's K is read by the phases of blocks 2t-1 (the next block's scores) and 2t; its V
   // by those of blocks 2t and 2t+1.  Tile t+2 is requested after the barrier in the middle
   // of step t, so K needs two buffers (tile t's is free by then) and V three.
-  __shared__ __attribute__((aligned(16))) bf16 Kb[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Vb[3][TILE];
+  // One LDS array, V buffers first: operand reads address their buffer with a constant in
+  // the instruction's 16-bit offset field (see OpOffsets), which reaches the three V buffers
+  // and the first K buffer.
+  __shared__ __attribute__((aligned(16))) bf16 lds[5 * TILE];
+  bf16* const Vb[3] = {lds, lds + TILE, lds + 2 * TILE};
+  bf16* const Kb[2] = {lds + 3 * TILE, lds + 4 * TILE};
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -175,14 +179,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int E = 16 / NS;  // scores per lane handled in one pipeline slot
   constexpr int KPRE = 2;     // K operand reads issued ahead of their MFMA
 
-  auto read_k1 = [&](const bf16* Kt, int kb, int kk) {
-    return tile_row8<D>(Kt, kb * 32 + krow_l, 2 * kk + hi);
-  };
+  OpOffsets<D> ofs;  // K operands (row krow_l) and transposed V operands
+  ofs.init(krow_l, hi, arow, vchunk, vhalf);
+  auto read_k1 = [&](const bf16* Kt, int kb, int kk) { return ofs.row8(Kt, kb * 32, kk); };
   // V^T operand i (half i / (D/32), d-block i % (D/32)) of the block at rows kb*32..
   auto read_v1 = [&](const bf16* Vt, int kb, int i) {
     const int half = i / (D / 32), mb = i % (D / 32);
-    const int vr = kb * 32 + 16 * hi + 8 * half + arow;  // rows vr .. vr + 7
-    return tile_tr8<D>(Vt, vr, vchunk + 4 * mb, vhalf);
+    return ofs.tr8(Vt, kb * 32 + 8 * half, mb);  // rows kb*32 + 16 hi + 8 half + arow ..
   };
 
   // Scores of block bi before the max, in place in its S accumulator: raw dot products,
@@ -339,6 +342,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // that every buffer index is a compile-time constant.
   auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl)
                   __attribute__((always_inline)) {
+    ofs.repin();
     // block 2t: V from this tile, K of block 2t+1 from this tile
     phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b, mk_e);
     // tile t+1 has landed for every wave, and no wave still reads K of tile t or V of
