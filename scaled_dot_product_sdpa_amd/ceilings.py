@@ -100,7 +100,50 @@ def run(scale: float = 1.0) -> str:
                         ("–" if tf is None else f"{100 * tf / PEAK_BF16_TFLOPS:.1f}") + " | " +
                         ("–" if lds is None else f"{lds:.1f}") + " | " +
                         ("–" if per_clk is None else f"{per_clk:.0f}") + " |")
-    rows += ["", atomics(scale)]
+    rows += ["", atomics(scale), "", streaming()]
+    return "\n".join(rows)
+
+
+def streaming() -> str:
+    """HBM read rate in the decode kernel's access pattern (csrc/ceilings.hip, probe 7):
+    one-wave workgroups each streaming a contiguous chunk of one or two 512 MiB streams (K,
+    V) in 8 KB tiles, two tiles per stream in flight, with and without the non-temporal
+    cache policy; chunk sizes of a 768-key decode split (192 KiB per stream) and of long
+    streams (2 MiB)."""
+    import torch
+    lib = ctypes.CDLL(str(CEIL_LIB))
+    lib.ceil_stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ceil_stream_probe.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sb = 512 << 20
+    buf = torch.ones(2 * sb // 4, dtype=torch.float32, device="cuda")
+    rows = ["| HBM streaming read | streams | chunk per stream | cache policy | us per launch | TB/s | % of 8 TB/s |",
+            "|---|---:|---:|---|---:|---:|---:|"]
+    for nstr in (1, 2):
+        for chunk in (192 << 10, 2 << 20):
+            n = sb // chunk * chunk  # whole chunks per stream
+            out = torch.empty(n // chunk * 64, dtype=torch.float32, device="cuda")
+            for nt in (1, 0):
+                def launch():
+                    rc = lib.ceil_stream_probe(nstr, nt, ctypes.c_void_p(buf.data_ptr()), n, chunk,
+                                               ctypes.c_void_p(out.data_ptr()), stream)
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe: status {rc}")
+
+                launch()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(REPS):
+                    launch()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / REPS
+                tbs = nstr * n / (us * 1e-6) / 1e12
+                rows.append(f"| one wave per chunk, 2 x 8 KB tiles in flight per stream | {nstr} | "
+                            f"{chunk >> 10} KiB | {'non-temporal' if nt else 'default'} | {us:.1f} | "
+                            f"{tbs:.2f} | {100 * tbs / 8.0:.1f} |")
+    del buf
     return "\n".join(rows)
 
 
@@ -144,5 +187,7 @@ def atomics(scale: float = 1.0) -> str:
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "atomics":
         print(atomics(float(sys.argv[2]) if len(sys.argv) > 2 else 1.0))
+    elif len(sys.argv) > 1 and sys.argv[1] == "streaming":
+        print(streaming())
     else:
         print(run(float(sys.argv[1]) if len(sys.argv) > 1 else 1.0))

@@ -239,6 +239,46 @@ __global__ __launch_bounds__(256) void ceil_atomic(float* buf, int64_t mask, int
   }
 }
 
+// 7. HBM streaming reads in the decode kernel's pattern: one-wave workgroups, two per SIMD,
+// each reading its own contiguous chunk of every one of NSTR streams (K and V) in 8 KB
+// tiles, 16 bytes per lane per load, two tiles of each stream in flight in registers
+// (buffer loads with cache policy AUX).  Loads past a chunk return zeros without touching
+// memory.  The loaded words are folded into one value per lane so no load is dead.
+template <int NSTR, int AUX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void ceil_stream(const char* buf, int64_t stream_bytes, int chunk, float* out) {
+  constexpr int TILE = 8192, LD = TILE / 1024;
+  const int lane = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  reg_rsrc_t r[NSTR];
+#pragma unroll
+  for (int st = 0; st < NSTR; ++st) r[st] = reg_rsrc(buf + st * stream_bytes + base, chunk);
+  const int ntiles = chunk / TILE;
+  u32x4 x[2][NSTR][LD];
+  auto load = [&](int t, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < NSTR; ++st)
+#pragma unroll
+      for (int i = 0; i < LD; ++i) x[set][st][i] = reg_ld16<AUX>(r[st], (uint32_t)(t * TILE + i * 1024 + lane * 16), 0);
+  };
+  u32x4 acc = zero16();
+  auto fold = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < NSTR; ++st)
+#pragma unroll
+      for (int i = 0; i < LD; ++i) acc ^= x[set][st][i];
+  };
+  load(0, 0);
+  load(1, 1);
+  for (int t = 0; t < ntiles; t += 2) {
+    fold(0);
+    load(t + 2, 0);
+    fold(1);
+    load(t + 3, 1);
+  }
+  out[(int64_t)blockIdx.x * 64 + lane] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
 template <typename K>
 hipError_t launch(K kern, int wps, float* out, int iters, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(256 * wps), dim3(256), 0, s, out, iters);
@@ -262,6 +302,23 @@ extern "C" int ceil_probe_agpr(int id, int wps, float* out, int iters, void* str
   }
 }
 #else
+// Runs the streaming probe (ceil_stream): nstr streams of stream_bytes each at buf, one
+// workgroup per chunk (stream_bytes / chunk of them, chunk a multiple of 16 KB); out holds
+// 64 floats per workgroup.  nt: non-temporal cache policy (as the decode kernel's loads).
+extern "C" int ceil_stream_probe(int nstr, int nt, const void* buf, int64_t stream_bytes, int chunk,
+                                 float* out, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (chunk <= 0 || chunk % 16384 != 0 || stream_bytes % chunk != 0) return -1;
+  const int64_t grid = stream_bytes / chunk;
+  const char* b = reinterpret_cast<const char*>(buf);
+  if (nstr == 1 && nt) hipLaunchKernelGGL((ceil_stream<1, 2>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else if (nstr == 1) hipLaunchKernelGGL((ceil_stream<1, 0>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else if (nstr == 2 && nt) hipLaunchKernelGGL((ceil_stream<2, 2>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else if (nstr == 2) hipLaunchKernelGGL((ceil_stream<2, 0>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else return -2;
+  return (int)hipGetLastError();
+}
+
 // Runs the accumulation probe (ceil_atomic) with `blocks` workgroups of 256 threads over
 // buf[0 .. n), n a power of two.
 extern "C" int ceil_atomic_probe(int mode, float* buf, int64_t n, int iters, int blocks, void* stream) {
