@@ -289,6 +289,12 @@ def cpu_model() -> str:
 # ---- profile helpers (no GPU): turn rocprofv3 output into the committed summaries ----
 
 COPY_KERNELS = ("__amd_rocclr_copyBuffer", "copy_kernel")
+# The decode kernels read the KV cache with non-temporal buffer loads, which the counters
+# see differently from the copy's loads; their counters are scaled by what the same counter
+# reads for the HBM streaming probe (ceilings.hip) in that load form over a known size.
+STREAM_CAL_KERNEL = "ceil_stream"
+STREAM_CAL_BYTES = 2 * (256 << 20)  # two 256 MiB streams
+STREAM_CAL_STAGES = ("decode_split",)
 CALIBRATION_BYTES = 1 << 30  # the --calibrate device copy: 1 GiB read and 1 GiB written
 
 
@@ -327,21 +333,31 @@ def write_traffic(fetch_dir, write_dir, command, workload):
             raise SystemExit(f"no calibration copy kernel in {d}")
         scale = CALIBRATION_BYTES / (max(cal) * 1024.0)
         out[counter.lower() + "_scale"] = round(scale, 4)
+        cal_nt = [v for n, v in rows if STREAM_CAL_KERNEL in n]
+        scale_nt = None
+        if cal_nt and counter == "FETCH_SIZE":
+            scale_nt = STREAM_CAL_BYTES / (max(cal_nt) * 1024.0)
+            out["fetch_size_scale_nontemporal"] = round(scale_nt, 4)
         for stage, frag in KERNEL_NAMES.items():
             vals = [v for n, v in rows if frag in n and "sdpa::" in n]
             if vals:
-                per.setdefault(stage, {})[counter] = (sum(vals) / len(vals), len(vals), scale)
+                sc = scale_nt if (scale_nt and stage in STREAM_CAL_STAGES) else scale
+                per.setdefault(stage, {})[counter] = (sum(vals) / len(vals), len(vals), sc, scale)
     for stage, c in per.items():
         if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
             continue
-        (fk, fn, fs), (wk, wn, ws) = c["FETCH_SIZE"], c["WRITE_SIZE"]
+        (fk, fn, fs, fcopy), (wk, wn, ws, _) = c["FETCH_SIZE"], c["WRITE_SIZE"]
         out[stage] = {"kernel": KERNEL_NAMES[stage], "source_hash": source_hash(stage),
                       "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
                       "dispatches": min(fn, wn),
                       "bytes_per_launch": int(fk * 1024 * fs + wk * 1024 * ws)}
+        if fs != fcopy:
+            out[stage]["bytes_per_launch_copy_scale"] = int(fk * 1024 * fcopy + wk * 1024 * ws)
     data[workload] = out
     data["note"] = {"text": "per workload: HBM bytes per launch = counter KiB * 1024 * scale, scale = "
-                            "known bytes of the calibration copy / its counter bytes"}
+                            "known bytes of the calibration copy / its counter bytes; the decode split "
+                            "kernel's FETCH_SIZE takes the scale of the streaming probe in its load form "
+                            "(non-temporal buffer loads) instead"}
     path.write_text(json.dumps(data, indent=1) + "\n")
     print(json.dumps(out, indent=1))
 
@@ -486,6 +502,25 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        # reads of a known size in the decode kernel's load form (see STREAM_CAL_KERNEL)
+        import ctypes
+        from scaled_dot_product_sdpa_amd.build import CEIL_LIB
+        if CEIL_LIB.exists():
+            lib = ctypes.CDLL(str(CEIL_LIB))
+            lib.ceil_stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            lib.ceil_stream_probe.restype = ctypes.c_int
+            half = STREAM_CAL_BYTES // 2
+            buf = torch.zeros(STREAM_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+            chunk = 256 << 10
+            res = torch.empty(half // chunk * 64, dtype=torch.float32, device="cuda")
+            rc = lib.ceil_stream_probe(2, 1, ctypes.c_void_p(buf.data_ptr()), half, chunk,
+                                       ctypes.c_void_p(res.data_ptr()),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise SystemExit(f"bench.py: streaming calibration probe failed ({rc})")
+            torch.cuda.synchronize()
+            del buf, res
         torch.cuda.empty_cache()
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
