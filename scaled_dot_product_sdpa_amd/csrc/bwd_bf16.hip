@@ -452,9 +452,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kBN = 64;
 
-// LDS bytes of the pipelined dQ body: three K and three V tiles.
+// LDS bytes of the pipelined dQ body: three K and two V tiles.  The phase of block bi
+// computes S and dP of block bi+1 and dQ of block bi-1, so K of tile t is read by the phases
+// of blocks 2t-1 .. 2t+2 and V of tile t by those of blocks 2t-1 and 2t.  Tile t+2 is
+// requested after the barrier that follows the phase of block 2t: it takes the K buffer of
+// tile t-1 (last read in that phase) and the V buffer of tile t.
 template <int D>
-constexpr int dq_lds_bytes() { return 6 * kBN * D * 2; }
+constexpr int dq_lds_bytes() { return 5 * kBN * D * 2; }
 
 template <int D, int NW, int CM, bool MASK>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, char* smem) {
@@ -471,8 +475,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   bf16* const K2 = K1 + TILE;
   bf16* const V0 = K2 + TILE;
   bf16* const V1 = V0 + TILE;
-  bf16* const V2 = V1 + TILE;
-  static_assert(6 * TILE * 2 == dq_lds_bytes<D>(), "LDS layout");
+  static_assert(5 * TILE * 2 == dq_lds_bytes<D>(), "LDS layout");
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -710,10 +713,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
       }
     }
   }
-  for (int t = t0; t < n_tiles; t += 3) {
-    step(t, K2, K0, V0, K1, V1, K2, V2);
-    if (t + 1 < n_tiles) step(t + 1, K0, K1, V1, K2, V2, K0, V0);
-    if (t + 2 < n_tiles) step(t + 2, K1, K2, V2, K0, V0, K1, V1);
+  // unrolled by six (three K and two V buffers), so every buffer is a compile-time choice
+  bf16* const Kb[3] = {K0, K1, K2};
+  bf16* const Vb[2] = {V0, V1};
+  for (int tl = 0; tl < n_tiles - t0; tl += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u)
+      if (tl + u < n_tiles - t0)
+        step(t0 + tl + u, Kb[(u + 2) % 3], Kb[u % 3], Vb[u % 2], Kb[(u + 1) % 3], Vb[(u + 1) % 2],
+             Kb[(u + 2) % 3], Vb[u % 2]);
   }
   // a wave whose last block is the workgroup's last: that block's dQ (second block of
   // tile n_tiles-1, buffer (n_tiles-1-t0) % 3, never overwritten)
@@ -1005,10 +1013,18 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
 // waves per SIMD; the workgroups' barriers are independent), measured faster than one
 // 8-wave workgroup on the MHA 1k and padded 2k workloads and equal on GQA 4k.
 template <int D> struct BwdShape;
-// PIPE_DQ: the software-pipelined dQ kernel fits two waves per SIMD (D = 64); at D = 128
-// its registers do not, and the block-sequential form is faster.
-template <> struct BwdShape<64> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = true; };
-template <> struct BwdShape<128> { static constexpr int KV_NW = 4; static constexpr int Q_NW = 4; static constexpr bool PIPE_DQ = false; };
+// PIPE_DQ / PIPE_DQ_MASK: dQ runs the software-pipelined kernel (else the block-sequential
+// one) without / with a mask; it needs two waves per SIMD, which its registers allow except
+// with a mask at D = 128.  FUSE: dK/dV and dQ in one launch (bwd_fused_kernel), whose
+// bodies fit two waves per SIMD only at D = 64.
+template <> struct BwdShape<64> {
+  static constexpr int KV_NW = 4, Q_NW = 4;
+  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = true, FUSE = true;
+};
+template <> struct BwdShape<128> {
+  static constexpr int KV_NW = 4, Q_NW = 4;
+  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = false, FUSE = false;
+};
 
 template <int D, int CM, bool MASK>
 hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
@@ -1016,7 +1032,7 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   const int n_kt = (a.p.Lk + 32 * KNW - 1) / (32 * KNW);
   constexpr int BM = 32 * QNW;
   const int n_qt = (a.p.Lq + BM - 1) / BM;
-  if constexpr (BwdShape<D>::PIPE_DQ && KNW == QNW && !MASK) {
+  if constexpr (BwdShape<D>::FUSE && KNW == QNW && !MASK) {
     // both passes in one launch (see bwd_fused_kernel)
     if ((stages & kBwdDkdv) && (stages & kBwdDq)) {
       const int n_dkdv = n_kt * a.p.B * a.p.Hkv, n_dq = n_qt * a.p.B * a.p.Hq;
@@ -1033,7 +1049,7 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & kBwdDq) && n_qt > 0) {
-    if constexpr (BwdShape<D>::PIPE_DQ)
+    if constexpr (MASK ? BwdShape<D>::PIPE_DQ_MASK : BwdShape<D>::PIPE_DQ)
       hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CM, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
                          dim3(64 * QNW), 0, s, a);
     else
