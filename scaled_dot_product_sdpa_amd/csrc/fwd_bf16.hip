@@ -112,6 +112,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   int vis_stop = wq_lo < q_end ? kv_stop : 0;
   if (CAUSAL) vis_stop = min(vis_stop, wq_hi + 1 + coff);
   const int nvis = vis_stop > 0 ? (vis_stop + 31) / 32 : 0;
+  // The fewest blocks any wave of the workgroup works on (wave 0's on a causal diagonal; 0
+  // if a wave's rows all lie past the length): tiles before t_full are whole for every wave.
+  int vis_min = row_lo + 32 * (NW - 1) < q_end ? kv_stop : 0;
+  if (CAUSAL) vis_min = min(vis_min, min(row_lo + 32, q_end) + coff);
+  const int t_full = min(vis_min > 0 ? (vis_min + 31) / 32 / 2 : 0, n_tiles);
 
   // ---- K/V tiles: HBM -> LDS (rows past kv_stop arrive as zeros).
   TileCopy<kBN, D, NW> kcopy, vcopy;
@@ -332,19 +337,24 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int pr = i * P; pr < (i + 1) * P; ++pr) stage_c(pr, t, pv_p);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // this block's P stays computed inside this phase (see pin)
+    pin(pv_p[0]);
+    pin(pv_p[1]);
   };
+  // `whole`: every wave works on this block (no per-wave test, so the phases join without
+  // the register copies a conditional phase costs).
   auto phase = [&](int bi, const bf16* Vt, int kb, const bf16* Kn, int kbn, f32x16& sacc,
-                   f32x16& snext, u32x4 (&mk)[2]) __attribute__((always_inline)) {
-    if (bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext, mk);
+                   f32x16& snext, u32x4 (&mk)[2], bool whole) __attribute__((always_inline)) {
+    if (whole || bi < nvis) body(bi, Vt, kb, Kn, kbn, sacc, snext, mk);
   };
 
   // One tile step; the loop below is unrolled by six (two K buffers, three V buffers) so
   // that every buffer index is a compile-time constant.
-  auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl)
-                  __attribute__((always_inline)) {
+  auto step = [&](int t, const bf16* Kc, const bf16* Vc, const bf16* Kn, bf16* Kl, bf16* Vl,
+                  bool whole) __attribute__((always_inline)) {
     ofs.repin();
     // block 2t: V from this tile, K of block 2t+1 from this tile
-    phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b, mk_e);
+    phase(2 * t, Vc, 0, Kc, 1, sacc_a, sacc_b, mk_e, whole);
     // tile t+1 has landed for every wave, and no wave still reads K of tile t or V of
     // tile t-1.  The wait is unconditional (after the last tile only mask loads are in
     // flight) so that the compiler sees every earlier load complete on every path.
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
     if (t + 2 < n_tiles) load_tile((t + 2) * kBN, Kl, Vl);
     // block 2t+1: V from this tile, K of block 2t+2 from the next tile
-    phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a, mk_o);
+    phase(2 * t + 1, Vc, 1, Kn, 0, sacc_b, sacc_a, mk_o, whole);
   };
 
   if (n_tiles > t0) {
@@ -362,11 +372,20 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int kk = 0; kk < NS; ++kk) sacc_a = mfma32(read_k1(Kb[0], 0, kk), qreg[kk], sacc_a);
     }
   }
-  for (int tl = 0; tl < n_tiles - t0; tl += 6) {
+  // whole groups of six tiles that every wave works on whole, then the rest (the diagonal
+  // and the lengths) with a per-wave test of each block.  With a mask the second copy of the
+  // loop costs more registers than two waves per SIMD leave, so it runs the tested loop only.
+  const int tl_main = !MASK && t_full > t0 ? (t_full - t0) / 6 * 6 : 0;
+  for (int tl = 0; tl < tl_main; tl += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u)
+      step(t0 + tl + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3], true);
+  }
+  for (int tl = tl_main; tl < n_tiles - t0; tl += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u)
       if (tl + u < n_tiles - t0)
-        step(t0 + tl + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3]);
+        step(t0 + tl + u, Kb[u % 2], Vb[u % 3], Kb[(u + 1) % 2], Kb[u % 2], Vb[(u + 2) % 3], false);
   }
   // the last block's PV
 #pragma unroll
