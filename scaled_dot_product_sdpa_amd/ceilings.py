@@ -143,6 +143,29 @@ def streaming() -> str:
                 rows.append(f"| one wave per chunk, 2 x 8 KB tiles in flight per stream | {nstr} | "
                             f"{chunk >> 10} KiB | {'non-temporal' if nt else 'default'} | {us:.1f} | "
                             f"{tbs:.2f} | {100 * tbs / 8.0:.1f} |")
+    # at the decode kernel's two workgroups per SIMD: two, then three tiles per stream in
+    # flight (non-temporal)
+    chunk = 192 << 10
+    n = sb // chunk * chunk
+    out = torch.empty(n // chunk * 64, dtype=torch.float32, device="cuda")
+    for code, tif in ((4, 2), (3, 3)):
+        def launch():
+            rc = lib.ceil_stream_probe(2, code, ctypes.c_void_p(buf.data_ptr()), n, chunk,
+                                       ctypes.c_void_p(out.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"stream probe: status {rc}")
+
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(REPS):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / REPS
+        tbs = 2 * n / (us * 1e-6) / 1e12
+        rows.append(f"| one wave per chunk, {tif} x 8 KB tiles in flight per stream, two workgroups per SIMD "
+                    f"| 2 | {chunk >> 10} KiB | non-temporal | {us:.1f} | {tbs:.2f} | {100 * tbs / 8.0:.1f} |")
     del buf
     return "\n".join(rows)
 

@@ -244,17 +244,25 @@ __global__ __launch_bounds__(256) void ceil_atomic(float* buf, int64_t mask, int
 // tiles, 16 bytes per lane per load, two tiles of each stream in flight in registers
 // (buffer loads with cache policy AUX).  Loads past a chunk return zeros without touching
 // memory.  The loaded words are folded into one value per lane so no load is dead.
-template <int NSTR, int AUX>
+// PIN2: hold 20 KB of LDS per workgroup, so that at most two run per SIMD (as the decode
+// kernel's registers allow); otherwise the registers set the occupancy.
+template <int NSTR, int AUX, int TIF = 2, bool PIN2 = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void ceil_stream(const char* buf, int64_t stream_bytes, int chunk, float* out) {
   constexpr int TILE = 8192, LD = TILE / 1024;
   const int lane = threadIdx.x;
+  __shared__ float pad[PIN2 ? 5120 : 1];
+  if (chunk < 0) {  // never true: keeps the allocation
+    pad[lane] = 0.f;
+    __syncthreads();
+    out[lane] = pad[lane ^ 1];
+  }
   const int64_t base = (int64_t)blockIdx.x * chunk;
   reg_rsrc_t r[NSTR];
 #pragma unroll
   for (int st = 0; st < NSTR; ++st) r[st] = reg_rsrc(buf + st * stream_bytes + base, chunk);
   const int ntiles = chunk / TILE;
-  u32x4 x[2][NSTR][LD];
+  u32x4 x[TIF][NSTR][LD];
   auto load = [&](int t, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < NSTR; ++st)
@@ -268,13 +276,14 @@ void ceil_stream(const char* buf, int64_t stream_bytes, int chunk, float* out) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) acc ^= x[set][st][i];
   };
-  load(0, 0);
-  load(1, 1);
-  for (int t = 0; t < ntiles; t += 2) {
-    fold(0);
-    load(t + 2, 0);
-    fold(1);
-    load(t + 3, 1);
+#pragma unroll
+  for (int k = 0; k < TIF; ++k) load(k, k);
+  for (int t = 0; t < ntiles; t += TIF) {
+#pragma unroll
+    for (int k = 0; k < TIF; ++k) {
+      fold(k);
+      load(t + TIF + k, k);
+    }
   }
   out[(int64_t)blockIdx.x * 64 + lane] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
@@ -304,14 +313,19 @@ extern "C" int ceil_probe_agpr(int id, int wps, float* out, int iters, void* str
 #else
 // Runs the streaming probe (ceil_stream): nstr streams of stream_bytes each at buf, one
 // workgroup per chunk (stream_bytes / chunk of them, chunk a multiple of 16 KB); out holds
-// 64 floats per workgroup.  nt: non-temporal cache policy (as the decode kernel's loads).
+// 64 floats per workgroup.  nt: non-temporal cache policy (as the decode kernel's loads);
+// with two streams and the non-temporal policy, nt = 4 holds two workgroups per SIMD (two
+// tiles per stream in flight, the decode kernel's occupancy) and nt = 3 also keeps three
+// tiles per stream in flight.
 extern "C" int ceil_stream_probe(int nstr, int nt, const void* buf, int64_t stream_bytes, int chunk,
                                  float* out, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (chunk <= 0 || chunk % 16384 != 0 || stream_bytes % chunk != 0) return -1;
   const int64_t grid = stream_bytes / chunk;
   const char* b = reinterpret_cast<const char*>(buf);
-  if (nstr == 1 && nt) hipLaunchKernelGGL((ceil_stream<1, 2>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  if (nstr == 2 && nt == 3) hipLaunchKernelGGL((ceil_stream<2, 2, 3, true>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else if (nstr == 2 && nt == 4) hipLaunchKernelGGL((ceil_stream<2, 2, 2, true>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
+  else if (nstr == 1 && nt) hipLaunchKernelGGL((ceil_stream<1, 2>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
   else if (nstr == 1) hipLaunchKernelGGL((ceil_stream<1, 0>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
   else if (nstr == 2 && nt) hipLaunchKernelGGL((ceil_stream<2, 2>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
   else if (nstr == 2) hipLaunchKernelGGL((ceil_stream<2, 0>), dim3(grid), dim3(64), 0, s, b, stream_bytes, chunk, out);
