@@ -137,7 +137,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   // (causal) queries and are launched first.
   int bg, kt;
   xcd_item(bid, p.B * p.Hkv, nblk / (p.B * p.Hkv), 1, !CAUSAL, bg, kt);
-  const int b = bg / p.Hkv;
+  const int b = batch_by_work(p, bg / p.Hkv);
   const int g = bg % p.Hkv;
   const int q_end = seq_len_q(p, b);
   const int kv_end = seq_len_kv(p, b);
@@ -487,7 +487,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   // Work item: (batch, KV head) group, then query tile `rank` of head h of the group.
   int gi, r;
   xcd_item(bid, p.B * p.Hkv, nblk / (p.B * p.Hkv), p.G, !CAUSAL, gi, r);
-  const int b = gi / p.Hkv;
+  const int b = batch_by_work(p, gi / p.Hkv);
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   // Work item: (batch, KV head) group, then query tile `rank` of head h of the group.
   int gi, r;
   xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
-  const int b = gi / p.Hkv;
+  const int b = batch_by_work(p, gi / p.Hkv);
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // (the G heads of one rank adjacent in launch order).
   int gi, r;
   xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
-  const int b = gi / p.Hkv;
+  const int b = batch_by_work(p, gi / p.Hkv);
   const int g = gi % p.Hkv;
   const int h = g * p.G + r % p.G;
   const int rank = r / p.G;

@@ -56,6 +56,25 @@ __device__ __forceinline__ int64_t v_base(const Problem& p, int b) {
   return p.off_kv ? (int64_t)p.off_kv[b] * p.v_sl : (int64_t)b * p.v_sb;
 }
 
+// The batch of rank k when batches are ordered by work, heaviest first (len_q * len_kv, ties
+// by index), so that a grid dealt in group order starts the long sequences first and the
+// short ones fill the tail; k itself without per-batch lengths or with more than 64
+// batches.  Every lane of the calling wave must be active: lane j reads batch j's lengths.
+__device__ __forceinline__ int batch_by_work(const Problem& p, int k) {
+  if ((!p.len_q && !p.len_kv && !p.off_q && !p.off_kv) || p.B > 64) return k;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = lane < p.B ? (int64_t)seq_len_q(p, lane) * seq_len_kv(p, lane) : -1;
+  int rank = 0;
+  for (int j = 0; j < p.B; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)w, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)w >> 32), j);
+    const int64_t wj = (int64_t)(((uint64_t)hi << 32) | lo);
+    rank += (wj > w || (wj == w && j < lane)) ? 1 : 0;
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(lane < p.B && rank == k);
+  return m ? (int)__builtin_ctzll(m) : k;
+}
+
 // Output rows (o, dq; dk, dv) a batch writes: every row up to the padded length (zeros past
 // the valid length), but only the valid rows of a ragged batch: the rows after them belong
 // to the next batch or to a gap the caller owns.
