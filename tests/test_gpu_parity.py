@@ -82,6 +82,16 @@ CASES = {
                                                     len_range=(1, 3000), window=1000, seed=57),
     "decode_window_d64": W["gqa_decode_8k"].scaled(B=3, Hq=4, Hkv=4, Lk=900, D=64, causal=2,
                                                    len_range=(30, 900), window=50, seed=58),
+    # long enough that the forward without a mask runs key tiles that every wave sees whole
+    # as its straight-line loop (groups of six 64-key tiles) before the per-block tested
+    # rest: causal with lengths, a long cross-attention, and a window on the bottom-right
+    # diagonal (the straight-line loop then starts at the window's first tile)
+    "long_causal_lens_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=900, Lk=900, lens="qkv",
+                                                       len_range=(500, 900), seed=60),
+    "long_cross_d64": W["mha_causal_1k"].scaled(B=1, Hq=2, Hkv=2, Lq=150, Lk=1000, causal=False,
+                                                seed=61),
+    "long_window_br_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=600, Lk=1300, causal=2,
+                                                     window=900, seed=62),
 }
 
 
