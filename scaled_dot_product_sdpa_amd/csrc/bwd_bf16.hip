@@ -22,6 +22,9 @@
 //            with dO^T and Q^T read from LDS by ds_read_b64_tr_b16.  Inside a wave the
 //            blocks are software-pipelined: the dV, dK MFMAs of block b-1 run with the P, dS
 //            arithmetic of block b, and the S, dP MFMAs of block b+1 with the rest of it.
+//            At D = 128 without a mask each 32-key slice is split over a pair of waves
+//            (S, P, dV in one; dP, dS, dK in the other, P handed over through LDS), which
+//            fits two waves per SIMD where one wave holding both needs ~320 registers.
 //  3. dq:    query-stationary (the forward's decomposition, 4 waves of 32 rows).  Per
 //            32-key block of a 64-key K/V tile (three LDS buffers, buffer-load copies):
 //              S^T = K Q^T,  P^T,  dP^T = V dO^T,  dS^T = P^T o (dP^T - D),
@@ -445,6 +448,326 @@ template <int D, int NW, int CM, bool MASK>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<D, NW, MASK>()];
   dkdv_body<D, NW, CM, MASK>(a, blockIdx.x, gridDim.x, smem);
+}
+
+// ---------------------------------------------------------------------------------------
+// 2b. dK, dV with each 32-key slice worked by a pair of waves
+// ---------------------------------------------------------------------------------------
+// Same decomposition and grid as the dK/dV body (a workgroup owns 32 * NP keys of one
+// (batch, KV head) and walks the group's query tiles through three LDS buffers), but each
+// 32-key slice is split over two waves by the products it feeds:
+//   wave w < NP ("P wave"):   S = Q K^T,  P = exp2(S * scale * log2e - lse2),  dV^T += dO^T P
+//   wave w + NP ("dS wave"):  dP = dO V^T,  dS = P o (dP - D),                  dK^T += Q^T dS
+// The P wave hands P (fp32, in its own accumulator layout: lane = key, 16 query rows) to
+// its partner through LDS, one barrier per 32-row block.  Each wave then holds one operand
+// (K or V) and one accumulator (dV^T or dK^T) instead of both, which fits two waves per SIMD
+// (the single-wave form needs ~320 registers); the two waves of a SIMD are one P wave and
+// one dS wave, so the exponentials of one run under the other's MFMAs.  dS is formed from
+// the same fp32 P and dP as in the single-wave body, so both give the same results.
+//
+// Phase k (between barriers k-1 and k) runs the S, P (or dP) of block k and the dV (or dK)
+// of block k-1; the dS wave forms dS of block k-1 from the P its partner stored in phase
+// k-1.  Block k is rows (k % 2) * 32 of tile k / 2.  Tile t+2 is copied into the buffer of
+// tile t-1 after barrier 2t (the last phase reading tile t-1 is 2t) and must have landed by
+// barrier 2t+3.
+template <int D, int NP>
+constexpr int dkdv_pair_lds_bytes() {
+  return 3 * (2 * kQT * D * 2 + 2 * kQT * 4) + 2 * NP * 64 * 16 * 4;
+}
+
+template <bool V> struct Role { static constexpr bool value = V; };
+
+// The waves of one role (PW: P waves, else dS waves).
+template <bool PW, int D, int NP, int CM>
+__device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nblk, char* smem) {
+  constexpr bool CAUSAL = CM != 0;
+  constexpr int NW = 2 * NP;
+  constexpr int KT = 32 * NP;    // keys per workgroup
+  constexpr int TILE = kQT * D;
+  constexpr int NS = D / 16;     // MFMAs of one S (or dP) block
+  constexpr int NT = D / 32;     // d-blocks of dV (or dK)
+  constexpr int NM = NS + 2 * NT;  // MFMAs of one phase
+  constexpr int PRE = 3;         // LDS operand reads issued ahead of their MFMA
+  bf16* const Q0 = reinterpret_cast<bf16*>(smem);
+  bf16* const Q1 = Q0 + TILE;
+  bf16* const Q2 = Q1 + TILE;
+  bf16* const G0 = Q2 + TILE;  // dO
+  bf16* const G1 = G0 + TILE;
+  bf16* const G2 = G1 + TILE;
+  float* const R0 = reinterpret_cast<float*>(G2 + TILE);  // lse2 rows, then D rows
+  float* const R1s = R0 + 2 * kQT;
+  float* const R2s = R1s + 2 * kQT;
+  char* const Pex = reinterpret_cast<char*>(R2s + 2 * kQT);  // [2][NP][64 lanes x 16 fp32]
+  static_assert(6 * TILE * 2 + 6 * kQT * 4 + 2 * NP * 4096 == dkdv_pair_lds_bytes<D, NP>(), "LDS layout");
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int pair = wave % NP;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bg, kt;
+  xcd_item(bid, p.B * p.Hkv, nblk / (p.B * p.Hkv), 1, !CAUSAL, bg, kt);
+  const int b = batch_by_work(p, bg / p.Hkv);
+  const int g = bg % p.Hkv;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
+  const int j0 = kt * KT;
+  const int jw = j0 + pair * 32;  // the pair's first key
+  const int myk = jw + l32;       // this lane's key
+
+  const int kstop = min(kv_end, j0 + KT);
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;
+  const int qt_begin = CAUSAL ? max(j0 - coff, 0) / kQT : 0;
+  const int W = CM == 2 ? p.window : 0;
+  const int q_last = W > 0 ? min(q_end, max(kstop - coff + W - 1, 0)) : q_end;
+  const int qt_end = (j0 < kstop) ? (q_last + kQT - 1) / kQT : 0;
+  const int n_q_tiles = qt_end > qt_begin ? qt_end - qt_begin : 0;
+  const int total = n_q_tiles * p.G;
+  // query tiles last to first, the group's heads in turn (see the dK/dV body)
+  auto tile_rows = [&](int it, int& h, int& i0) __attribute__((always_inline)) {
+    h = g * p.G + it / n_q_tiles;
+    i0 = (qt_end - 1 - it % n_q_tiles) * kQT;
+  };
+
+  // Tiles HBM -> LDS.  The row copies (lse2 by wave 0, D by wave 1) go first, so that every
+  // wave has at most four copies of a tile issued after the previous tile's.
+  TileCopy<kQT, D, NW> qcopy, gcopy;
+  qcopy.init(p.q_sl, wave, lane);
+  gcopy.init(p.o_sl, wave, lane);
+  auto load_tile = [&](int it, bf16* Qd, bf16* Gd, float* Rd) __attribute__((always_inline)) {
+    int h, i0;
+    tile_rows(it, h, i0);
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+    if (uw < 2) {
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Lq + i0;
+      const float* src = (uw ? a.dsum : a.lse2) + rb;
+      buffer_to_lds<4>(raw_rsrc(src, (int64_t)max(min(p.Lq - i0, kQT), 0) * 4), Rd, uw * kQT * 4, lane * 4);
+    }
+    const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
+    const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + o_base(p, b) + h * p.o_sh;
+    qcopy.copy(rows_rsrc<D, kQT>(qb, p.q_sl, i0, q_end), Qd, wave);
+    gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
+  };
+  static_assert(2 * TileCopy<kQT, D, NW>::PER_WAVE == 4, "copies per wave and tile");
+
+  const float c2 = p.scale_log2;
+  const int qr = perm_row(l32);
+  const int blk = lane >> 4;
+  const int arow = (lane & 15) >> 2;
+  const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
+  const int thalf = 4 * (lane & 1);
+
+  {
+    // K (P wave) or V (dS wave) of this lane's key: B operand of S or dP
+    if (total > 0) load_tile(0, Q0, G0, R0);
+    bf16x8 kv[NS];
+    {
+      const bf16* base = reinterpret_cast<const bf16*>(PW ? a.k : a.v) +
+                         (PW ? k_base(p, b) + g * p.k_sh : v_base(p, b) + g * p.v_sh);
+      const int64_t sl = PW ? p.k_sl : p.v_sl;
+      const bool ok = myk < kv_end;
+#pragma unroll
+      for (int kk = 0; kk < NS; ++kk)
+        kv[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(base + (int64_t)myk * sl + kk * 16 + 8 * hi) : zero16());
+    }
+    wait_vmem();
+    if (total > 1) load_tile(1, Q1, G1, R1s);
+
+    f32x16 acc[NT];
+#pragma unroll
+    for (int mb = 0; mb < NT; ++mb) acc[mb] = f32x16{};
+    OpOffsets<D> ofs;
+    ofs.init(qr, hi, arow, tchunk, thalf);
+
+    // One phase.  FIRST: no block k-1; LAST: no block k.  Cur/kb: tile and rows of block k;
+    // Prv/kbp: those of block k-1.  P wave: cur_bf receives bf16 P of block k, prv_bf holds
+    // that of block k-1.  dS wave: cur_dp receives dP of block k, prv_dp holds dP of block
+    // k-1.
+    auto phase = [&](auto first_t, auto last_t, int k, const bf16* Qc, const bf16* Gc, const float* Rc, int kb,
+                     const bf16* Qp, const bf16* Gp, const float* Rp, int kbp, bf16x8 (&cur_bf)[2],
+                     const bf16x8 (&prv_bf)[2], f32x16& cur_dp, f32x16& prv_dp) __attribute__((always_inline)) {
+      constexpr bool FIRST = decltype(first_t)::value, LAST = decltype(last_t)::value;
+      constexpr int n_lo = LAST ? NS : 0, n_hi = FIRST ? NS : NM;
+      // operand n: A of the S/dP MFMAs (rows of Q or dO), then the transposed A of the
+      // dV/dK MFMAs (dO^T or Q^T of block k-1)
+      auto opr = [&](int n) __attribute__((always_inline)) {
+        if (n < NS) return ofs.row8(PW ? Qc : Gc, kb * 32, n);
+        const int j = n - NS;
+        return ofs.tr8(PW ? Gp : Qp, kbp * 32 + 8 * (j / NT), j % NT);
+      };
+      bf16x8 op[NM];
+#pragma unroll
+      for (int n = n_lo; n < n_lo + PRE && n < n_hi; ++n) op[n] = opr(n);
+      f32x16 s = f32x16{};  // S (P wave) or dP (dS wave) of block k
+      char* const pex_w = Pex + ((k & 1) * NP + pair) * 4096 + lane * 16;      // block k
+      const char* const pex_r = Pex + (((k + 1) & 1) * NP + pair) * 4096 + lane * 16;  // block k-1
+      float xv[16];
+      bf16x8 ds[2];
+      f32x4 d4[4];
+      if constexpr (!PW && !FIRST) {
+        // P of block k-1 (stored by the partner before the last barrier) and D of its rows
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 pc = *reinterpret_cast<const f32x4*>(pex_r + c * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[4 * c + e] = pc[e];
+          d4[c] = reinterpret_cast<const f32x4*>(Rp + kQT + kbp * 32 + 16 * hi)[c];
+        }
+      }
+      // dS of block k-1 for the scores of slot n (E per slot), into the bf16 B operands
+      constexpr int E = 16 / NS;
+      auto ds_slot = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = n * E; e < (n + 1) * E; e += 2) {
+          xv[e] *= prv_dp[e] - d4[e / 4][e % 4];
+          xv[e + 1] *= prv_dp[e + 1] - d4[e / 4][(e + 1) % 4];
+          const f32x2 ss = {xv[e], xv[e + 1]};
+          const bf16x2 s2 = __builtin_convertvector(ss, bf16x2);
+          ds[e / 8][e % 8] = s2[0];
+          ds[e / 8][e % 8 + 1] = s2[1];
+        }
+      };
+      if constexpr (!PW && LAST) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) ds_slot(n);
+      }
+      // P of block k (P wave): lane holds key myk and query rows r0 + 16*hi + v.  The
+      // exponentials run in the dV MFMA slots once S is complete (after the loop in the
+      // first phase, which has no dV slots); each finished group of four is stored for the
+      // partner.
+      int r0 = 0;
+      f32x4 l4[4];
+      if constexpr (PW && !LAST) {
+        int h, i0;
+        tile_rows(k >> 1, h, i0);
+        (void)h;
+        r0 = i0 + kb * 32;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) l4[c] = reinterpret_cast<const f32x4*>(Rc + kb * 32 + 16 * hi)[c];
+      }
+      auto p_mask = [&]() __attribute__((always_inline)) {
+        const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 + coff < jw + 31) ||
+                             (W > 0 && jw <= r0 + 31 + coff - W);
+        if (partial) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qi = r0 + 16 * hi + v;
+            const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff) &&
+                            (W == 0 || myk > qi + coff - W);
+            s[v] = ok ? s[v] : kNegInf;
+          }
+        }
+      };
+      auto p_scores = [&](int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = e0; e < e1; e += 2) {
+          xv[e] = fast_exp2(fmaf(s[e], c2, -l4[e / 4][e % 4]));
+          xv[e + 1] = fast_exp2(fmaf(s[e + 1], c2, -l4[e / 4][(e + 1) % 4]));
+          const f32x2 pp = {xv[e], xv[e + 1]};
+          const bf16x2 p2 = __builtin_convertvector(pp, bf16x2);
+          cur_bf[e / 8][e % 8] = p2[0];
+          cur_bf[e / 8][e % 8 + 1] = p2[1];
+          if ((e + 2) % 4 == 0) {
+            const int c = e / 4;
+            *reinterpret_cast<f32x4*>(pex_w + c * 1024) = f32x4{xv[4 * c], xv[4 * c + 1], xv[4 * c + 2], xv[4 * c + 3]};
+          }
+        }
+      };
+      constexpr int E2 = 16 / (2 * NT);  // scores per dV slot
+#pragma unroll
+      for (int n = n_lo; n < n_hi; ++n) {
+        if (n + PRE < n_hi) op[n + PRE] = opr(n + PRE);
+        if (n < NS) {
+          s = mfma32(op[n], kv[n], s);
+          if constexpr (!PW && !FIRST) ds_slot(n);
+        } else {
+          const int j = n - NS;
+          acc[j % NT] = mfma32(op[n], PW ? prv_bf[j / NT] : ds[j / NT], acc[j % NT]);
+          if constexpr (PW && !LAST) {
+            if (j == 0) p_mask();
+            p_scores(j * E2, (j + 1) * E2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (!PW && !LAST) cur_dp = s;
+      if constexpr (PW && FIRST) {
+        p_mask();
+        p_scores(0, 16);
+      }
+      if constexpr (PW && !LAST) {
+        pin(cur_bf[0]);
+        pin(cur_bf[1]);
+      }
+    };
+
+    bf16x8 pa[2] = {bf16x8{}, bf16x8{}}, pb[2] = {bf16x8{}, bf16x8{}};
+    f32x16 dpa = f32x16{}, dpb = f32x16{};
+    using T = Role<true>;
+    using F = Role<false>;
+    // tile t: phase 2t (block 2t; block 2t-1 of tile t-1), barrier, copy of tile t+2 into
+    // tile t-1's buffer, phase 2t+1 (block 2t+1; block 2t), wait for tile t+1, barrier.
+    auto step = [&](auto first_t, int t, const bf16* Qp, const bf16* Gp, const float* Rp, const bf16* Qc,
+                    const bf16* Gc, const float* Rc, bf16* Ql, bf16* Gl, float* Rl) __attribute__((always_inline)) {
+      ofs.repin();
+      phase(first_t, F{}, 2 * t, Qc, Gc, Rc, 0, Qp, Gp, Rp, 1, pa, pb, dpa, dpb);
+      __syncthreads();
+      if (t + 2 < total) load_tile(t + 2, Ql, Gl, Rl);
+      phase(F{}, F{}, 2 * t + 1, Qc, Gc, Rc, 1, Qc, Gc, Rc, 0, pb, pa, dpb, dpa);
+      if (t + 2 < total) wait_vmem_le<4>();
+      else wait_vmem();
+      __syncthreads();
+    };
+    if (total > 0) {
+      __syncthreads();  // every wave's share of tile 0 has landed
+      step(T{}, 0, Q2, G2, R2s, Q0, G0, R0, Q2, G2, R2s);
+    }
+    for (int t = 1; t < total; t += 3) {
+      step(F{}, t, Q0, G0, R0, Q1, G1, R1s, Q0, G0, R0);
+      if (t + 1 < total) step(F{}, t + 1, Q1, G1, R1s, Q2, G2, R2s, Q1, G1, R1s);
+      if (t + 2 < total) step(F{}, t + 2, Q2, G2, R2s, Q0, G0, R0, Q2, G2, R2s);
+    }
+    if (total > 0) {
+      // block 2 total - 1 (rows 32.. of tile total-1)
+      const int lb = (total - 1) % 3;
+      const bf16* Ql = lb == 0 ? Q0 : (lb == 1 ? Q1 : Q2);
+      const bf16* Gl = lb == 0 ? G0 : (lb == 1 ? G1 : G2);
+      const float* Rl = lb == 0 ? R0 : (lb == 1 ? R1s : R2s);
+      phase(F{}, T{}, 2 * total, Ql, Gl, Rl, 0, Ql, Gl, Rl, 1, pa, pb, dpa, dpb);
+    }
+
+    // Epilogue: lane holds key myk, d = mb*32 + (v/4)*8 + 4*hi + v%4.
+    if (myk < kv_rows_out(p, kv_end)) {
+      bf16* row = PW ? reinterpret_cast<bf16*>(a.dv) + v_base(p, b) + g * p.v_sh + (int64_t)myk * p.v_sl
+                     : reinterpret_cast<bf16*>(a.dk) + k_base(p, b) + g * p.k_sh + (int64_t)myk * p.k_sl;
+      const float f = PW ? 1.f : p.scale;
+#pragma unroll
+      for (int mb = 0; mb < NT; ++mb) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[mb][v4 * 4 + e] * f);
+          *reinterpret_cast<bf16x4*>(row + mb * 32 + v4 * 8 + hi * 4) = w;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int NP, int CM>
+__device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int bid, int nblk, char* smem) {
+  if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < NP) dkdv_pair_wave<true, D, NP, CM>(a, bid, nblk, smem);
+  else dkdv_pair_wave<false, D, NP, CM>(a, bid, nblk, smem);
+}
+
+template <int D, int NP, int CM>
+__global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_pair_lds_bytes<D, NP>()];
+  dkdv_pair_body<D, NP, CM>(a, blockIdx.x, gridDim.x, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1017,13 +1340,15 @@ template <int D> struct BwdShape;
 // one) without / with a mask; it needs two waves per SIMD, which its registers allow except
 // with a mask at D = 128.  FUSE: dK/dV and dQ in one launch (bwd_fused_kernel), whose
 // bodies fit two waves per SIMD only at D = 64.
+// PAIR_DKDV: dK/dV without a mask runs the paired-wave kernel (two waves per 32-key slice);
+// with a mask its tiles do not fit the LDS beside the P exchange buffers.
 template <> struct BwdShape<64> {
   static constexpr int KV_NW = 4, Q_NW = 4;
-  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = true, FUSE = true;
+  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = true, FUSE = true, PAIR_DKDV = false;
 };
 template <> struct BwdShape<128> {
   static constexpr int KV_NW = 4, Q_NW = 4;
-  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = false, FUSE = false;
+  static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = false, FUSE = false, PAIR_DKDV = true;
 };
 
 template <int D, int CM, bool MASK>
@@ -1043,8 +1368,12 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
     }
   }
   if ((stages & kBwdDkdv) && n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
-                       dim3(64 * KNW), 0, s, a);
+    if constexpr (BwdShape<D>::PAIR_DKDV && !MASK)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM>), dim3(n_kt * a.p.B * a.p.Hkv), dim3(128 * KNW), 0,
+                         s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
+                         dim3(64 * KNW), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

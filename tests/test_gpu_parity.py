@@ -92,6 +92,11 @@ CASES = {
                                                 seed=61),
     "long_window_br_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=600, Lk=1300, causal=2,
                                                      window=900, seed=62),
+    # d = 128 without a diagonal or a mask (the dK/dV kernel that splits each key slice over
+    # two waves): GQA cross-attention with ragged tails, then with per-batch key lengths
+    "cross_gqa_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=333, Lk=200, causal=False, seed=63),
+    "cross_gqa_lens_d128": W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=1, Lq=150, Lk=460, causal=False,
+                                                     lens="kv", len_range=(1, 460), poison=True, seed=64),
 }
 
 
