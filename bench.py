@@ -39,7 +39,7 @@ EXTRA = ["mha_causal_1k", "padded_mask_2k", "gqa_decode_8k", "tiny_fp32", "gqa_s
 
 # kernel-name fragments (as rocprofv3 reports them) of each launch stage
 KERNEL_NAMES = {
-    "fwd": "fwd_bf16_kernel", "prep": "bwd_prep_kernel", "dkdv": "bwd_dkdv_kernel",
+    "fwd": "fwd_bf16_kernel", "prep": "bwd_prep_kernel", "dkdv": "bwd_dkdv_",
     "dq": "bwd_dq_", "main": "bwd_fused_kernel", "decode_split": "decode_split_kernel",
     "decode_combine": "decode_combine_kernel",
 }
@@ -266,8 +266,11 @@ def roofline(name, w, res):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(name, dom)
     kname = KERNEL_NAMES[dom]
-    if dom == "dq":  # the pipelined dQ kernel at d = 64, the block-sequential one at d = 128
-        kname = "bwd_dq_kernel" if w.D == 64 else "bwd_dq_seq_kernel"
+    masked = w.mask != "none"
+    if dom == "dq":  # the block-sequential dQ kernel runs only at d = 128 with a mask
+        kname = "bwd_dq_seq_kernel" if (w.D == 128 and masked) else "bwd_dq_kernel"
+    if dom == "dkdv":  # at d = 128 without a mask each key slice is split over two waves
+        kname = "bwd_dkdv_pair_kernel" if (w.D == 128 and not masked) else "bwd_dkdv_kernel"
     if w.dtype == "f32":  # the fp32 path's kernels (main: its dK/dV and dQ kernels)
         kname = {"fwd": "fwd_f32_kernel", "prep": "bwd_prep_f32_kernel", "dkdv": "bwd_dkdv_f32_kernel",
                  "dq": "bwd_dq_f32_kernel"}.get(dom, kname)
@@ -311,11 +314,12 @@ def _pmc_rows(directory, counter):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, command, workload):
+def write_traffic(fetch_dir, write_dir, command, workload, l2_dir=None):
     """profiles/traffic.json, entry `workload`: HBM bytes per launch of each of its kernels,
     from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch) of a bench command that
     runs that workload alone, each counter scaled by what it reads for the --calibrate copy
-    of known size."""
+    of known size; with l2_dir (a TCC_HIT_sum, TCC_MISS_sum run of the same command) also
+    each kernel's L2 hit rate, hits / (hits + misses) over its dispatches."""
     path = ROOT / "profiles" / "traffic.json"
     data = {}
     if path.exists():
@@ -353,6 +357,14 @@ def write_traffic(fetch_dir, write_dir, command, workload):
                       "bytes_per_launch": int(fk * 1024 * fs + wk * 1024 * ws)}
         if fs != fcopy:
             out[stage]["bytes_per_launch_copy_scale"] = int(fk * 1024 * fcopy + wk * 1024 * ws)
+    if l2_dir:
+        out["l2_command"] = command.replace("FETCH_SIZE", "TCC_HIT_sum TCC_MISS_sum")
+        hits, misses = _pmc_rows(l2_dir, "TCC_HIT_sum"), _pmc_rows(l2_dir, "TCC_MISS_sum")
+        for stage, frag in KERNEL_NAMES.items():
+            h = sum(v for n, v in hits if frag in n and "sdpa::" in n)
+            m = sum(v for n, v in misses if frag in n and "sdpa::" in n)
+            if stage in out and h + m > 0:
+                out[stage]["l2_hit_pct"] = round(100.0 * h / (h + m), 1)
     data[workload] = out
     data["note"] = {"text": "per workload: HBM bytes per launch = counter KiB * 1024 * scale, scale = "
                             "known bytes of the calibration copy / its counter bytes; the decode split "
@@ -466,6 +478,8 @@ def main():
                     help="first run one 1 GiB device copy (the reference for HBM counters)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND", "WORKLOAD"),
                     help="add WORKLOAD to profiles/traffic.json from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--l2-dir", default=None,
+                    help="with --write-traffic: a TCC_HIT_sum TCC_MISS_sum --pmc run of the same command")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv (no GPU)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "OUT_MD", "COMMAND"),
@@ -475,7 +489,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, l2_dir=args.l2_dir)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
