@@ -40,6 +40,8 @@ PROBES = {
     12: ("MFMA + 4 (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
     13: ("MFMA + 4 v_fma_f32 + (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
     14: ("MFMA + 5 v_fma_f32 + (v_exp_f32, v_sub_f32) per MFMA", 8, 0),
+    18: ("probe 13's work per 16 MFMAs in their second half only: 8 + 0, then 8 x (8 v_fma_f32 + 2 (v_exp_f32, v_sub_f32))", 16, 0),
+    19: ("the same as a forward phase spreads it: 8 x 1 v_fma_f32, then 8 x (7 v_fma_f32 + 2 (v_exp_f32, v_sub_f32))", 16, 0),
 }
 SKELETON = {4, 5, 6, 7, 15, 16}
 # probes whose registers do not fit two waves per SIMD
@@ -53,7 +55,9 @@ def _iters(pid, scale):
     return max(1, int(ITERS[kind] * scale))
 
 
-def run(scale: float = 1.0) -> str:
+def run(scale: float = 1.0, ids=None) -> str:
+    """The MFMA / LDS / mix table (only the probes in `ids` if given, then without the
+    atomics and streaming tables)."""
     import torch
     lib = ctypes.CDLL(str(CEIL_LIB))
     lib.ceil_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
@@ -77,6 +81,8 @@ def run(scale: float = 1.0) -> str:
             "| probe | waves / SIMD | us per launch | MFMA TFLOP/s | % of bf16 peak | LDS TB/s | LDS B/clk/CU |",
             "|---|---:|---:|---:|---:|---:|---:|"]
     for pid, (name, mf, lds_bytes) in PROBES.items():
+        if ids is not None and pid not in ids:
+            continue
         for wps in (1, 2):
             if wps == 2 and pid in ONE_WAVE_ONLY:
                 continue
@@ -100,7 +106,8 @@ def run(scale: float = 1.0) -> str:
                         ("–" if tf is None else f"{100 * tf / PEAK_BF16_TFLOPS:.1f}") + " | " +
                         ("–" if lds is None else f"{lds:.1f}") + " | " +
                         ("–" if per_clk is None else f"{per_clk:.0f}") + " |")
-    rows += ["", atomics(scale), "", streaming()]
+    if ids is None:
+        rows += ["", atomics(scale), "", streaming()]
     return "\n".join(rows)
 
 
@@ -212,5 +219,7 @@ if __name__ == "__main__":
         print(atomics(float(sys.argv[2]) if len(sys.argv) > 2 else 1.0))
     elif len(sys.argv) > 1 and sys.argv[1] == "streaming":
         print(streaming())
+    elif len(sys.argv) > 1 and sys.argv[1] == "mix":
+        print(run(1.0, ids={8, 9, 10, 11, 12, 13, 14, 18, 19}))
     else:
         print(run(float(sys.argv[1]) if len(sys.argv) > 1 else 1.0))

@@ -196,6 +196,38 @@ __global__ __launch_bounds__(256, WPS) void ceil_mfma_valu(float* out, int iters
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// 4b. The same vector work unevenly spread: per 16 MFMAs (two accumulation chains),
+// slots 0..7 carry NF0 v_fma_f32 and NE0 v_exp_f32 each and slots 8..15 NF1 and NE1, as a
+// two-region pipeline phase does (one region of MFMAs with little vector work, one with the
+// exponentials).
+template <int WPS, int NF0, int NE0, int NF1, int NE1>
+__global__ __launch_bounds__(256, WPS) void ceil_mfma_valu2(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  const bf16x8 a = lane_bf16x8(lane, 5), b = lane_bf16x8(lane, 6);
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  float r[8], e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { r[j] = 0.01f * (lane + j); e[j] = -0.001f * j; }
+  const float m = 0.999f, c = 1e-4f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u & 1) acc1 = mfma32(a, b, acc1);
+      else acc0 = mfma32(a, b, acc0);
+      const int nf = u < 8 ? NF0 : NF1, ne = u < 8 ? NE0 : NE1;
+#pragma unroll
+      for (int f = 0; f < (u < 8 ? NF0 : NF1); ++f) r[(u * nf + f) % 8] = fmaf(r[(u * nf + f) % 8], m, c);
+#pragma unroll
+      for (int x = 0; x < (u < 8 ? NE0 : NE1); ++x) e[(u * ne + x) % 8] = fast_exp2(e[(u * ne + x) % 8]) - 1.f;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float s = fold16(acc0) + fold16(acc1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += r[j] + e[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // 5. Clock: four MFMA chains per wave as in probe 1; thread 0 of workgroup 0 records the
 // shader-clock cycles (s_memtime) and the constant-rate wall ticks (s_memrealtime,
 // 100 MHz) across its loop, as out[0] and out[1].
@@ -369,6 +401,12 @@ extern "C" int ceil_probe(int id, int wps, float* out, int iters, void* stream) 
     case 15:
     case 16: return ceil_probe_agpr(id, wps, out, iters, stream);
     case 17: return wps == 1 ? launch(ceil_clock<1>, 1, out, iters, s) : launch(ceil_clock<2>, 2, out, iters, s);
+    case 18:
+      return wps == 1 ? launch(ceil_mfma_valu2<1, 0, 0, 8, 2>, 1, out, iters, s)
+                      : launch(ceil_mfma_valu2<2, 0, 0, 8, 2>, 2, out, iters, s);
+    case 19:
+      return wps == 1 ? launch(ceil_mfma_valu2<1, 1, 0, 7, 2>, 1, out, iters, s)
+                      : launch(ceil_mfma_valu2<2, 1, 0, 7, 2>, 2, out, iters, s);
     default: return -2;
   }
 }
