@@ -503,7 +503,7 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   const Problem& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int pair = wave % NP;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -579,8 +579,13 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
     f32x16 acc[NT];
 #pragma unroll
     for (int mb = 0; mb < NT; ++mb) acc[mb] = f32x16{};
+    // The dO tiles follow the three Q tiles; the operand offsets of the dO reads (transposed
+    // in the P wave, rows in the dS wave) carry the Q tiles' bytes and the reads go through
+    // dO pointers moved back by as much, so every read's buffer lies within its 16-bit
+    // offset field.
+    constexpr int GB = 3 * TILE;
     OpOffsets<D> ofs;
-    ofs.init(qr, hi, arow, tchunk, thalf);
+    ofs.init(qr, hi, arow, tchunk, thalf, PW ? 0 : GB * 2, PW ? GB * 2 : 0);
 
     // One phase.  FIRST: no block k-1; LAST: no block k.  Cur/kb: tile and rows of block k;
     // Prv/kbp: those of block k-1.  P wave: cur_bf receives bf16 P of block k, prv_bf holds
@@ -594,9 +599,9 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
       // operand n: A of the S/dP MFMAs (rows of Q or dO), then the transposed A of the
       // dV/dK MFMAs (dO^T or Q^T of block k-1)
       auto opr = [&](int n) __attribute__((always_inline)) {
-        if (n < NS) return ofs.row8(PW ? Qc : Gc, kb * 32, n);
+        if (n < NS) return ofs.row8(PW ? Qc : Gc - GB, kb * 32, n);
         const int j = n - NS;
-        return ofs.tr8(PW ? Gp : Qp, kbp * 32 + 8 * (j / NT), j % NT);
+        return ofs.tr8(PW ? Gp - GB : Qp, kbp * 32 + 8 * (j / NT), j % NT);
       };
       bf16x8 op[NM];
 #pragma unroll

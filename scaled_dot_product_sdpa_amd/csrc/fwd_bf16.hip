@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const Problem& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
 
@@ -184,9 +184,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int E = 16 / NS;  // scores per lane handled in one pipeline slot
   constexpr int KPRE = 2;     // K operand reads issued ahead of their MFMA
 
-  OpOffsets<D> ofs;  // K operands (row krow_l) and transposed V operands
-  ofs.init(krow_l, hi, arow, vchunk, vhalf);
-  auto read_k1 = [&](const bf16* Kt, int kb, int kk) { return ofs.row8(Kt, kb * 32, kk); };
+  // K operands (row krow_l) and transposed V operands.  The K rows are read through tile
+  // pointers moved back by the three V buffers (their offsets carry those bytes instead), so
+  // that both K buffers lie within the read's 16-bit offset field and a read needs no add.
+  OpOffsets<D> ofs;
+  ofs.init(krow_l, hi, arow, vchunk, vhalf, 3 * TILE * 2);
+  auto read_k1 = [&](const bf16* Kt, int kb, int kk) { return ofs.row8(Kt - 3 * TILE, kb * 32, kk); };
   // V^T operand i (half i / (D/32), d-block i % (D/32)) of the block at rows kb*32..
   auto read_v1 = [&](const bf16* Vt, int kb, int i) {
     const int half = i / (D / 32), mb = i % (D / 32);

@@ -179,15 +179,19 @@ struct OpOffsets {
   // byte offsets (the reads add them to byte addresses, so no shift is needed per read)
   int a[D / 16];     // tile_row8 of row `row` at logical chunk 2 kk + hi
   int t[D / 32][2];  // tile_tr8 of rows tr0 = 16 hi + arow and tr0 + 4 at chunk tchunk + 4 mb
-  __device__ __forceinline__ void init(int row, int hi, int arow, int tchunk, int thalf) {
+  // abias, tbias: bytes added to the row and to the transposed offsets, for a caller that
+  // reads those operands through tile pointers moved back by as much (so that tiles far into
+  // the LDS array still fall within the read's 16-bit offset field and need no add)
+  __device__ __forceinline__ void init(int row, int hi, int arow, int tchunk, int thalf, int abias = 0,
+                                       int tbias = 0) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) a[kk] = 2 * (row * D + (((2 * kk + hi) ^ swz<D>(row)) * 8));
+    for (int kk = 0; kk < D / 16; ++kk) a[kk] = abias + 2 * (row * D + (((2 * kk + hi) ^ swz<D>(row)) * 8));
     const int tr0 = 16 * hi + arow;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       const int c = tchunk + 4 * mb;
-      t[mb][0] = 2 * (tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf);
-      t[mb][1] = 2 * ((tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf);
+      t[mb][0] = tbias + 2 * (tr0 * D + ((c ^ swz<D>(tr0)) * 8) + thalf);
+      t[mb][1] = tbias + 2 * ((tr0 + 4) * D + ((c ^ swz<D>(tr0 + 4)) * 8) + thalf);
     }
     repin();
   }
