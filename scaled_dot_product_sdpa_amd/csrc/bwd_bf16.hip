@@ -298,8 +298,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int qi = r0 + 16 * hi + v;
-        const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff) &&
-                        (W == 0 || myk > qi + coff - W);
+        const bool ok = (myk < kv_end) & (qi < q_end) & (!CAUSAL | (myk <= qi + coff)) &
+                        ((W == 0) | (myk > qi + coff - W));
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -660,8 +660,8 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int qi = r0 + 16 * hi + v;
-            const bool ok = myk < kv_end && qi < q_end && (!CAUSAL || myk <= qi + coff) &&
-                            (W == 0 || myk > qi + coff - W);
+            const bool ok = (myk < kv_end) & (qi < q_end) & (!CAUSAL | (myk <= qi + coff)) &
+                            ((W == 0) | (myk > qi + coff - W));
             s[v] = ok ? s[v] : kNegInf;
           }
         }
@@ -949,8 +949,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff) &&
-                        (W == 0 || key > qi + coff - W);
+        const bool ok = (key < kv_end) & qok & (!CAUSAL | (key <= qi + coff)) &
+                        ((W == 0) | (key > qi + coff - W));
         s[v] = ok ? s[v] : kNegInf;
       }
     }
@@ -1287,8 +1287,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
           float x = MASK ? s_acc[v] : fmaf(s_acc[v], c2, -lse2);
           if (partial_t) {
             const int key = key0 + v;
-            const bool ok = key < kv_end && qok && (!CAUSAL || key <= qi + coff) &&
-                            (W == 0 || key > qi + coff - W);
+            const bool ok = (key < kv_end) & qok & (!CAUSAL | (key <= qi + coff)) &
+                            ((W == 0) | (key > qi + coff - W));
             x = ok ? x : kNegInf;
           }
           const float pv = fast_exp2(x);

@@ -225,8 +225,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + v;
-        const bool ok = key < kv_end && qrow < q_end && (!CAUSAL || key <= qrow + coff) &&
-                        (W == 0 || key > qrow + coff - W);
+        const bool ok = (key < kv_end) & (qrow < q_end) & (!CAUSAL | (key <= qrow + coff)) &
+                        ((W == 0) | (key > qrow + coff - W));
         x[v] = ok ? x[v] : kNegInf;
       }
     }
