@@ -132,7 +132,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int bid, int nblk, c
   const Problem& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -808,6 +808,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int bid, int nblk, cha
   const Problem& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // the wave index stays a vector value here: as a scalar, the per-wave block tests become
+  // branches whose joins copy the accumulators (a vector test runs both sides under exec)
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -1117,6 +1119,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   const Problem& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // the wave index stays a vector value here: as a scalar, the per-wave block tests become
+  // branches whose joins copy the accumulators (a vector test runs both sides under exec)
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
