@@ -97,6 +97,14 @@ CASES = {
     "cross_gqa_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=333, Lk=200, causal=False, seed=63),
     "cross_gqa_lens_d128": W["gqa_causal_4k"].scaled(B=3, Hq=4, Hkv=1, Lq=150, Lk=460, causal=False,
                                                      lens="kv", len_range=(1, 460), poison=True, seed=64),
+    # the paired dK/dV loop's first and last phases with nothing between: one query tile
+    # (40 rows, MHA), two (65 rows: a tile and a one-row tail) and, causal, a key range
+    # whose last workgroup has keys for only some of its wave pairs (300 = 2*128 + 44)
+    "one_q_tile_d128": W["gqa_causal_4k"].scaled(B=2, Hq=2, Hkv=2, Lq=40, Lk=300, causal=False, seed=65),
+    "two_q_tiles_d128": W["gqa_causal_4k"].scaled(B=1, Hq=4, Hkv=2, Lq=65, Lk=300, causal=False, seed=66),
+    "causal_pair_tail_d128": W["gqa_causal_4k"].scaled(B=1, Hq=2, Hkv=1, Lq=300, Lk=300, seed=67),
+    "window_cross_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=260, Lk=700, causal=2,
+                                                   window=100, seed=68),
 }
 
 
