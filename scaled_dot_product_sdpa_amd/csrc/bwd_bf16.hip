@@ -470,15 +470,19 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // k-1.  Block k is rows (k % 2) * 32 of tile k / 2.  Tile t+2 is copied into the buffer of
 // tile t-1 after barrier 2t (the last phase reading tile t-1 is 2t) and must have landed by
 // barrier 2t+3.
-template <int D, int NP>
+// With a mask (rows that allow 16-byte copies), each block's 32 mask rows of the workgroup's
+// keys are copied by the eight waves (one 1 KB copy each) into three 8 KB buffers: block
+// k+3's after barrier k, into the buffer block k used, landed by barrier k+2 (the copy of a
+// block goes before the tile copied with it, so waiting for it leaves the tile in flight).
+template <int D, int NP, bool MASK>
 constexpr int dkdv_pair_lds_bytes() {
-  return 3 * (2 * kQT * D * 2 + 2 * kQT * 4) + 2 * NP * 64 * 16 * 4;
+  return 3 * (2 * kQT * D * 2 + 2 * kQT * 4) + 2 * NP * 64 * 16 * 4 + (MASK ? 3 * 32 * 32 * NP * 2 : 0);
 }
 
 template <bool V> struct Role { static constexpr bool value = V; };
 
 // The waves of one role (PW: P waves, else dS waves).
-template <bool PW, int D, int NP, int CM>
+template <bool PW, int D, int NP, int CM, bool MASK>
 __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nblk, char* smem) {
   constexpr bool CAUSAL = CM != 0;
   constexpr int NW = 2 * NP;
@@ -498,7 +502,10 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   float* const R1s = R0 + 2 * kQT;
   float* const R2s = R1s + 2 * kQT;
   char* const Pex = reinterpret_cast<char*>(R2s + 2 * kQT);  // [2][NP][64 lanes x 16 fp32]
-  static_assert(6 * TILE * 2 + 6 * kQT * 4 + 2 * NP * 4096 == dkdv_pair_lds_bytes<D, NP>(), "LDS layout");
+  constexpr int MBLK = 32 * KT;  // mask rows of one block
+  bf16* const Mk = reinterpret_cast<bf16*>(Pex + 2 * NP * 4096);  // [3][32 rows x KT keys]
+  static_assert(6 * TILE * 2 + 6 * kQT * 4 + 2 * NP * 4096 + (MASK ? 3 * MBLK * 2 : 0) ==
+                    dkdv_pair_lds_bytes<D, NP, MASK>(), "LDS layout");
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
@@ -552,8 +559,36 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
     gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
   };
   static_assert(2 * TileCopy<kQT, D, NW>::PER_WAVE == 4, "copies per wave and tile");
+  // Mask rows of block k (32 rows x KT keys, 16-byte chunks, row-major) into Mk[k % 3]:
+  // chunk wave * 64 + lane; keys past Lk read the next row (or zeros past the end), and
+  // those pairs are masked by the predicates.
+  const int nb = 2 * total;
+  uint32_t mvoff = 0;
+  if (MASK) {
+    const int ci = wave * 64 + lane;
+    mvoff = (uint32_t)((ci / (KT / 8)) * p.m_si * 2 + (ci % (KT / 8)) * 16);
+  }
+  static_assert(!MASK || 32 * KT / 8 == 64 * NW, "one mask chunk per lane and block");
+  auto load_mask = [&](int k) __attribute__((always_inline)) {
+    if (!MASK || k >= nb) return;
+    int h, i0;
+    tile_rows(k >> 1, h, i0);
+    const int r0 = i0 + (k & 1) * 32;
+    const bf16* mb = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh + (int64_t)r0 * p.m_si + j0;
+    const int nr = min(p.Lq - r0, 32);
+    const i32x4 rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
+    buffer_to_lds<16>(rs, Mk + (k % 3) * MBLK, wave * 1024, mvoff);
+  };
+  // Wait until the copies issued after the mask (or tile) that the next barrier publishes
+  // are the only ones in flight: one tile's copies (five for the waves that also copy the
+  // row values) and one block's mask.
+  auto wait_tile_and_mask = [&]() __attribute__((always_inline)) {
+    if (wave < 2) wait_vmem_le<6>();
+    else wait_vmem_le<5>();
+  };
 
   const float c2 = p.scale_log2;
+  const float sc = p.scale;
   const int qr = perm_row(l32);
   const int blk = lane >> 4;
   const int arow = (lane & 15) >> 2;
@@ -563,6 +598,8 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   {
     // K (P wave) or V (dS wave) of this lane's key: B operand of S or dP
     if (total > 0) load_tile(0, Q0, G0, R0);
+    load_mask(0);
+    load_mask(1);
     bf16x8 kv[NS];
     {
       const bf16* base = reinterpret_cast<const bf16*>(PW ? a.k : a.v) +
@@ -574,6 +611,7 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
         kv[kk] = __builtin_bit_cast(bf16x8, ok ? ld16(base + (int64_t)myk * sl + kk * 16 + 8 * hi) : zero16());
     }
     wait_vmem();
+    load_mask(2);
     if (total > 1) load_tile(1, Q1, G1, R1s);
 
     f32x16 acc[NT];
@@ -653,6 +691,13 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
 #pragma unroll
         for (int c = 0; c < 4; ++c) l4[c] = reinterpret_cast<const f32x4*>(Rc + kb * 32 + 16 * hi)[c];
       }
+      // the mask values of the lane's key and rows (copied before the last barrier)
+      float mbias[16];
+      if constexpr (PW && !LAST && MASK) {
+        const bf16* mc = Mk + (k % 3) * MBLK + 16 * hi * KT + pair * 32 + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mbias[v] = bf2f(mc[v * KT]);
+      }
       auto p_mask = [&]() __attribute__((always_inline)) {
         const bool partial = (jw + 32 > kv_end) || (r0 + 32 > q_end) || (CAUSAL && r0 + coff < jw + 31) ||
                              (W > 0 && jw <= r0 + 31 + coff - W);
@@ -669,8 +714,15 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
       auto p_scores = [&](int e0, int e1) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = e0; e < e1; e += 2) {
-          xv[e] = fast_exp2(fmaf(s[e], c2, -l4[e / 4][e % 4]));
-          xv[e + 1] = fast_exp2(fmaf(s[e + 1], c2, -l4[e / 4][(e + 1) % 4]));
+          // with a mask, scale * s + m - LSE in natural units (the prep kernel then stores
+          // LSE itself), and only the difference goes to log2 units
+          if constexpr (MASK) {
+            xv[e] = fast_exp2((fmaf(s[e], sc, mbias[e]) - l4[e / 4][e % 4]) * kLog2e);
+            xv[e + 1] = fast_exp2((fmaf(s[e + 1], sc, mbias[e + 1]) - l4[e / 4][(e + 1) % 4]) * kLog2e);
+          } else {
+            xv[e] = fast_exp2(fmaf(s[e], c2, -l4[e / 4][e % 4]));
+            xv[e + 1] = fast_exp2(fmaf(s[e + 1], c2, -l4[e / 4][(e + 1) % 4]));
+          }
           const f32x2 pp = {xv[e], xv[e + 1]};
           const bf16x2 p2 = __builtin_convertvector(pp, bf16x2);
           cur_bf[e / 8][e % 8] = p2[0];
@@ -715,16 +767,31 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
     using F = Role<false>;
     // tile t: phase 2t (block 2t; block 2t-1 of tile t-1), barrier, copy of tile t+2 into
     // tile t-1's buffer, phase 2t+1 (block 2t+1; block 2t), wait for tile t+1, barrier.
+    // With a mask, the mask of block k+3 is copied after barrier k, and the barrier before
+    // phase k waits for the mask of block k: behind it are then only the copies issued after
+    // barrier k-2 (a tile, if one was, and a mask).
     auto step = [&](auto first_t, int t, const bf16* Qp, const bf16* Gp, const float* Rp, const bf16* Qc,
                     const bf16* Gc, const float* Rc, bf16* Ql, bf16* Gl, float* Rl) __attribute__((always_inline)) {
       ofs.repin();
       phase(first_t, F{}, 2 * t, Qc, Gc, Rc, 0, Qp, Gp, Rp, 1, pa, pb, dpa, dpb);
+      if constexpr (MASK) {
+        if (t + 1 < total) wait_tile_and_mask();  // tile t+1 and the mask of block 2t+2 behind
+        else wait_vmem();
+      }
       __syncthreads();
+      load_mask(2 * t + 3);
       if (t + 2 < total) load_tile(t + 2, Ql, Gl, Rl);
       phase(F{}, F{}, 2 * t + 1, Qc, Gc, Rc, 1, Qc, Gc, Rc, 0, pb, pa, dpb, dpa);
-      if (t + 2 < total) wait_vmem_le<4>();
-      else wait_vmem();
+      if (t + 2 < total) {
+        if constexpr (MASK) wait_tile_and_mask();  // the mask of block 2t+3 and tile t+2 behind
+        else wait_vmem_le<4>();
+      } else if (MASK && 2 * t + 3 < nb) {
+        wait_vmem_le<1>();  // the mask of block 2t+3 behind
+      } else {
+        wait_vmem();
+      }
       __syncthreads();
+      load_mask(2 * t + 4);
     };
     if (total > 0) {
       __syncthreads();  // every wave's share of tile 0 has landed
@@ -763,16 +830,18 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   }
 }
 
-template <int D, int NP, int CM>
+template <int D, int NP, int CM, bool MASK>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int bid, int nblk, char* smem) {
-  if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < NP) dkdv_pair_wave<true, D, NP, CM>(a, bid, nblk, smem);
-  else dkdv_pair_wave<false, D, NP, CM>(a, bid, nblk, smem);
+  if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < NP)
+    dkdv_pair_wave<true, D, NP, CM, MASK>(a, bid, nblk, smem);
+  else
+    dkdv_pair_wave<false, D, NP, CM, MASK>(a, bid, nblk, smem);
 }
 
-template <int D, int NP, int CM>
+template <int D, int NP, int CM, bool MASK>
 __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[dkdv_pair_lds_bytes<D, NP>()];
-  dkdv_pair_body<D, NP, CM>(a, blockIdx.x, gridDim.x, smem);
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_pair_lds_bytes<D, NP, MASK>()];
+  dkdv_pair_body<D, NP, CM, MASK>(a, blockIdx.x, gridDim.x, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1349,8 +1418,8 @@ template <int D> struct BwdShape;
 // one) without / with a mask; it needs two waves per SIMD, which its registers allow except
 // with a mask at D = 128.  FUSE: dK/dV and dQ in one launch (bwd_fused_kernel), whose
 // bodies fit two waves per SIMD only at D = 64.
-// PAIR_DKDV: dK/dV without a mask runs the paired-wave kernel (two waves per 32-key slice);
-// with a mask its tiles do not fit the LDS beside the P exchange buffers.
+// PAIR_DKDV: dK/dV runs the paired-wave kernel (two waves per 32-key slice), with a mask
+// when its rows allow 16-byte copies (the mask is staged per 32-row block).
 template <> struct BwdShape<64> {
   static constexpr int KV_NW = 4, Q_NW = 4;
   static constexpr bool PIPE_DQ = true, PIPE_DQ_MASK = true, FUSE = true, PAIR_DKDV = false;
@@ -1377,10 +1446,15 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
     }
   }
   if ((stages & kBwdDkdv) && n_kt > 0) {
-    if constexpr (BwdShape<D>::PAIR_DKDV && !MASK)
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM>), dim3(n_kt * a.p.B * a.p.Hkv), dim3(128 * KNW), 0,
-                         s, a);
-    else
+    bool paired = false;
+    if constexpr (BwdShape<D>::PAIR_DKDV) {
+      if (!MASK || a.p.mask_vec) {
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
+                           dim3(128 * KNW), 0, s, a);
+        paired = true;
+      }
+    }
+    if (!paired)
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
                          dim3(64 * KNW), 0, s, a);
     hipError_t e = hipGetLastError();

@@ -105,6 +105,17 @@ CASES = {
     "causal_pair_tail_d128": W["gqa_causal_4k"].scaled(B=1, Hq=2, Hkv=1, Lq=300, Lk=300, seed=67),
     "window_cross_d128": W["gqa_causal_4k"].scaled(B=2, Hq=4, Hkv=2, Lq=260, Lk=700, causal=2,
                                                    window=100, seed=68),
+    # masks whose rows allow 16-byte copies (key count a multiple of 8), which the paired
+    # dK/dV kernel stages per 32-row block: padded with lengths, the same mask only, a GQA
+    # causal mask with Lq != Lk and a single query tile
+    "padded_mask_vec_d128": W["padded_mask_2k"].scaled(B=3, Hq=2, Hkv=2, Lq=264, Lk=264,
+                                                       len_range=(40, 264), seed=69),
+    "padded_mask_vec_only_d128": W["padded_mask_2k"].scaled(B=3, Hq=2, Hkv=2, Lq=264, Lk=264,
+                                                            len_range=(40, 264), seed=69, lens="none_keep"),
+    "causal_mask_gqa_d128": W["padded_mask_2k"].scaled(B=2, Hq=4, Hkv=2, Lq=200, Lk=328, causal=2,
+                                                       lens="chunk", len_range=(150, 328), seed=70),
+    "mask_one_q_tile_d128": W["padded_mask_2k"].scaled(B=2, Hq=2, Hkv=2, Lq=40, Lk=40,
+                                                       len_range=(1, 40), seed=71),
 }
 
 
