@@ -269,8 +269,8 @@ def roofline(name, w, res):
     masked = w.mask != "none"
     if dom == "dq":  # the block-sequential dQ kernel runs only at d = 128 with a mask
         kname = "bwd_dq_seq_kernel" if (w.D == 128 and masked) else "bwd_dq_kernel"
-    if dom == "dkdv":  # at d = 128 without a mask each key slice is split over two waves
-        kname = "bwd_dkdv_pair_kernel" if (w.D == 128 and not masked) else "bwd_dkdv_kernel"
+    if dom == "dkdv":  # at d = 128 each key slice is split over two waves (the workloads' masks
+        kname = "bwd_dkdv_pair_kernel" if w.D == 128 else "bwd_dkdv_kernel"  # allow 16-byte copies)
     if w.dtype == "f32":  # the fp32 path's kernels (main: its dK/dV and dQ kernels)
         kname = {"fwd": "fwd_f32_kernel", "prep": "bwd_prep_f32_kernel", "dkdv": "bwd_dkdv_f32_kernel",
                  "dq": "bwd_dq_f32_kernel"}.get(dom, kname)

@@ -22,9 +22,10 @@
 //            with dO^T and Q^T read from LDS by ds_read_b64_tr_b16.  Inside a wave the
 //            blocks are software-pipelined: the dV, dK MFMAs of block b-1 run with the P, dS
 //            arithmetic of block b, and the S, dP MFMAs of block b+1 with the rest of it.
-//            At D = 128 without a mask each 32-key slice is split over a pair of waves
-//            (S, P, dV in one; dP, dS, dK in the other, P handed over through LDS), which
-//            fits two waves per SIMD where one wave holding both needs ~320 registers.
+//            At D = 128 (with a mask, when its rows allow 16-byte copies) each 32-key slice
+//            is split over a pair of waves (S, P, dV in one; dP, dS, dK in the other, P
+//            handed over through LDS), which fits two waves per SIMD where one wave holding
+//            both needs ~320 registers.
 //  3. dq:    query-stationary (the forward's decomposition, 4 waves of 32 rows).  Per
 //            32-key block of a 64-key K/V tile (three LDS buffers, buffer-load copies):
 //              S^T = K Q^T,  P^T,  dP^T = V dO^T,  dS^T = P^T o (dP^T - D),
