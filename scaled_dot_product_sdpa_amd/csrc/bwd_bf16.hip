@@ -458,6 +458,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // (batch, KV head) and walks the group's query tiles through three LDS buffers), but each
 // 32-key slice is split over two waves by the products it feeds:
 //   wave w < NP ("P wave"):   S = Q K^T,  P = exp2(S * scale * log2e - lse2),  dV^T += dO^T P
+//                             (with a mask, P = exp2((S * scale + m - LSE) * log2e))
 //   wave w + NP ("dS wave"):  dP = dO V^T,  dS = P o (dP - D),                  dK^T += Q^T dS
 // The P wave hands P (fp32, in its own accumulator layout: lane = key, 16 query rows) to
 // its partner through LDS, one barrier per 32-row block.  Each wave then holds one operand
@@ -480,6 +481,8 @@ constexpr int dkdv_pair_lds_bytes() {
   return 3 * (2 * kQT * D * 2 + 2 * kQT * 4) + 2 * NP * 64 * 16 * 4 + (MASK ? 3 * 32 * 32 * NP * 2 : 0);
 }
 
+// A compile-time flag passed as an argument, so that the generic phase and step lambdas
+// below are instantiated separately for the first and last phases.
 template <bool V> struct Role { static constexpr bool value = V; };
 
 // The waves of one role (PW: P waves, else dS waves).
