@@ -134,12 +134,13 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // Mask values of block `bi` for this lane (keys 32*bi + 16*hi + 0..15 of row qrow),
   // read two blocks ahead (see body).  Rows whose mask cannot be read with 16-byte loads
   // take the element path in pre_scores.
-  auto mask_vec_ok = [&](int bi) {
-    return p.mask_vec && qrow < q_end && 32 * bi + 16 * hi + 16 <= p.Lk;
-  };
+  // A block's mask values come as two 16-byte loads per lane when its 32 keys lie within the
+  // mask rows (a test on the block alone, so that the whole wave takes one path); rows past
+  // the last one read the last row instead, their scores being hidden by the predicates.
+  auto mask_vec_ok = [&](int bi) { return p.mask_vec && 32 * bi + 32 <= p.Lk; };
   auto load_mask = [&](int bi, u32x4 (&m)[2]) {
     if (MASK && bi < nvis && mask_vec_ok(bi)) {
-      const bf16* mp = mb_ + (int64_t)qrow * p.m_si + 32 * bi + 16 * hi;
+      const bf16* mp = mb_ + (int64_t)min(qrow, p.Lq - 1) * p.m_si + 32 * bi + 16 * hi;
       m[0] = ld16(mp);
       m[1] = ld16(mp + 8);
     } else {
@@ -202,9 +203,19 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // mask value near the bottom of the fp32 range (say the most negative bf16) times
   // log2(e) would overflow to -inf and turn a row masked that way into an empty one,
   // where the definition gives equal weights.
+  // With a mask, the pairs a boundary block hides get a mask value of -inf before it is
+  // added (the score itself is finite), so that the scores are written once, after the
+  // branch: a branch that rewrites them makes the compiler copy all sixteen at its join.
   auto pre_scores = [&](int bi, f32x16& x, const u32x4 (&mk)[2]) {
     const int key_lo = 32 * bi;
     const int key0 = key_lo + 16 * hi;
+    const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo + coff) ||
+                         (wq_lo + 32 > q_end) || (W > 0 && key_lo <= wq_hi + coff - W);
+    auto visible = [&](int v) __attribute__((always_inline)) {
+      const int key = key0 + v;
+      return (key < kv_end) & (qrow < q_end) & (!CAUSAL | (key <= qrow + coff)) &
+             ((W == 0) | (key > qrow + coff - W));
+    };
     if (MASK) {
       float mv[16];
       if (mask_vec_ok(bi)) {
@@ -216,19 +227,15 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
         for (int v = 0; v < 16; ++v)
           mv[v] = (qrow < q_end && key0 + v < kv_end) ? bf2f(mb_[(int64_t)qrow * p.m_si + key0 + v]) : 0.f;
       }
+      if (partial) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mv[v] = visible(v) ? mv[v] : kNegInf;
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) x[v] = fmaf(x[v], sc, mv[v]);
-    }
-    const bool partial = (key_lo + 32 > kv_end) || (CAUSAL && key_lo + 31 > wq_lo + coff) ||
-                         (wq_lo + 32 > q_end) || (W > 0 && key_lo <= wq_hi + coff - W);
-    if (partial) {
+    } else if (partial) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + v;
-        const bool ok = (key < kv_end) & (qrow < q_end) & (!CAUSAL | (key <= qrow + coff)) &
-                        ((W == 0) | (key > qrow + coff - W));
-        x[v] = ok ? x[v] : kNegInf;
-      }
+      for (int v = 0; v < 16; ++v) x[v] = visible(v) ? x[v] : kNegInf;
     }
   };
 
