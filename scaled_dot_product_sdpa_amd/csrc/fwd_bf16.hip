@@ -168,11 +168,18 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   // chains.
   f32x16 oacc[D / 32];
   float mref = kNegInf, frow = 0.f, frow2 = 0.f;
+  // The per-block test and offset come precomputed from the last move of mref, so a block
+  // that leaves it in place spends one compare on it: mthr is the block max (raw score, or
+  // natural units with a mask) past which mref moves, nmu the negated offset stage A adds
+  // (0 while a row has seen no key).
+  float mthr = kNegInf, nmu = 0.f;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
 
   const float c2 = p.scale_log2;
   const float sc = p.scale;
+  // growth of the block max (raw score units; natural units with a mask) that moves mref
+  const float thr = MASK ? kRescaleLog2 * kLn2 : kRescaleLog2 / c2;
   // K operand read: row kb*32 + perm_row(l32), logical chunk 2*kk + hi
   const int krow_l = perm_row(l32);
   // V^T operand (transposing read): row key_base + arow, logical chunk vchunk, half vhalf
@@ -240,34 +247,36 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Row max of the block (partial maxima `mx` over the lane's scores) -> moves the
-  // reference max if some row grew past the threshold; returns the offset stage A takes
-  // off the scores.  mref is in log2 units, or in natural units with a mask.
+  // reference max if some row grew past the threshold; returns the negated offset stage A
+  // adds to the scores.  mref is in log2 units, or in natural units with a mask.
   auto post_max = [&](float mx) {
     mx = xhalf_max(mx);
-    const float mt = MASK ? mx : mx * c2;  // block max (c2 > 0)
-    const bool need = mt > mref + (MASK ? kRescaleLog2 * kLn2 : kRescaleLog2);
+    const bool need = mx > mthr;
     if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mt = MASK ? mx : mx * c2;  // block max in mref's units (c2 > 0)
       const float mnew = need ? mt : mref;
       const float corr = need ? fast_exp2(MASK ? (mref - mnew) * kLog2e : mref - mnew) : 1.f;
       mref = mnew;
+      mthr = need ? mx + thr : mthr;
+      nmu = mref == kNegInf ? 0.f : -mref;
       frow *= corr;
       frow2 *= corr;
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= corr;
     }
-    return (mref == kNegInf) ? 0.f : mref;
+    return nmu;
   };
 
   // Weights of score pair pr (scores 2pr, 2pr+1) in three stages one pipeline slot apart,
   // so that no stage waits on the result of the one before it:
   //   A: exp2 argument;  B: exp2;  C: bf16 B operand of O^T += V^T P^T, both sums.
-  auto stage_a = [&](const f32x16& x, float m_use, int pr, f32x2 (&t)[8]) {
+  auto stage_a = [&](const f32x16& x, float nm, int pr, f32x2 (&t)[8]) {
     if (MASK) {
-      t[pr][0] = (x[2 * pr] - m_use) * kLog2e;
-      t[pr][1] = (x[2 * pr + 1] - m_use) * kLog2e;
+      t[pr][0] = (x[2 * pr] + nm) * kLog2e;
+      t[pr][1] = (x[2 * pr + 1] + nm) * kLog2e;
     } else {
-      t[pr][0] = fmaf(x[2 * pr], c2, -m_use);
-      t[pr][1] = fmaf(x[2 * pr + 1], c2, -m_use);
+      t[pr][0] = fmaf(x[2 * pr], c2, nm);
+      t[pr][1] = fmaf(x[2 * pr + 1], c2, nm);
     }
   };
   auto stage_b = [&](int pr, f32x2 (&t)[8]) {
@@ -324,14 +333,14 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int v = j * E; v < (j + 1) * E; ++v) mx = fmaxf(mx, x[v]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float m_use = post_max(mx);
+    const float nm = post_max(mx);
     // region 2
 
     snext = f32x16{};
     constexpr int P = 8 / NS;  // score pairs per slot
     f32x2 t[8];
 #pragma unroll
-    for (int pr = 0; pr < 2 * P; ++pr) stage_a(x, m_use, pr, t);
+    for (int pr = 0; pr < 2 * P; ++pr) stage_a(x, nm, pr, t);
 #pragma unroll
     for (int pr = 0; pr < P; ++pr) stage_b(pr, t);
 #pragma unroll
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void fwd_bf16_kernel(FwdArgs a) {
       pv_v[i] = read_v1(Vt, kb, i);
       snext = mfma32(kop[i], qreg[i], snext);
 #pragma unroll
-      for (int pr = (i + 2) * P; pr < (i + 3) * P && pr < 8; ++pr) stage_a(x, m_use, pr, t);
+      for (int pr = (i + 2) * P; pr < (i + 3) * P && pr < 8; ++pr) stage_a(x, nm, pr, t);
 #pragma unroll
       for (int pr = (i + 1) * P; pr < (i + 2) * P && pr < 8; ++pr) stage_b(pr, t);
 #pragma unroll
