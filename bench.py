@@ -266,9 +266,8 @@ def roofline(name, w, res):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(name, dom)
     kname = KERNEL_NAMES[dom]
-    masked = w.mask != "none"
-    if dom == "dq":  # the block-sequential dQ kernel runs only at d = 128 with a mask
-        kname = "bwd_dq_seq_kernel" if (w.D == 128 and masked) else "bwd_dq_kernel"
+    if dom == "dq":  # at d = 128 dQ is formed from the dS blocks the dK/dV pass stored
+        kname = "bwd_dq_ds_kernel" if w.D == 128 else "bwd_dq_kernel"
     if dom == "dkdv":  # at d = 128 each key slice is split over two waves (the workloads' masks
         kname = "bwd_dkdv_pair_kernel" if w.D == 128 else "bwd_dkdv_kernel"  # allow 16-byte copies)
     if w.dtype == "f32":  # the fp32 path's kernels (main: its dK/dV and dQ kernels)

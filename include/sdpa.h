@@ -107,9 +107,22 @@ typedef struct {
  * work on the stream has finished. */
 size_t sdpa_forward_workspace_bytes(const sdpa_problem* p);
 
-/* Device workspace (bytes) the backward needs: per query row, D = rowsum(dO o O) and
- * LSE * log2(e), both fp32. */
+/* Device workspace (bytes) the backward takes: per query row, D = rowsum(dO o O) and
+ * LSE * log2(e), both fp32; then, for bf16 at Dqk = Dv = 128 when it stays within 8 GiB, a
+ * buffer of bf16 dS blocks.  With that buffer, sdpa_backward (and sdpa_backward_main)
+ * write dS = P o (dP - D) from the dK/dV pass, rounded to bf16 as the dK and dQ products
+ * take it, and form dQ = scale dS K from it instead of recomputing S, P and dP in a second
+ * pass (tinyllm L5.1 section 2.3 gives dQ = scale dS K; cuDNN "Attention", SDPA FP16/BF16
+ * Backward, lists a backward workspace).  Buffer size: 2 KB per 32 x 32 block of every
+ * (batch, query head), i.e. B * Hq * 2ceil(Lq/64) * 4ceil(Lk/128) * 2048 bytes.  The
+ * result stays deterministic. */
 size_t sdpa_backward_workspace_bytes(const sdpa_problem* p);
+
+/* The least workspace (bytes) the backward accepts: the per-row values alone.  A workspace
+ * smaller than sdpa_backward_workspace_bytes runs dQ as its own pass, which recomputes
+ * S, P and dP (the same gradients within rounding: the fp32 accumulation order of dQ
+ * differs). */
+size_t sdpa_backward_workspace_bytes_min(const sdpa_problem* p);
 
 /*
  * Forward.  q (B,Hq,Lq,Dqk), k (B,Hkv,Lk,Dqk), v (B,Hkv,Lk,Dv), o (B,Hq,Lq,Dv) in the io
@@ -158,13 +171,18 @@ sdpa_status sdpa_backward(const sdpa_problem* p, const void* q, const void* k, c
  * arguments, validation and workspace as sdpa_backward.
  *   prep: D_i = rowsum(dO o O)_i and LSE_i * log2(e) (fp32, into the workspace; D = 0 and
  *         +inf for empty rows);
- *   dkdv: dK and dV (reads D from the workspace);
- *   dq:   dQ       (reads D from the workspace).
+ *   dkdv: dK and dV (reads D from the workspace; stores dS when the workspace holds the
+ *         dS buffer);
+ *   dq:   dQ       (reads D from the workspace; with the dS buffer, reads the dS that dkdv
+ *         stored).
  *   main: dkdv and dq in one call (after prep), which is what sdpa_backward runs after its
  *         prep: at d = 64 without a mask the two passes share one launch, dQ work filling
- *         the CUs that the dK/dV work leaves idle; otherwise dkdv then dq.
- * Once prep has finished, dkdv and dq are independent of each other and may run
- * concurrently on two streams.  Source: the backward of tinyllm L5.1 section 2.3, with D
+ *         the CUs that the dK/dV work leaves idle; at d = 128 with the dS buffer, dkdv
+ *         storing dS, then dQ from it; otherwise dkdv then dq.
+ * With the dS buffer in the workspace (sdpa_backward_workspace_bytes at d = 128), dq must
+ * follow dkdv on the same workspace.  With the least workspace
+ * (sdpa_backward_workspace_bytes_min), dkdv and dq are independent of each other once prep
+ * has finished and may run concurrently on two streams.  Source: the backward of tinyllm L5.1 section 2.3, with D
  * computed from the output as that section's identity D_i = dO_i . o_i allows.
  */
 sdpa_status sdpa_backward_prep(const sdpa_problem* p, const void* q, const void* k,

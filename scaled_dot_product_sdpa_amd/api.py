@@ -30,7 +30,8 @@ SDPA_DTYPE_F32 = 0
 SDPA_DTYPE_BF16 = 1
 
 EXPORTS = (
-    "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes", "sdpa_forward",
+    "sdpa_forward_workspace_bytes", "sdpa_backward_workspace_bytes",
+    "sdpa_backward_workspace_bytes_min", "sdpa_forward",
     "sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv", "sdpa_backward_dq",
     "sdpa_backward_main",
     "sdpa_status_string", "sdpa_last_error", "sdpa_version", "sdpa_decode_paged_workspace_bytes",
@@ -90,6 +91,8 @@ def load_library(path: Path | str | None = None):
     lib.sdpa_forward_workspace_bytes.restype = sz
     lib.sdpa_backward_workspace_bytes.argtypes = [pp]
     lib.sdpa_backward_workspace_bytes.restype = sz
+    lib.sdpa_backward_workspace_bytes_min.argtypes = [pp]
+    lib.sdpa_backward_workspace_bytes_min.restype = sz
     lib.sdpa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sdpa_forward.restype = ctypes.c_int
     lib.sdpa_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -380,7 +383,7 @@ class BackwardCall:
 
     def __init__(self, q, k, v, o, dO, lse, mask=None, scale=None, is_causal=False,
                  seq_lens_q=None, seq_lens_kv=None, offsets_q=None, offsets_kv=None,
-                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0):
+                 max_seqlen_q=None, max_seqlen_kv=None, sliding_window=0, ds_buffer=True):
         self.lib = load_library()
         self.ragged = offsets_q is not None or offsets_kv is not None
         self.squeeze = q.dim() == 3 and not self.ragged
@@ -427,7 +430,11 @@ class BackwardCall:
         self.dq = _grad_like(qt, oq is not None)
         self.dk = _grad_like(kt, ok is not None)
         self.dv = _grad_like(vt, ok is not None)
-        nws = self.lib.sdpa_backward_workspace_bytes(ctypes.byref(self.p))
+        # the full workspace holds the dS buffer (d = 128, bf16): dQ is then formed from the
+        # dK/dV pass's dS; ds_buffer=False passes the least workspace (dQ recomputed)
+        ws_bytes = (self.lib.sdpa_backward_workspace_bytes if ds_buffer
+                    else self.lib.sdpa_backward_workspace_bytes_min)
+        nws = ws_bytes(ctypes.byref(self.p))
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self._keep = (qt, kt, vt, o, dO, lse, m, lq, lk, oq, ok)
         self.device = dev

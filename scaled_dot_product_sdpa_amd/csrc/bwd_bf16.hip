@@ -485,8 +485,14 @@ constexpr int dkdv_pair_lds_bytes() {
 // below are instantiated separately for the first and last phases.
 template <bool V> struct Role { static constexpr bool value = V; };
 
-// The waves of one role (PW: P waves, else dS waves).
-template <bool PW, int D, int NP, int CM, bool MASK>
+// The waves of one role (PW: P waves, else dS waves).  STORE: the dS waves also write each
+// block's bf16 dS to the dS buffer (BwdArgs::ds) for the dQ-from-dS kernel, and the P waves
+// alone copy the tiles and masks.  The vector-memory counter completes loads, copies and
+// stores in issue order, so a wave's copy cannot count as landed before that wave's earlier
+// stores are acknowledged, which for stores that go out to HBM takes longer than the copy
+// pipeline allows (measured: the copy waits then stall the kernel by a sixth).  The dS
+// waves therefore issue no copies and never wait on the counter; the barriers order them.
+template <bool PW, int D, int NP, int CM, bool MASK, bool STORE>
 __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nblk, char* smem) {
   constexpr bool CAUSAL = CM != 0;
   constexpr int NW = 2 * NP;
@@ -543,11 +549,15 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
     i0 = (qt_end - 1 - it % n_q_tiles) * kQT;
   };
 
-  // Tiles HBM -> LDS.  The row copies (lse2 by wave 0, D by wave 1) go first, so that every
-  // wave has at most four copies of a tile issued after the previous tile's.
-  TileCopy<kQT, D, NW> qcopy, gcopy;
-  qcopy.init(p.q_sl, wave, lane);
-  gcopy.init(p.o_sl, wave, lane);
+  // Tiles HBM -> LDS by the CW copying waves (all NW, or the P waves of a storing kernel).
+  // The row copies (lse2 by wave 0, D by wave 1) go first, so that every wave has at most
+  // TPW copies of a tile issued after the previous tile's.
+  constexpr bool CP = !STORE || PW;  // this wave copies
+  constexpr int CW = STORE ? NP : NW;
+  static_assert(NP >= 2, "waves 0 and 1 (P waves) copy the row values");
+  TileCopy<kQT, D, CW> qcopy, gcopy;
+  qcopy.init(p.q_sl, CP ? wave : 0, lane);
+  gcopy.init(p.o_sl, CP ? wave : 0, lane);
   auto load_tile = [&](int it, bf16* Qd, bf16* Gd, float* Rd) __attribute__((always_inline)) {
     int h, i0;
     tile_rows(it, h, i0);
@@ -559,36 +569,41 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
     }
     const bf16* qb = reinterpret_cast<const bf16*>(a.q) + q_base(p, b) + h * p.q_sh;
     const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + o_base(p, b) + h * p.o_sh;
-    qcopy.copy(rows_rsrc<D, kQT>(qb, p.q_sl, i0, q_end), Qd, wave);
-    gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
+    if constexpr (CP) {
+      qcopy.copy(rows_rsrc<D, kQT>(qb, p.q_sl, i0, q_end), Qd, wave);
+      gcopy.copy(rows_rsrc<D, kQT>(dob, p.o_sl, i0, q_end), Gd, wave);
+    }
   };
-  static_assert(2 * TileCopy<kQT, D, NW>::PER_WAVE == 4, "copies per wave and tile");
+  constexpr int TPW = 2 * TileCopy<kQT, D, CW>::PER_WAVE;  // tile copies per copying wave
   // Mask rows of block k (32 rows x KT keys, 16-byte chunks, row-major) into Mk[k % 3]:
-  // chunk wave * 64 + lane; keys past Lk read the next row (or zeros past the end), and
-  // those pairs are masked by the predicates.
+  // chunks (wave * MPW + i) * 64 + lane; keys past Lk read the next row (or zeros past the
+  // end), and those pairs are masked by the predicates.
   const int nb = 2 * total;
-  uint32_t mvoff = 0;
-  if (MASK) {
-    const int ci = wave * 64 + lane;
-    mvoff = (uint32_t)((ci / (KT / 8)) * p.m_si * 2 + (ci % (KT / 8)) * 16);
+  constexpr int MPW = 32 * KT / 8 / (64 * CW);  // mask copies per copying wave and block
+  static_assert(!MASK || MPW * 64 * CW == 32 * KT / 8, "whole mask chunks per lane and block");
+  uint32_t mvoff[MPW];
+#pragma unroll
+  for (int i = 0; i < MPW; ++i) {
+    const int ci = ((CP ? wave : 0) * MPW + i) * 64 + lane;
+    mvoff[i] = MASK ? (uint32_t)((ci / (KT / 8)) * p.m_si * 2 + (ci % (KT / 8)) * 16) : 0u;
   }
-  static_assert(!MASK || 32 * KT / 8 == 64 * NW, "one mask chunk per lane and block");
   auto load_mask = [&](int k) __attribute__((always_inline)) {
-    if (!MASK || k >= nb) return;
+    if (!MASK || !CP || k >= nb) return;
     int h, i0;
     tile_rows(k >> 1, h, i0);
     const int r0 = i0 + (k & 1) * 32;
     const bf16* mb = reinterpret_cast<const bf16*>(p.mask) + b * p.m_sb + h * p.m_sh + (int64_t)r0 * p.m_si + j0;
     const int nr = min(p.Lq - r0, 32);
     const i32x4 rs = raw_rsrc(mb, nr > 0 ? (int64_t)(nr - 1) * p.m_si * 2 + (p.Lk - j0) * 2 : 0);
-    buffer_to_lds<16>(rs, Mk + (k % 3) * MBLK, wave * 1024, mvoff);
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) buffer_to_lds<16>(rs, Mk + (k % 3) * MBLK, (wave * MPW + i) * 1024, mvoff[i]);
   };
   // Wait until the copies issued after the mask (or tile) that the next barrier publishes
-  // are the only ones in flight: one tile's copies (five for the waves that also copy the
-  // row values) and one block's mask.
+  // are the only ones in flight: one tile's copies (one more for the waves that also copy
+  // the row values) and one block's mask.
   auto wait_tile_and_mask = [&]() __attribute__((always_inline)) {
-    if (wave < 2) wait_vmem_le<6>();
-    else wait_vmem_le<5>();
+    if (wave < 2) wait_vmem_le<TPW + MPW + 1>();
+    else wait_vmem_le<TPW + MPW>();
   };
 
   const float c2 = p.scale_log2;
@@ -598,6 +613,7 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   const int arow = (lane & 15) >> 2;
   const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
   const int thalf = 4 * (lane & 1);
+  const uint32_t dso = (uint32_t)(l32 * 64 + hi * 32);  // this lane's bytes of a dS^T block
 
   {
     // K (P wave) or V (dS wave) of this lane's key: B operand of S or dP
@@ -677,9 +693,26 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
           ds[e / 8][e % 8 + 1] = s2[1];
         }
       };
+      // Block k-1's dS to the dS buffer as its 32 x 32 dS^T block: this lane's key row, its
+      // 16 queries (one 32-byte half of the 64-byte row).  The storing waves issue no copies,
+      // so these stores hold up no copy wait.
+      auto store_ds = [&]() __attribute__((always_inline)) {
+        if constexpr (STORE && !PW && !FIRST) {
+          int hp, i0p;
+          tile_rows((k - 1) >> 1, hp, i0p);
+          const int qb = (i0p >> 5) + kbp;
+          const int64_t blk_i = (((int64_t)b * p.Hq + hp) * a.ds_nqb + qb) * a.ds_nkb + (jw >> 5);
+          const reg_rsrc_t rs = reg_rsrc(reinterpret_cast<const bf16*>(a.ds) + blk_i * 1024, 2048);
+          // non-temporal: 2 bytes per visible pair that the dQ pass reads once, after this
+          // kernel; they should not push the group's Q and dO rows out of L2
+          reg_st16<kNonTemporalPolicy>(rs, dso, 0, __builtin_bit_cast(u32x4, ds[0]));
+          reg_st16<kNonTemporalPolicy>(rs, dso + 16, 0, __builtin_bit_cast(u32x4, ds[1]));
+        }
+      };
       if constexpr (!PW && LAST) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) ds_slot(n);
+        store_ds();
       }
       // P of block k (P wave): lane holds key myk and query rows r0 + 16*hi + v.  The
       // exponentials run in the dV MFMA slots once S is complete (after the loop in the
@@ -744,6 +777,7 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
         if (n < NS) {
           s = mfma32(op[n], kv[n], s);
           if constexpr (!PW && !FIRST) ds_slot(n);
+          if (n == NS - 1) store_ds();
         } else {
           const int j = n - NS;
           acc[j % NT] = mfma32(op[n], PW ? prv_bf[j / NT] : ds[j / NT], acc[j % NT]);
@@ -778,7 +812,7 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
                     const bf16* Gc, const float* Rc, bf16* Ql, bf16* Gl, float* Rl) __attribute__((always_inline)) {
       ofs.repin();
       phase(first_t, F{}, 2 * t, Qc, Gc, Rc, 0, Qp, Gp, Rp, 1, pa, pb, dpa, dpb);
-      if constexpr (MASK) {
+      if constexpr (MASK && CP) {
         if (t + 1 < total) wait_tile_and_mask();  // tile t+1 and the mask of block 2t+2 behind
         else wait_vmem();
       }
@@ -786,13 +820,15 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
       load_mask(2 * t + 3);
       if (t + 2 < total) load_tile(t + 2, Ql, Gl, Rl);
       phase(F{}, F{}, 2 * t + 1, Qc, Gc, Rc, 1, Qc, Gc, Rc, 0, pb, pa, dpb, dpa);
-      if (t + 2 < total) {
-        if constexpr (MASK) wait_tile_and_mask();  // the mask of block 2t+3 and tile t+2 behind
-        else wait_vmem_le<4>();
-      } else if (MASK && 2 * t + 3 < nb) {
-        wait_vmem_le<1>();  // the mask of block 2t+3 behind
-      } else {
-        wait_vmem();
+      if constexpr (CP) {
+        if (t + 2 < total) {
+          if constexpr (MASK) wait_tile_and_mask();  // the mask of block 2t+3 and tile t+2 behind
+          else wait_vmem_le<TPW>();
+        } else if (MASK && 2 * t + 3 < nb) {
+          wait_vmem_le<MPW>();  // the mask of block 2t+3 behind
+        } else {
+          wait_vmem();
+        }
       }
       __syncthreads();
       load_mask(2 * t + 4);
@@ -834,18 +870,18 @@ __device__ __forceinline__ void dkdv_pair_wave(const BwdArgs& a, int bid, int nb
   }
 }
 
-template <int D, int NP, int CM, bool MASK>
+template <int D, int NP, int CM, bool MASK, bool STORE>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int bid, int nblk, char* smem) {
   if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < NP)
-    dkdv_pair_wave<true, D, NP, CM, MASK>(a, bid, nblk, smem);
+    dkdv_pair_wave<true, D, NP, CM, MASK, STORE>(a, bid, nblk, smem);
   else
-    dkdv_pair_wave<false, D, NP, CM, MASK>(a, bid, nblk, smem);
+    dkdv_pair_wave<false, D, NP, CM, MASK, STORE>(a, bid, nblk, smem);
 }
 
-template <int D, int NP, int CM, bool MASK>
+template <int D, int NP, int CM, bool MASK, bool STORE>
 __global__ __launch_bounds__(128 * NP, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv_pair_lds_bytes<D, NP, MASK>()];
-  dkdv_pair_body<D, NP, CM, MASK>(a, blockIdx.x, gridDim.x, smem);
+  dkdv_pair_body<D, NP, CM, MASK, STORE>(a, blockIdx.x, gridDim.x, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1414,6 +1450,160 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// 3c. dQ from the stored dS blocks (d = 128, when dK/dV and dQ run in one call)
+// ---------------------------------------------------------------------------------------
+// The paired dK/dV kernel forms every bf16 dS block of the problem anyway (the operand of its
+// dK product, rounded as the dQ product takes it); with a dS buffer it also writes them out
+// (BwdArgs::ds).  dQ = scale dS K then needs one product per block, not the recomputation
+// of S, P and dP (three of the query-stationary pass's four): this kernel streams each
+// row block's dS^T blocks from HBM once, through LDS, and reads them back transposed
+// (ds_read_b64_tr_b16) as the B operand of dQ^T += K^T dS^T, with K^T read as in the other
+// dQ kernels.  Its cost is the dS traffic: 2 bytes per visible pair written and read again,
+// instead of 6 D flops per pair recomputed.
+//
+// A wave (32 query rows) visits the key blocks [lo, hi) in which some row sees some key:
+// the union of the rows' visible keys is one interval (consecutive rows' windows overlap),
+// so every such block holds a visible pair.  The dK/dV kernel has written each of them: a
+// visible pair (i, j) lies in a query tile (64 rows) and key workgroup it visits.
+// Workgroup: NW waves of 32 rows of one head (the other dQ kernels' items and order); each
+// step copies one 32-key K block (shared) and each wave's dS block into one of kDsBufs
+// buffers, kDsBufs - 1 blocks ahead.
+constexpr int kDsBufs = 5;  // 80 KB of LDS: two workgroups per CU
+
+template <int D, int NW, int CM>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_ds_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = CM != 0;
+  constexpr int BM = NW * 32;
+  constexpr int KB = 32 * D;  // elements of a 32-key K block
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kDsBufs * KB];
+  __shared__ __attribute__((aligned(16))) bf16 Ss[kDsBufs * NW * 1024];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int gi, r;
+  xcd_item(blockIdx.x, p.B * p.Hkv, (int)(gridDim.x / (p.B * p.Hkv)), p.G, !CAUSAL, gi, r);
+  const int b = batch_by_work(p, gi / p.Hkv);
+  const int g = gi % p.Hkv;
+  const int h = g * p.G + r % p.G;
+  const int rank = r / p.G;
+  const int q_end = seq_len_q(p, b);
+  const int kv_end = seq_len_kv(p, b);
+  const int qt = CAUSAL ? (p.Lq + BM - 1) / BM - 1 - rank : rank;
+  const int row_lo = qt * BM;
+  const int coff = CAUSAL ? causal_offset(p.causal, q_end, kv_end) : 0;
+  const int W = CM == 2 ? p.window : 0;
+
+  // key blocks [lo, hi_) with a visible pair for the 32 rows from r0: the rows' visible keys
+  // together are [first, stop)
+  auto blocks = [&](int r0, int& lo, int& hi_) __attribute__((always_inline)) {
+    lo = hi_ = 0;
+    if (r0 >= q_end) return;
+    int stop = kv_end;
+    if (CAUSAL) stop = min(stop, min(r0 + 32, q_end) + coff);
+    const int first = W > 0 ? max(r0 + coff - W + 1, 0) : 0;
+    if (stop <= first) return;
+    lo = first >> 5;
+    hi_ = (stop + 31) >> 5;
+  };
+  int my_lo, my_hi;
+  blocks(row_lo + 32 * wave, my_lo, my_hi);
+  int kb0 = 0, kb1 = 0;  // the workgroup's blocks: the union of its waves' ranges
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    int lo, hi_;
+    blocks(row_lo + 32 * w, lo, hi_);
+    if (hi_ > lo) {
+      kb0 = kb1 > kb0 ? min(kb0, lo) : lo;
+      kb1 = max(kb1, hi_);
+    }
+  }
+  const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;
+
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + k_base(p, b) + g * p.k_sh;
+  // this wave's row of dS blocks (query block row_lo / 32 + wave of head h)
+  const bf16* dsrow = reinterpret_cast<const bf16*>(a.ds) +
+                      (((int64_t)b * p.Hq + h) * a.ds_nqb + (row_lo >> 5) + wave) * a.ds_nkb * 1024;
+  TileCopy<32, D, NW> kcopy;
+  kcopy.init(p.k_sl, wave, lane);
+  constexpr int CPB = TileCopy<32, D, NW>::PER_WAVE + 2;  // copies per wave and block
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int kb = kb0 + i;
+    const int buf = i % kDsBufs;
+    kcopy.copy(rows_rsrc<D, 32>(kbase, p.k_sl, kb * 32, kv_end), Ks + buf * KB, wave);
+    // a block this wave does not visit is copied from an empty range (zeros, no traffic)
+    const bool mine = kb >= my_lo && kb < my_hi;
+    const i32x4 rs = raw_rsrc(dsrow + (int64_t)kb * 1024, mine ? 2048 : 0);
+    bf16* dst = Ss + (buf * NW + wave) * 1024;
+    buffer_to_lds<16, true>(rs, dst, 0, lane * 16);
+    buffer_to_lds<16, true>(rs, dst, 1024, 1024 + lane * 16);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
+  const int blk = lane >> 4;
+  const int arow = (lane & 15) >> 2;
+  const int tchunk = ((lane & 3) >> 1) + 2 * (blk & 1);
+  const int thalf = 4 * (lane & 1);
+  OpOffsets<D> ofs;
+  ofs.init(perm_row(l32), hi, arow, tchunk, thalf);
+  // B operand of k-step `half` (keys 16 hi + 8 half + t, t = 0..7, of query l32): each
+  // 16-lane block reads four key rows of its sixteen queries; lane j supplies the address of
+  // key row 16 hi + j / 4 (+ 8 half, + 4 for the second read), queries 16 (blk & 1) + 4 (j % 4)
+  // .. + 3 (one 64-byte row per key; a 32-lane phase reads four whole rows, every bank once)
+  const uint32_t dso = (uint32_t)((16 * hi + arow) * 64 + 32 * (blk & 1) + 8 * (lane & 3));
+
+#pragma unroll
+  for (int i = 0; i < kDsBufs - 1; ++i)
+    if (i < nblk) issue(i);
+  for (int i = 0; i < nblk; ++i) {
+    // block i has landed when only the copies of the blocks issued after it are in flight
+    static_assert(kDsBufs == 5, "waits below cover up to three blocks in flight");
+    const int after = min(nblk - 1 - i, kDsBufs - 2);
+    if (after >= 3) wait_vmem_le<3 * CPB>();
+    else if (after == 2) wait_vmem_le<2 * CPB>();
+    else if (after == 1) wait_vmem_le<CPB>();
+    else wait_vmem();
+    __syncthreads();
+    // into the buffer of block i - 1, which every wave has finished reading
+    if (i + kDsBufs - 1 < nblk) issue(i + kDsBufs - 1);
+    const int kb = kb0 + i;
+    if (kb >= my_lo && kb < my_hi) {
+      const bf16* Kt = Ks + (i % kDsBufs) * KB;
+      const char* St = reinterpret_cast<const char*>(Ss + ((i % kDsBufs) * NW + wave) * 1024);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 bop = join_tr(lds_read_tr4(reinterpret_cast<const bf16*>(St + dso + half * 512)),
+                                   lds_read_tr4(reinterpret_cast<const bf16*>(St + dso + half * 512 + 256)));
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) acc[mb] = mfma32(ofs.tr8(Kt, 8 * half, mb), bop, acc[mb]);
+      }
+    }
+  }
+
+  const int qi = row_lo + 32 * wave + l32;
+  if (qi < q_rows_out(p, q_end)) {
+    const bool qok = qi < q_end;
+    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + q_base(p, b) + h * p.q_sh + (int64_t)qi * p.q_sl;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(qok ? acc[mb][v4 * 4 + e] * p.scale : 0.f);
+        *reinterpret_cast<bf16x4*>(dqrow + mb * 32 + v4 * 8 + hi * 4) = w;
+      }
+    }
+  }
+}
+
 // Waves per workgroup of the two main kernels.  dQ runs two 4-wave workgroups per CU (two
 // waves per SIMD; the workgroups' barriers are independent), measured faster than one
 // 8-wave workgroup on the MHA 1k and padded 2k workloads and equal on GQA 4k.
@@ -1449,11 +1639,22 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  // With a dS buffer (d = 128, where dK/dV runs the paired kernel) the dK/dV pass stores
+  // dS and dQ is formed from it: the dq stage then reads what the dkdv stage wrote.
+  bool ds_path = false;
+  if constexpr (BwdShape<D>::PAIR_DKDV) {
+    static_assert(32 * KNW == kDsKeysPerGroup, "dS buffer key blocks follow the dK/dV workgroups");
+    ds_path = a.ds != nullptr && (!MASK || a.p.mask_vec);
+  }
   if ((stages & kBwdDkdv) && n_kt > 0) {
     bool paired = false;
     if constexpr (BwdShape<D>::PAIR_DKDV) {
-      if (!MASK || a.p.mask_vec) {
-        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM, MASK>), dim3(n_kt * a.p.B * a.p.Hkv),
+      if (ds_path) {
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM, MASK, true>), dim3(n_kt * a.p.B * a.p.Hkv),
+                           dim3(128 * KNW), 0, s, a);
+        paired = true;
+      } else if (!MASK || a.p.mask_vec) {
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, KNW, CM, MASK, false>), dim3(n_kt * a.p.B * a.p.Hkv),
                            dim3(128 * KNW), 0, s, a);
         paired = true;
       }
@@ -1465,6 +1666,12 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & kBwdDq) && n_qt > 0) {
+    if constexpr (BwdShape<D>::PAIR_DKDV) {
+      if (ds_path) {
+        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, QNW, CM>), dim3(n_qt * a.p.B * a.p.Hq), dim3(64 * QNW), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     if constexpr (MASK ? BwdShape<D>::PIPE_DQ_MASK : BwdShape<D>::PIPE_DQ)
       hipLaunchKernelGGL((bwd_dq_kernel<D, QNW, CM, MASK>), dim3(n_qt * a.p.B * a.p.Hq),
                          dim3(64 * QNW), 0, s, a);

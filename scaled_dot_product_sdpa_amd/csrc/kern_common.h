@@ -245,6 +245,9 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int64_t bytes) {
 }
 
 
+// Cache-policy bits of a buffer load or store: non-temporal (the nt bit), for data touched once.
+constexpr int kNonTemporalPolicy = 2;
+
 // Buffer resource over `bytes` bytes at `base` for loads into registers (reads past the end
 // return zeros); the compiler tracks these loads like any other and inserts the wait before
 // the first use of a result.  The resource type exists only for the GPU target; the host
@@ -262,12 +265,20 @@ __device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t r, uint32_t voff, uint32_t 
 __device__ __forceinline__ float reg_ld4f(reg_rsrc_t r, uint32_t voff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
+// 16 bytes from registers to byte offset voff + soff (a vector store; stores past the end are
+// dropped; AUX: cache policy bits)
+template <int AUX = 0>
+__device__ __forceinline__ void reg_st16(reg_rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, AUX);
+}
 #else
 struct reg_rsrc_t { uint32_t w[4]; };
 __device__ __forceinline__ reg_rsrc_t reg_rsrc(const void*, int64_t) { return reg_rsrc_t{}; }
 template <int AUX = 0>
 __device__ __forceinline__ u32x4 reg_ld16(reg_rsrc_t, uint32_t, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ float reg_ld4f(reg_rsrc_t, uint32_t) { return 0.f; }
+template <int AUX = 0>
+__device__ __forceinline__ void reg_st16(reg_rsrc_t, uint32_t, uint32_t, u32x4) {}
 #endif
 
 // SIZE bytes per lane from src + voff into LDS at lds + byte_off + SIZE * lane (wave-uniform
@@ -279,12 +290,17 @@ __device__ __forceinline__ float reg_ld4f(reg_rsrc_t, uint32_t) { return 0.f; }
 // ISA's table of manually inserted wait states), hence the s_nop; without it the load can
 // see the previous copy's M0 and land in the wrong place.  M0 is a reserved register that
 // cannot be named as clobbered; nothing else in these kernels uses it.
-template <int SIZE>
+// NT: the non-temporal cache policy, for data read once (it is then the first to leave L2).
+template <int SIZE, bool NT = false>
 __device__ __forceinline__ void buffer_to_lds(i32x4 src, void* lds, uint32_t byte_off, uint32_t voff) {
   static_assert(SIZE == 4 || SIZE == 16, "4 or 16 bytes per lane");
+  static_assert(SIZE == 16 || !NT, "non-temporal copies of 16 bytes only");
   const uint32_t addr = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds + byte_off));
-  if constexpr (SIZE == 16)
+  if constexpr (SIZE == 16 && NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(addr),
+                 "v"(voff), "s"(src) : "memory");
+  else if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(addr),
                  "v"(voff), "s"(src) : "memory");
   else

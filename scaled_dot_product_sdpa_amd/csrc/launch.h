@@ -104,7 +104,21 @@ struct BwdArgs {
   float* dsum;  // workspace: D = rowsum(dO o O), contiguous (B, Hq, Lq)
   float* lse2;  // workspace: LSE * log2(e) (LSE itself with a mask), +inf for empty rows,
                 // contiguous (B, Hq, Lq)
+  // workspace, may be null: bf16 dS blocks written by the paired dK/dV kernel and read by
+  // the dQ-from-dS kernel when both passes run in one call.  Block (b, h, qb, kb) holds dS^T
+  // of query rows 32 qb .. 32 qb + 31 and keys 32 kb .. 32 kb + 31 as 32 x 32 row-major
+  // (one 64-byte row per key) at element ((((b * Hq + h) * ds_nqb + qb) * ds_nkb + kb) * 1024.
+  void* ds;
+  int ds_nqb;  // query blocks per head: 2 * ceil(Lq / 64) (whole 64-row dK/dV query tiles)
+  int ds_nkb;  // key blocks per head: whole 128-key dK/dV workgroups
 };
+
+// Size of the dS block buffer (bytes) and its block counts; see BwdArgs::ds.
+constexpr int kDsKeysPerGroup = 128;
+inline void ds_blocks(int Lq, int Lk, int* nqb, int* nkb) {
+  *nqb = 2 * ((Lq + 63) / 64);
+  *nkb = (kDsKeysPerGroup / 32) * ((Lk + kDsKeysPerGroup - 1) / kDsKeysPerGroup);
+}
 
 struct DecodeArgs {
   Problem p;

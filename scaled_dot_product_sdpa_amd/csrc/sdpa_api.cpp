@@ -178,6 +178,19 @@ sdpa_status hip_result(hipError_t e, const char* what) {
   return SDPA_OK;
 }
 
+// The bf16 dS block buffer of the backward (d = 128; see sdpa_backward_workspace_bytes in
+// include/sdpa.h): 2 KB per 32 x 32 block of every (batch, query head), whole dK/dV query
+// tiles and key workgroups; 0 where the backward does not use one or it would exceed
+// kDsBufferCap.
+constexpr size_t kDsBufferCap = size_t(8) << 30;
+size_t ds_buffer_bytes(const sdpa_problem* p) {
+  if (p->dtype != SDPA_DTYPE_BF16 || p->Dqk != 128 || p->Dv != 128) return 0;
+  int nqb = 0, nkb = 0;
+  sdpa::ds_blocks(p->Lq, p->Lk, &nqb, &nkb);
+  const size_t bytes = (size_t)p->B * p->Hq * nqb * nkb * 2048;
+  return bytes <= kDsBufferCap ? bytes : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,10 +204,15 @@ size_t sdpa_forward_workspace_bytes(const sdpa_problem* p) {
   return round_up(rows * p->Dv * sizeof(float)) + round_up(rows * sizeof(float));
 }
 
-size_t sdpa_backward_workspace_bytes(const sdpa_problem* p) {
+size_t sdpa_backward_workspace_bytes_min(const sdpa_problem* p) {
   if (check_problem(p) != SDPA_OK) return 0;
   // D = rowsum(dO o O) and LSE * log2(e), one fp32 each per query row
   return 2 * round_up((size_t)p->B * p->Hq * p->Lq * sizeof(float));
+}
+
+size_t sdpa_backward_workspace_bytes(const sdpa_problem* p) {
+  if (check_problem(p) != SDPA_OK) return 0;
+  return sdpa_backward_workspace_bytes_min(p) + ds_buffer_bytes(p);
 }
 
 namespace {
@@ -354,7 +372,7 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
                     "%s has a zero batch or head stride: its gradient would alias (pass a copy)",
                     names[t]);
   }
-  const size_t need = sdpa_backward_workspace_bytes(p);
+  const size_t need = sdpa_backward_workspace_bytes_min(p);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(SDPA_ERR_WORKSPACE_TOO_SMALL, "backward needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
@@ -367,6 +385,12 @@ sdpa_status backward_stages(int stages, const sdpa_problem* p, const void* q, co
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = reinterpret_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + need / 2);
+  // room for the dS block buffer after the row values: dQ is formed from the stored dS
+  const size_t dsb = ds_buffer_bytes(p);
+  if (dsb > 0 && workspace_bytes - need >= dsb) {
+    a.ds = reinterpret_cast<char*>(workspace) + need;
+    sdpa::ds_blocks(p->Lq, p->Lk, &a.ds_nqb, &a.ds_nkb);
+  }
   if (p->dtype == SDPA_DTYPE_F32)
     return hip_result(sdpa::launch_bwd_f32(a, stages, s), "fp32 backward launch");
   return hip_result(sdpa::launch_bwd_bf16(a, stages, s), "bf16 backward launch");

@@ -122,8 +122,28 @@ def test_prefill_and_backward_workspace(lib):
     assert lib.sdpa_forward_workspace_bytes(ctypes.byref(p)) == 0
     nb = lib.sdpa_backward_workspace_bytes(ctypes.byref(p))
     assert nb >= 4 * 16 * 1024 * 4 and nb % 256 == 0
+    # no dS buffer at d = 64: the full and the least workspace agree
+    assert lib.sdpa_backward_workspace_bytes_min(ctypes.byref(p)) == nb
     bad = _problem(Hq=3)
     assert lib.sdpa_backward_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.sdpa_backward_workspace_bytes_min(ctypes.byref(bad)) == 0
+
+
+def test_backward_ds_buffer_size(lib):
+    """At d = 128 (bf16) the backward workspace adds the dS block buffer: 2 KB per 32 x 32
+    block, over whole 64-row query tiles and 128-key groups of every (batch, query head)."""
+    p = _problem(B=2, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128, causal=1)
+    nmin = lib.sdpa_backward_workspace_bytes_min(ctypes.byref(p))
+    assert nmin == 2 * 2 * 32 * 4096 * 4
+    assert lib.sdpa_backward_workspace_bytes(ctypes.byref(p)) == nmin + 2 * 32 * 128 * 128 * 2048
+    # ragged tails round up to whole query tiles (64 rows) and key groups (128 keys)
+    p = _problem(B=3, Hq=4, Hkv=2, Lq=90, Lk=130, D=128)
+    nmin = lib.sdpa_backward_workspace_bytes_min(ctypes.byref(p))
+    assert lib.sdpa_backward_workspace_bytes(ctypes.byref(p)) == nmin + 3 * 4 * 4 * 8 * 2048
+    # over 8 GiB of blocks: no buffer (dQ is recomputed)
+    p = _problem(B=8, Hq=32, Hkv=8, Lq=16384, Lk=16384, D=128, causal=1)
+    assert lib.sdpa_backward_workspace_bytes(ctypes.byref(p)) == \
+        lib.sdpa_backward_workspace_bytes_min(ctypes.byref(p))
 
 
 @pytest.mark.parametrize("stage", ["sdpa_backward", "sdpa_backward_prep", "sdpa_backward_dkdv",
