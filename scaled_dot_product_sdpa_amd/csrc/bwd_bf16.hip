@@ -1468,8 +1468,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
 // visible pair (i, j) lies in a query tile (64 rows) and key workgroup it visits.
 // Workgroup: NW waves of 32 rows of one head (the other dQ kernels' items and order); each
 // step copies one 32-key K block (shared) and each wave's dS block into one of kDsBufs
-// buffers, kDsBufs - 1 blocks ahead.
-constexpr int kDsBufs = 5;  // 80 KB of LDS: two workgroups per CU
+// buffers, kDsBufs - 1 blocks ahead.  Eight waves share each K block and three buffers
+// (72 KB of LDS, two workgroups and sixteen waves per CU): measured against four waves with
+// three, four or five buffers (the fewer buffers, the more workgroups per CU and the
+// faster), 215 against 229-239 us on the causal GQA 4k step, equal on the padded 2k one.
+// Grids too small to give every CU two such workgroups (a 512-row prefill chunk) take
+// four-wave ones (48 KB, three per CU).
+constexpr int kDsBufs = 3;
+constexpr int kNumCu = 256;
 
 template <int D, int NW, int CM>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_ds_kernel(BwdArgs a) {
@@ -1564,11 +1570,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_ds_kernel(BwdArgs a) {
     if (i < nblk) issue(i);
   for (int i = 0; i < nblk; ++i) {
     // block i has landed when only the copies of the blocks issued after it are in flight
-    static_assert(kDsBufs == 5, "waits below cover up to three blocks in flight");
-    const int after = min(nblk - 1 - i, kDsBufs - 2);
-    if (after >= 3) wait_vmem_le<3 * CPB>();
-    else if (after == 2) wait_vmem_le<2 * CPB>();
-    else if (after == 1) wait_vmem_le<CPB>();
+    static_assert(kDsBufs == 3, "the wait below covers one block in flight");
+    if (i + 1 < nblk) wait_vmem_le<CPB>();
     else wait_vmem();
     __syncthreads();
     // into the buffer of block i - 1, which every wave has finished reading
@@ -1668,7 +1671,12 @@ hipError_t launch_main(const BwdArgs& a, int stages, hipStream_t s) {
   if ((stages & kBwdDq) && n_qt > 0) {
     if constexpr (BwdShape<D>::PAIR_DKDV) {
       if (ds_path) {
-        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, QNW, CM>), dim3(n_qt * a.p.B * a.p.Hq), dim3(64 * QNW), 0, s, a);
+        // eight-wave workgroups where they still give every CU two; else four waves
+        const int n8 = ((a.p.Lq + 255) / 256) * a.p.B * a.p.Hq;
+        if (n8 >= 2 * kNumCu)
+          hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 8, CM>), dim3(n8), dim3(512), 0, s, a);
+        else
+          hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4, CM>), dim3(n_qt * a.p.B * a.p.Hq), dim3(256), 0, s, a);
         return hipGetLastError();
       }
     }

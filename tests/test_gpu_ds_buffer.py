@@ -77,3 +77,23 @@ def test_ds_buffer_poisoned_workspace_is_bitwise_clean():
             outs.append([t.clone() for t in bc.result()])
         for a, b in zip(*outs):
             assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("causal,window", [(1, 0), (2, 300)])
+def test_ds_buffer_eight_wave_grid(causal, window):
+    """A grid large enough for the eight-wave dQ-from-dS workgroups (256 rows each, ragged
+    last tile): the same gradients as the recomputing path (dK, dV bit for bit, dQ within
+    rounding), with the workspace NaN-filled first.  (The oracle checks the recomputing path
+    on the same shapes at reduced size; this size is beyond a quick fp64 run.)"""
+    banner(f"dS buffer, eight-wave grid: causal={causal} window={window}")
+    w = GQA.scaled(B=4, Hq=32, Hkv=8, Lq=1000, Lk=1000, causal=causal, window=window, seed=68)
+    d = to_dev(make_inputs(w))
+    fc = ForwardCall(d["q"], d["k"], d["v"], d["mask"], d["scale"], d["is_causal"], d["len_q"],
+                     d["len_kv"], sliding_window=w.window)
+    fc.launch()
+    torch.cuda.synchronize()
+    (dq1, dk1, dv1), _ = _run(d, fc.o, fc.lse, w, True, poison=True)
+    (dq2, dk2, dv2), _ = _run(d, fc.o, fc.lse, w, False)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    assert torch.isfinite(dq1.float()).all()
+    assert rel_fro(f64(dq1), f64(dq2)) <= 2e-3
