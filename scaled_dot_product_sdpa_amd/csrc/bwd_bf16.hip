@@ -8,7 +8,7 @@
 // forward's LSE (that page's "Going further" table: the FlashAttention-2 backward
 // recomputes P from saved row statistics and uses D = rowsum(dO o O)).
 //
-// Three kernels, no atomics (the result is deterministic):
+// Three kernels (a fourth with the dS buffer), no atomics (the result is deterministic):
 //  1. prep:  per row, D_i = sum_t dO_it O_it and lse2_i = LSE_i * log2(e) (+inf for a row
 //            with no visible key or past the length, so that exp2(s - lse2) = 0 there),
 //            both fp32 into the workspace.
@@ -33,6 +33,11 @@
 //            At D = 64 the blocks are software-pipelined inside each wave like the other
 //            kernels (dQ one block late); at D = 128 that form needs more than the 256
 //            registers two waves per SIMD allow, so each block runs start to finish.
+//  4. dq from stored dS (D = 128, with the dS buffer in the workspace): the paired dK/dV
+//            kernel also writes each bf16 dS block it forms, and dQ^T += K^T dS^T is then
+//            one product per block that streams the stored blocks instead of recomputing
+//            S, P and dP (see section 3c).  Still no atomics: each dQ element is written by
+//            one lane.
 // Rows and keys past the lengths and pairs above the causal diagonal carry P = 0; blocks
 // that are blocked as a whole are skipped.  LDS tiles are unpadded with XOR-swizzled
 // 16-byte chunks (kern_common.h).
