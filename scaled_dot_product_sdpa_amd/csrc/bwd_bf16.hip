@@ -1460,12 +1460,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_seq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // The paired dK/dV kernel forms every bf16 dS block of the problem anyway (the operand of its
 // dK product, rounded as the dQ product takes it); with a dS buffer it also writes them out
-// (BwdArgs::ds).  dQ = scale dS K then needs one product per block, not the recomputation
-// of S, P and dP (three of the query-stationary pass's four): this kernel streams each
-// row block's dS^T blocks from HBM once, through LDS, and reads them back transposed
-// (ds_read_b64_tr_b16) as the B operand of dQ^T += K^T dS^T, with K^T read as in the other
-// dQ kernels.  Its cost is the dS traffic: 2 bytes per visible pair written and read again,
-// instead of 6 D flops per pair recomputed.
+// (BwdArgs::ds).  dQ = scale dS K then needs one product per block, without recomputing S,
+// P and dP (two of the query-stationary pass's three products, and its exponentials): this
+// kernel streams each row block's dS^T blocks from HBM once, through LDS, and reads them
+// back transposed (ds_read_b64_tr_b16) as the B operand of dQ^T += K^T dS^T, with K^T read
+// as in the other dQ kernels.  Its cost is the dS traffic: 2 bytes per visible pair written
+// and read again, instead of 4 D flops and an exponential per pair recomputed.
 //
 // A wave (32 query rows) visits the key blocks [lo, hi) in which some row sees some key:
 // the union of the rows' visible keys is one interval (consecutive rows' windows overlap),
