@@ -121,17 +121,24 @@ def test_empty_key_sequence():
 
 
 def test_strided_bshd_layout(orc):
-    """Inputs in (B, S, H, D) memory order (strided views) give the same result."""
+    """Inputs in (B, S, H, D) memory order (strided views) give the same result, forward and
+    backward (the gradients are written with the strides of q, k, v; at d = 128 the backward
+    forms dQ from the stored dS)."""
     banner("BSHD strided layout")
     w = MID.scaled(Hq=4, Hkv=2, Lq=200, Lk=200, seed=35)
     inp = make_inputs(w)
     d = to_dev(inp)
     o1, l1 = gpu_forward(d)
     ds = dict(d)
-    for n in ("q", "k", "v"):
+    for n in ("q", "k", "v", "dO"):
         ds[n] = d[n].transpose(1, 2).contiguous().transpose(1, 2)  # BSHD storage, BHSD view
     o2, l2 = gpu_forward(ds)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = gpu_backward(d, o1, l1)
+    g2 = gpu_backward(ds, o2, l2)
+    for a, b in zip(g1, g2):
+        assert a.shape == b.shape and torch.equal(a, b.contiguous())
+    assert g2[0].stride() == ds["q"].stride() and g2[1].stride() == ds["k"].stride()
 
 
 def test_graph_replay_matches_eager():
