@@ -470,6 +470,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the live MFMA / HBM ceiling probes (libceilings.so)")
     ap.add_argument("--no-headline", action="store_true",
                     help="skip the headline step (with --only: profile other workloads alone)")
     ap.add_argument("--only", default=None, help="comma list of extra workloads to run")
@@ -606,6 +608,30 @@ def main():
             del fc2, bc2
             torch.cuda.empty_cache()
         out["workloads"] = extra
+
+    # ---- the chip's ceilings measured now (clock under MFMA load, a bf16 MFMA stream, a
+    # MALL-busting HBM read), and each roofline's fraction of them beside that of the spec
+    # (the default run only: the per-workload profiling runs keep their traces to the kernels)
+    if not (args.no_ceilings or args.only or args.no_headline):
+        log("measured ceilings: MFMA stream, HBM read, clock")
+        from scaled_dot_product_sdpa_amd.ceilings import measured
+        ceil = measured()
+        out["measured_ceilings"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ceil.items()}
+
+        def add_frac(roof):
+            if not roof:
+                return
+            c = (ceil["hbm_read_tbs"] * 1e3 if roof["unit"] == "GB/s"
+                 else ceil["mfma_bf16_tflops"] if roof["bound"] == "mfma" else None)
+            roof["frac_of_measured"] = round(roof["achieved"] / c, 4) if c else None
+
+        add_frac(out.get("roofline"))
+        for res in out.get("workloads", {}).values():
+            add_frac(res.get("roofline"))
+        if "peak_frac_fwd" in out:
+            r = PEAK_BF16_TFLOPS / ceil["mfma_bf16_tflops"]
+            out["measured_frac_fwd"] = round(out["peak_frac_fwd"] * r, 4)
+            out["measured_frac_bwd"] = round(out["peak_frac_bwd"] * r, 4)
 
     # ---- CPU baseline (rank 0, N = 1 only)
     if not args.no_cpu and inp is not None:

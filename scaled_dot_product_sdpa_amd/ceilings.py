@@ -214,6 +214,63 @@ def atomics(scale: float = 1.0) -> str:
     return "\n".join(rows)
 
 
+def measured() -> dict:
+    """The ceilings a bench line is read against, measured now: the shader clock under MFMA
+    load, the bf16 MFMA rate of a 32x32x16 stream (four independent accumulation chains, two
+    waves per SIMD; probe 1) and the HBM read rate of two 512 MiB streams in the decode
+    kernel's pattern with the non-temporal policy (probe 7; 1 GiB per launch, four times the
+    256 MB last-level cache).  About a second of GPU time."""
+    import torch
+    lib = ctypes.CDLL(str(CEIL_LIB))
+    lib.ceil_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_probe.restype = ctypes.c_int
+    lib.ceil_stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ceil_stream_probe.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(65536 * 2, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(REPS):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / REPS  # us
+
+    def probe(pid, wps, it):
+        rc = lib.ceil_probe(pid, wps, ctypes.c_void_p(out.data_ptr()), it, stream)
+        if rc != 0:
+            raise RuntimeError(f"probe {pid}: status {rc}")
+
+    it = _iters(1, 1.0)
+    probe(17, 2, it)
+    torch.cuda.synchronize()
+    cyc, ticks = out[0].item(), out[1].item()
+    ghz = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else float("nan")
+    us = timed(lambda: probe(1, 2, it))
+    mfma_tf = CUS * 4 * 2 * it * 4 * 32768 / (us * 1e-6) / 1e12
+    sb = 512 << 20
+    chunk = 192 << 10
+    n = sb // chunk * chunk
+    buf = torch.ones(2 * sb // 4, dtype=torch.float32, device="cuda")
+    sout = torch.empty(n // chunk * 64, dtype=torch.float32, device="cuda")
+
+    def stream_read():
+        rc = lib.ceil_stream_probe(2, 1, ctypes.c_void_p(buf.data_ptr()), n, chunk,
+                                   ctypes.c_void_p(sout.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe: status {rc}")
+
+    us = timed(stream_read)
+    del buf, sout
+    return {"clock_ghz": ghz, "mfma_bf16_tflops": mfma_tf, "hbm_read_tbs": 2 * n / (us * 1e-6) / 1e12,
+            "mfma_probe": "v_mfma_f32_32x32x16_bf16, four independent chains, two waves per SIMD",
+            "hbm_probe": "two 512 MiB streams, one-wave workgroups, 192 KiB chunks, non-temporal loads"}
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "atomics":
         print(atomics(float(sys.argv[2]) if len(sys.argv) > 2 else 1.0))
