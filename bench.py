@@ -357,7 +357,9 @@ def write_traffic(fetch_dir, write_dir, command, workload, l2_dir=None):
         if fs != fcopy:
             out[stage]["bytes_per_launch_copy_scale"] = int(fk * 1024 * fcopy + wk * 1024 * ws)
     if l2_dir:
-        out["l2_command"] = command.replace("FETCH_SIZE", "TCC_HIT_sum TCC_MISS_sum")
+        # the FETCH_SIZE run's command with the L2 counters and their output folder
+        out["l2_command"] = (command.split(" ; ")[0].replace("--pmc FETCH_SIZE", "--pmc TCC_HIT_sum TCC_MISS_sum")
+                             .replace("pmc_FETCH_SIZE_", "pmc_L2_"))
         hits, misses = _pmc_rows(l2_dir, "TCC_HIT_sum"), _pmc_rows(l2_dir, "TCC_MISS_sum")
         for stage, frag in KERNEL_NAMES.items():
             h = sum(v for n, v in hits if frag in n and "sdpa::" in n)
